@@ -1,0 +1,305 @@
+/*
+ * CPU oracle for the MoGA + STGA forward path.  TEST INFRASTRUCTURE ONLY:
+ * only the tests, the package smoke check and the benchmark's CPU-baseline leg
+ * may load or call it.  It shares no code, header, table or helper with the
+ * HIP library, and the HIP library never calls it.
+ *
+ * Everything here is the plain definition written out, in fp64, one query row
+ * at a time.  Page citations use the page's site and section:
+ *   [N]  papernotes.org ICLR 2026 note "MoGA: Mixture-of-Groups Attention for
+ *        End-to-End Long Video Generation", section 方法详解 / 关键设计 1-4.
+ *   [T]  jxzklqfsx.com Chinese translation of the paper, section 方法
+ *        (混合分組注意力, 組平衡損失, 時空分組注意力).
+ *   [B]  xugj520.cn blog on MoGA, §2.2-2.3 (router), §3.2 (STGA boundary
+ *        frames), §9 (augment_kv=2).
+ * Readings where the pages are silent are marked READING and listed with the
+ * design notes.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC moga_oracle.c -o liboracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------- */
+/* Router  ([N] key design 1; [B] §2.3)                                       */
+/*   r = x W (linear, no bias); p(i|x) = softmax(r)_i; g(x) = argmax_i p(i|x) */
+/* READING: the argmax is taken over the logits (softmax is monotone), the    */
+/* first maximum wins on an exact tie.  pin[t] >= 0 forces g(t) = pin[t].     */
+/* gap[t] = top-1 minus top-2 logit (INFINITY when M = 1).                    */
+/* ------------------------------------------------------------------------- */
+int oracle_route(const float *x, const float *w, int64_t n, int d, int m,
+                 const int32_t *pin, int32_t *group_id, double *p_sel, double *gap,
+                 double *prob_sum, int64_t *counts, double *probs /* NULL or [n][m] */)
+{
+    if (n < 0 || d < 1 || m < 1 || m > 256) return -1;
+    double *p_all = probs ? probs : (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * m);
+    if (!p_all) return -2;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double r[256];
+        double rmax = -INFINITY, r2 = -INFINITY;
+        int best = 0;
+        for (int i = 0; i < m; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < d; ++j)
+                acc += (double)x[t * (int64_t)d + j] * (double)w[(int64_t)j * m + i];
+            r[i] = acc;
+        }
+        for (int i = 0; i < m; ++i) {
+            if (r[i] > rmax) { r2 = rmax; rmax = r[i]; best = i; }
+            else if (r[i] > r2) { r2 = r[i]; }
+        }
+        double z = 0.0;
+        for (int i = 0; i < m; ++i) z += exp(r[i] - rmax);
+        for (int i = 0; i < m; ++i) p_all[t * (int64_t)m + i] = exp(r[i] - rmax) / z;
+        int g = (pin && pin[t] >= 0) ? pin[t] : best;
+        group_id[t] = g;
+        p_sel[t] = p_all[t * (int64_t)m + g];
+        gap[t] = (m == 1) ? INFINITY : rmax - r2;
+    }
+    for (int i = 0; i < m; ++i) { prob_sum[i] = 0.0; counts[i] = 0; }
+    for (int64_t t = 0; t < n; ++t) {
+        for (int i = 0; i < m; ++i) prob_sum[i] += p_all[t * (int64_t)m + i];
+        counts[group_id[t]] += 1;
+    }
+    if (!probs) free(p_all);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Group boundaries and the permutation ([N] key design 2)                    */
+/*   n_i = #{t : g(t) = i};  cu[0] = 0, cu[i+1] = cu[i] + n_i;                */
+/*   perm lists group 0's tokens, then group 1's, ... each in ascending t.    */
+/* READING: ascending token order inside a group and ascending group id.      */
+/* ------------------------------------------------------------------------- */
+int oracle_groups(const int32_t *group_id, int64_t n, int m, int64_t *cu, int64_t *perm)
+{
+    if (n < 0 || m < 1) return -1;
+    int64_t j = 0;
+    cu[0] = 0;
+    for (int i = 0; i < m; ++i) {
+        for (int64_t t = 0; t < n; ++t)
+            if (group_id[t] == i) perm[j++] = t;
+        cu[i + 1] = j;
+    }
+    return j == n ? 0 : -3; /* an id outside [0, m) leaves perm short */
+}
+
+/* ------------------------------------------------------------------------- */
+/* Group-balancing loss ([N] key design 3)                                    */
+/*   F_i = n_i / N;  P_i = mean over all tokens of p(i|x);                    */
+/*   L_gb = alpha * M * sum_i F_i P_i.                                        */
+/* READING: P_i averages p(i|x) over every token (the MoE load-balancing     */
+/* convention the pages say the loss is borrowed from).                       */
+/* ------------------------------------------------------------------------- */
+double oracle_balance_loss(const int64_t *counts, const double *prob_sum, int64_t n, int m,
+                           double alpha, double *F, double *P)
+{
+    double acc = 0.0;
+    for (int i = 0; i < m; ++i) {
+        double f = (double)counts[i] / (double)n;
+        double p = prob_sum[i] / (double)n;
+        if (F) F[i] = f;
+        if (P) P[i] = p;
+        acc += f * p;
+    }
+    return alpha * (double)m * acc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* One attention row: out = sum_u softmax_u(scale <q, k_u>) v_u over the key   */
+/* list, in fp64, max-subtracted.                                              */
+/* ------------------------------------------------------------------------- */
+static void attend_row(const float *qrow, const float *kh, const float *vh, int hd,
+                       const int64_t *keys, int64_t nk, double scale, double *s, double *out)
+{
+    double smax = -INFINITY;
+    for (int64_t a = 0; a < nk; ++a) {
+        const float *kr = kh + keys[a] * (int64_t)hd;
+        double acc = 0.0;
+        for (int c = 0; c < hd; ++c) acc += (double)qrow[c] * (double)kr[c];
+        s[a] = scale * acc;
+        if (s[a] > smax) smax = s[a];
+    }
+    double z = 0.0;
+    for (int64_t a = 0; a < nk; ++a) { s[a] = exp(s[a] - smax); z += s[a]; }
+    for (int c = 0; c < hd; ++c) out[c] = 0.0;
+    for (int64_t a = 0; a < nk; ++a) {
+        const float *vr = vh + keys[a] * (int64_t)hd;
+        double wgt = s[a] / z;
+        for (int c = 0; c < hd; ++c) out[c] += wgt * (double)vr[c];
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* MoGA attention rows ([N] key design 1)                                     */
+/*   MoGA(x_t) = p(g(t)|x_t) * SA(q_t, K_{g(t)}, V_{g(t)})                    */
+/* with the key set {u : g(u) = g(t)}.  q/k/v hold n_heads_in heads, each      */
+/* [n][hd]; row r asks for head rows_h[r] (an index into those), token        */
+/* rows_t[r].  p_sel NULL means no probability scale.  Returns the number of   */
+/* (query, key) pairs evaluated, or a negative value on bad arguments.         */
+/* ------------------------------------------------------------------------- */
+int64_t oracle_moga_attn(const float *q, const float *k, const float *v, int64_t n, int hd,
+                         const int32_t *group_id, int m, const double *p_sel, double scale,
+                         int64_t n_rows, const int32_t *rows_h, const int64_t *rows_t, double *out)
+{
+    if (n < 1 || hd < 1 || m < 1) return -1;
+    int64_t *cnt = (int64_t *)calloc((size_t)m + 1, sizeof(int64_t));
+    int64_t *members = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    if (!cnt || !members) { free(cnt); free(members); return -2; }
+    /* member lists of every group, ascending token order */
+    int64_t j = 0;
+    for (int i = 0; i < m; ++i) {
+        cnt[i] = j;
+        for (int64_t t = 0; t < n; ++t)
+            if (group_id[t] == i) members[j++] = t;
+    }
+    cnt[m] = j;
+    int64_t pairs = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : pairs)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t t = rows_t[r];
+        int g = group_id[t];
+        int64_t nk = cnt[g + 1] - cnt[g];
+        double *s = (double *)malloc(sizeof(double) * (size_t)nk);
+        const int64_t hoff = (int64_t)rows_h[r] * n * hd;
+        attend_row(q + hoff + t * hd, k + hoff, v + hoff, hd, members + cnt[g], nk, scale, s,
+                   out + r * (int64_t)hd);
+        double ps = p_sel ? p_sel[t] : 1.0;
+        for (int c = 0; c < hd; ++c) out[r * (int64_t)hd + c] *= ps;
+        pairs += nk;
+        free(s);
+    }
+    free(cnt);
+    free(members);
+    return pairs;
+}
+
+/* ------------------------------------------------------------------------- */
+/* STGA key sets ([N] key design 4; [T] 時空分組注意力; [B] §3.2, §9)           */
+/* Token t sits in frame f = t / (H W) at (y, x), frame-major (READING).      */
+/* Temporal groups: same shot s, same chunk c = (f - start_s) / T (chunks      */
+/* start at each shot's first frame; a short last chunk is its own group,     */
+/* READING), same spatial window (y / win_h, x / win_w).  Keys and values     */
+/* (never queries) of the FIRST chunk of shot s > 0 also take the last `aug`   */
+/* frames of shot s-1, and those of the LAST chunk of shot s < S-1 the first   */
+/* `aug` frames of shot s+1, same window, clipped to the neighbour shot        */
+/* (READING: only chunks that touch a shot boundary are augmented).           */
+/* Per-frame groups: every token of frame f.                                  */
+/* Fills keys[] and returns their count.                                       */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+    int frames, height, width, n_shots, win_h, win_w, t_group, aug;
+    const int32_t *shot_start;
+} oracle_grid;
+
+static int64_t stga_keys(const oracle_grid *G, int mode, int64_t t, int64_t *keys)
+{
+    const int64_t hw = (int64_t)G->height * G->width;
+    const int f = (int)(t / hw);
+    const int y = (int)((t % hw) / G->width);
+    const int x = (int)(t % G->width);
+    int64_t nk = 0;
+    if (mode == 1) { /* per-frame group */
+        for (int64_t u = 0; u < hw; ++u) keys[nk++] = (int64_t)f * hw + u;
+        return nk;
+    }
+    int s = 0;
+    while (s + 1 < G->n_shots && G->shot_start[s + 1] <= f) ++s;
+    const int s0 = G->shot_start[s], s1 = G->shot_start[s + 1];
+    const int c = (f - s0) / G->t_group;
+    const int n_chunks = (s1 - s0 + G->t_group - 1) / G->t_group;
+    const int y0 = (y / G->win_h) * G->win_h, x0 = (x / G->win_w) * G->win_w;
+    int lo = s0 + c * G->t_group;
+    int hi = lo + G->t_group < s1 ? lo + G->t_group : s1;
+    /* frame ranges: [a0,a1) borrowed from the previous shot, [lo,hi) own, [b0,b1) next shot */
+    int a0 = lo, a1 = lo, b0 = hi, b1 = hi;
+    if (c == 0 && s > 0) {
+        int prev0 = G->shot_start[s - 1];
+        a0 = s0 - G->aug < prev0 ? prev0 : s0 - G->aug;
+        a1 = s0;
+    }
+    if (c == n_chunks - 1 && s + 1 < G->n_shots) {
+        int next1 = G->shot_start[s + 2];
+        b0 = s1;
+        b1 = s1 + G->aug > next1 ? next1 : s1 + G->aug;
+    }
+    int ranges[3][2] = {{a0, a1}, {lo, hi}, {b0, b1}};
+    for (int rg = 0; rg < 3; ++rg)
+        for (int ff = ranges[rg][0]; ff < ranges[rg][1]; ++ff)
+            for (int yy = y0; yy < y0 + G->win_h; ++yy)
+                for (int xx = x0; xx < x0 + G->win_w; ++xx)
+                    keys[nk++] = (int64_t)ff * hw + (int64_t)yy * G->width + xx;
+    return nk;
+}
+
+static int grid_ok(const oracle_grid *G)
+{
+    if (G->frames < 1 || G->height < 1 || G->width < 1 || G->n_shots < 1) return 0;
+    if (G->win_h < 1 || G->win_w < 1 || G->height % G->win_h || G->width % G->win_w) return 0;
+    if (G->t_group < 1 || G->aug < 0) return 0;
+    if (G->shot_start[0] != 0 || G->shot_start[G->n_shots] != G->frames) return 0;
+    for (int s = 0; s < G->n_shots; ++s)
+        if (G->shot_start[s + 1] <= G->shot_start[s]) return 0;
+    return 1;
+}
+
+/* STGA attention rows; mode 0 = temporal groups, 1 = per-frame groups.        */
+int64_t oracle_stga_attn(const float *q, const float *k, const float *v, int hd, int frames,
+                         int height, int width, int n_shots, const int32_t *shot_start,
+                         int win_h, int win_w, int t_group, int aug, int mode, double scale,
+                         int64_t n_rows, const int32_t *rows_h, const int64_t *rows_t,
+                         double *out)
+{
+    oracle_grid G = {frames, height, width, n_shots, win_h, win_w, t_group, aug, shot_start};
+    if (!grid_ok(&G) || hd < 1) return -1;
+    const int64_t n = (int64_t)frames * height * width;
+    const int64_t max_keys = (int64_t)height * width * (t_group + 2 * aug) + (int64_t)height * width;
+    int64_t pairs = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(+ : pairs)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)max_keys);
+        double *s = (double *)malloc(sizeof(double) * (size_t)max_keys);
+        int64_t t = rows_t[r];
+        int64_t nk = stga_keys(&G, mode, t, keys);
+        const int64_t hoff = (int64_t)rows_h[r] * n * hd;
+        attend_row(q + hoff + t * hd, k + hoff, v + hoff, hd, keys, nk, scale, s,
+                   out + r * (int64_t)hd);
+        pairs += nk;
+        free(keys);
+        free(s);
+    }
+    return pairs;
+}
+
+/* Number of (query, key) pairs of one head: the sum over tokens of the key-set size. */
+int64_t oracle_stga_pairs(int frames, int height, int width, int n_shots,
+                          const int32_t *shot_start, int win_h, int win_w, int t_group, int aug,
+                          int mode)
+{
+    oracle_grid G = {frames, height, width, n_shots, win_h, win_w, t_group, aug, shot_start};
+    if (!grid_ok(&G)) return -1;
+    const int64_t n = (int64_t)frames * height * width;
+    const int64_t max_keys = (int64_t)height * width * (t_group + 2 * aug) + (int64_t)height * width;
+    int64_t pairs = 0;
+#pragma omp parallel for schedule(static) reduction(+ : pairs)
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)max_keys);
+        pairs += stga_keys(&G, mode, t, keys);
+        free(keys);
+    }
+    return pairs;
+}
+
+/* Key list of one token (for tests of the grouping itself). */
+int64_t oracle_stga_key_list(int frames, int height, int width, int n_shots,
+                             const int32_t *shot_start, int win_h, int win_w, int t_group,
+                             int aug, int mode, int64_t t, int64_t *keys)
+{
+    oracle_grid G = {frames, height, width, n_shots, win_h, win_w, t_group, aug, shot_start};
+    if (!grid_ok(&G)) return -1;
+    return stga_keys(&G, mode, t, keys);
+}

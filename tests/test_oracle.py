@@ -1,0 +1,290 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test checks the oracle against the brute force (a second, dense
+formulation), a library routine, a closed form or a hand computation, so that
+a dropped term, a wrong sign or index or a transposed operand fails one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return (np.random.Generator(np.random.PCG64(seed)).standard_normal(shape) * scale).astype(
+        np.float32)
+
+
+# --------------------------------------------------------------------------- router
+def test_router_matches_dense_bruteforce():
+    x, w = _rand((700, 48), 1), _rand((48, 5), 2, 0.3)
+    r = oracle.route(x, w, want_probs=True)
+    logits, p, g = bf.router(x, w)
+    assert np.all(r["gap"] > 1e-9)  # no ties in this draw
+    np.testing.assert_array_equal(r["group_id"], g)
+    np.testing.assert_allclose(r["probs"], p, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["p_sel"], p[np.arange(700), g], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["prob_sum"], p.sum(0), rtol=1e-13)
+    np.testing.assert_array_equal(r["counts"], np.bincount(g, minlength=5))
+    top2 = np.sort(logits, axis=1)[:, -2:]
+    np.testing.assert_allclose(r["gap"], top2[:, 1] - top2[:, 0], atol=1e-12)
+
+
+def test_router_closed_forms():
+    # one-hot inputs read one row of W: logits = W[j, :]
+    d, m = 6, 4
+    w = np.array([[0, 1, 2, 3], [3, 2, 1, 0], [0, 0, 5, 0], [1, 1, 1, 1],
+                  [-1, 0, 0, 0], [0, 0, 0, 2]], np.float32)
+    x = np.eye(d, dtype=np.float32)
+    r = oracle.route(x, w, want_probs=True)
+    np.testing.assert_array_equal(r["group_id"], [3, 0, 2, 0, 1, 3])  # row 3: tie -> first
+    assert r["gap"][3] == 0.0
+    e = np.exp(np.array([0.0, 1, 2, 3]) - 3)
+    np.testing.assert_allclose(r["probs"][0], e / e.sum(), atol=1e-15)
+    np.testing.assert_allclose(r["probs"][3], 0.25, atol=1e-15)
+    # probabilities are a distribution and the chosen one is the largest
+    x2, w2 = _rand((300, 20), 3), _rand((20, 7), 4)
+    r2 = oracle.route(x2, w2, want_probs=True)
+    np.testing.assert_allclose(r2["probs"].sum(1), 1.0, atol=1e-12)
+    assert np.all(r2["p_sel"] >= 1.0 / 7 - 1e-15)
+    assert np.all(r2["p_sel"] == r2["probs"].max(1))
+
+
+def test_router_single_group_is_exact():
+    r = oracle.route(_rand((100, 8), 5), _rand((8, 1), 6))
+    assert np.all(r["group_id"] == 0) and np.all(r["p_sel"] == 1.0)
+    assert np.all(np.isinf(r["gap"])) and r["counts"][0] == 100
+
+
+def test_router_pins_override():
+    x, w = _rand((50, 8), 7), _rand((8, 3), 8)
+    free = oracle.route(x, w, want_probs=True)
+    pin = np.full(50, -1, np.int32)
+    pin[[3, 10]] = (free["group_id"][[3, 10]] + 1) % 3
+    r = oracle.route(x, w, pin=pin)
+    assert r["group_id"][3] == pin[3] and r["group_id"][10] == pin[10]
+    assert r["p_sel"][3] == free["probs"][3, pin[3]]
+    other = np.setdiff1d(np.arange(50), [3, 10])
+    np.testing.assert_array_equal(r["group_id"][other], free["group_id"][other])
+    np.testing.assert_array_equal(r["counts"], np.bincount(r["group_id"], minlength=3))
+
+
+def test_near_tie_pins():
+    r = {"group_id": np.array([0, 1, 2], np.int32), "gap": np.array([1e-3, 5e-6, 0.0])}
+    np.testing.assert_array_equal(oracle.near_tie_pins(r), [-1, 1, 2])
+
+
+# --------------------------------------------------------------------------- groups
+@pytest.mark.parametrize("m", [1, 3, 7])
+def test_groups_against_stable_sort(m):
+    rng = np.random.Generator(np.random.PCG64(m))
+    g = rng.integers(0, m, 1000).astype(np.int32)
+    if m == 7:
+        g[g == 4] = 5  # an empty group
+    cu, perm = oracle.groups(g, m)
+    counts = np.bincount(g, minlength=m)
+    np.testing.assert_array_equal(cu, np.concatenate([[0], np.cumsum(counts)]))
+    np.testing.assert_array_equal(perm, np.argsort(g, kind="stable"))
+    assert cu[0] == 0 and cu[-1] == len(g) and np.all(np.diff(cu) >= 0)
+    assert np.array_equal(np.sort(perm), np.arange(len(g)))
+    for i in range(m):
+        seg = perm[cu[i]:cu[i + 1]]
+        assert np.all(g[seg] == i) and np.all(np.diff(seg) > 0)
+    # permute then unpermute is the identity (bitwise)
+    data = _rand((len(g), 3), 9)
+    grouped = data[perm]
+    back = np.empty_like(grouped)
+    back[perm] = grouped
+    assert np.array_equal(back, data)
+
+
+def test_groups_rejects_bad_ids():
+    with pytest.raises(ValueError):
+        oracle.groups(np.array([0, 3], np.int32), 2)
+
+
+# --------------------------------------------------------------------------- loss
+def test_loss_hand_example():
+    # Logits chosen so p is (3/4, 1/4) or (1/4, 3/4):  W = I, x = logits.
+    l3 = math.log(3.0)
+    x = np.array([[l3, 0], [0, l3], [l3, 0], [l3, 0]], np.float32)
+    r = oracle.route(x, np.eye(2, dtype=np.float32))
+    loss, F, P = oracle.balance_loss(r["counts"], r["prob_sum"], 4, 0.1)
+    # by hand: F = (3/4, 1/4); P = ((3*.75+.25)/4, (3*.25+.75)/4) = (.625, .375)
+    # L = 0.1 * 2 * (.75*.625 + .25*.375) = 0.1125
+    np.testing.assert_allclose(F, [0.75, 0.25], atol=0)
+    np.testing.assert_allclose(P, [0.625, 0.375], atol=2e-8)  # log(3) rounded to fp32
+    assert abs(loss - 0.1125) < 2e-8
+
+
+@pytest.mark.parametrize("m", [2, 5, 20])
+def test_loss_uniform_assignment_equals_alpha(m):
+    # token t gets the base logits rotated by t mod M, so every group gets N/M tokens
+    base = _rand((m,), 10 + m)
+    n = 40 * m
+    x = np.stack([np.roll(base, t % m) for t in range(n)]).astype(np.float32)
+    r = oracle.route(x, np.eye(m, dtype=np.float32))
+    assert np.all(r["counts"] == n // m)
+    loss, F, P = oracle.balance_loss(r["counts"], r["prob_sum"], n, 0.1)
+    assert abs(loss - 0.1) < 1e-15
+    assert abs(P.sum() - 1.0) < 1e-14
+
+
+def test_loss_single_group_and_collapse():
+    x, w = _rand((64, 8), 11), _rand((8, 1), 12)
+    r = oracle.route(x, w)
+    assert abs(oracle.balance_loss(r["counts"], r["prob_sum"], 64, 0.1)[0] - 0.1) < 1e-15
+    w4 = _rand((8, 4), 13)
+    r4 = oracle.route(x, w4, pin=np.zeros(64, np.int32))  # every token forced to group 0
+    loss, F, P = oracle.balance_loss(r4["counts"], r4["prob_sum"], 64, 0.1)
+    assert F[0] == 1.0 and abs(loss - 0.1 * 4 * P[0]) < 1e-15
+
+
+# --------------------------------------------------------------------------- MoGA attention
+def _moga_case(n, d, m, h, hd, seed):
+    x, w = _rand((n, d), seed), _rand((d, m), seed + 1)
+    q, k, v = (_rand((h, n, hd), seed + 2 + i) for i in range(3))
+    return x, w, q, k, v
+
+
+def test_moga_attention_matches_bruteforce():
+    n, m, h, hd = 300, 4, 2, 16
+    x, w, q, k, v = _moga_case(n, 12, m, h, hd, 20)
+    scale = 1 / math.sqrt(hd)
+    r = oracle.route(x, w)
+    rows_h = np.repeat(np.arange(h), n)
+    rows_t = np.tile(np.arange(n), h)
+    out, pairs = oracle.moga_attn(q, k, v, r["group_id"], m, r["p_sel"], scale, rows_h, rows_t)
+    ref, g, p = bf.moga_forward(x, w, q, k, v, scale)
+    np.testing.assert_array_equal(g, r["group_id"])
+    np.testing.assert_allclose(out.reshape(h, n, hd), ref, rtol=0, atol=1e-12)
+    counts = np.bincount(g, minlength=m)
+    assert pairs == h * int((counts.astype(np.int64) ** 2).sum())
+
+
+def test_single_group_is_full_attention_sdpa():
+    n, h, hd = 257, 3, 32
+    q, k, v = (_rand((h, n, hd), 30 + i) for i in range(3))
+    g = np.zeros(n, np.int32)
+    rows_h, rows_t = np.repeat(np.arange(h), n), np.tile(np.arange(n), h)
+    out, pairs = oracle.moga_attn(q, k, v, g, 1, np.ones(n), 1 / math.sqrt(hd), rows_h, rows_t)
+    tq, tk, tv = (torch.from_numpy(a).double() for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).numpy()
+    np.testing.assert_allclose(out.reshape(h, n, hd), ref, rtol=0, atol=1e-12)
+    assert pairs == h * n * n
+
+
+def test_singleton_group_and_identical_keys():
+    n, hd = 40, 8
+    q, k, v = (_rand((1, n, hd), 40 + i) for i in range(3))
+    g = np.zeros(n, np.int32)
+    g[7] = 1          # token 7 alone in group 1 -> output p * v_7
+    g[20:30] = 2      # group 2 with identical key rows -> p * mean(V of group 2)
+    k[0, 20:30] = k[0, 20]
+    p_sel = np.linspace(0.3, 0.9, n)
+    out, _ = oracle.moga_attn(q, k, v, g, 3, p_sel, 0.5, np.zeros(n), np.arange(n))
+    np.testing.assert_allclose(out[7], p_sel[7] * v[0, 7], atol=1e-15)
+    for t in range(20, 30):
+        np.testing.assert_allclose(out[t], p_sel[t] * v[0, 20:30].astype(np.float64).mean(0),
+                                   atol=1e-14)
+
+
+# --------------------------------------------------------------------------- STGA
+TINY_GRID = dict(frames=6, height=4, width=6, shot_start=[0, 2, 5, 6], win_h=2, win_w=3,
+                 t_group=2, aug_frames=2)
+# shot 1 is a single frame, so shot 2 borrows only one frame from it (clipped)
+SHORT_SHOT_GRID = dict(TINY_GRID, shot_start=[0, 3, 4, 6])
+
+
+@pytest.mark.parametrize("mode", ["temporal", "frame"])
+@pytest.mark.parametrize("aug", [0, 1, 2])
+@pytest.mark.parametrize("layout", ["tiny", "short_shot"])
+def test_stga_matches_bruteforce(mode, aug, layout):
+    grid = dict(TINY_GRID if layout == "tiny" else SHORT_SHOT_GRID, aug_frames=aug)
+    n, h, hd = 144, 2, 8
+    q, k, v = (_rand((h, n, hd), 50 + i) for i in range(3))
+    rows_h, rows_t = np.repeat(np.arange(h), n), np.tile(np.arange(n), h)
+    out, pairs = oracle.stga_attn(q, k, v, grid, mode, 0.3, rows_h, rows_t)
+    mask = bf.stga_mask(grid, mode)
+    ref = np.stack([bf.masked_attention(q[i], k[i], v[i], mask, 0.3) for i in range(h)])
+    np.testing.assert_allclose(out.reshape(h, n, hd), ref, rtol=0, atol=1e-13)
+    assert pairs == h * int(mask.sum())
+    assert oracle.stga_pairs(grid, mode) == int(mask.sum())
+
+
+def test_stga_key_sets_by_hand():
+    g = TINY_GRID  # shots: frames [0,2), [2,5), [5,6); 24 tokens per frame; 2x2 windows of 2x3
+    tok = lambda f, y, x: f * 24 + y * 6 + x
+    # frame 2 is the first chunk of shot 1: own frames 2,3 + shot 0's frames 0,1 (window (0,0))
+    keys = set(oracle.stga_key_list(g, "temporal", tok(2, 1, 1)).tolist())
+    want = {tok(f, y, x) for f in (0, 1, 2, 3) for y in (0, 1) for x in (0, 1, 2)}
+    assert keys == want
+    # frame 4 is the last chunk of shot 1 (single frame): + shot 2's only frame (clipped to 1)
+    keys = set(oracle.stga_key_list(g, "temporal", tok(4, 3, 4)).tolist())
+    assert keys == {tok(f, y, x) for f in (4, 5) for y in (2, 3) for x in (3, 4, 5)}
+    # frame 0: first chunk of shot 0 and last chunk of shot 0 -> + shot 1's frames 2,3
+    keys = set(oracle.stga_key_list(g, "temporal", tok(0, 0, 5)).tolist())
+    assert keys == {tok(f, y, x) for f in (0, 1, 2, 3) for y in (0, 1) for x in (3, 4, 5)}
+    # frame 5 (shot 2, the last): + shot 1's last 2 frames 3,4
+    keys = set(oracle.stga_key_list(g, "temporal", tok(5, 0, 0)).tolist())
+    assert keys == {tok(f, y, x) for f in (3, 4, 5) for y in (0, 1) for x in (0, 1, 2)}
+    # one-frame neighbour shot: shot 2 of SHORT_SHOT_GRID borrows frame 3 only, not frame 2
+    keys = set(oracle.stga_key_list(SHORT_SHOT_GRID, "temporal", tok(4, 0, 0)).tolist())
+    assert keys == {tok(f, y, x) for f in (3, 4, 5) for y in (0, 1) for x in (0, 1, 2)}
+    # per-frame group: all of the frame
+    keys = oracle.stga_key_list(g, "frame", tok(3, 2, 2))
+    assert sorted(keys.tolist()) == list(range(72, 96))
+
+
+def test_stga_degenerate_cases():
+    n, hd = 144, 8
+    q, k, v = (_rand((1, n, hd), 60 + i) for i in range(3))
+    rows_h, rows_t = np.zeros(n), np.arange(n)
+    # whole-frame window, T=1, no augmentation -> temporal groups are the frames
+    g1 = dict(TINY_GRID, win_h=4, win_w=6, t_group=1, aug_frames=0)
+    a, _ = oracle.stga_attn(q, k, v, g1, "temporal", 0.4, rows_h, rows_t)
+    b, _ = oracle.stga_attn(q, k, v, g1, "frame", 0.4, rows_h, rows_t)
+    np.testing.assert_array_equal(a, b)
+    # whole-frame window, T >= shot length, no augmentation -> full attention per shot (SDPA)
+    g2 = dict(TINY_GRID, win_h=4, win_w=6, t_group=8, aug_frames=0)
+    a, _ = oracle.stga_attn(q, k, v, g2, "temporal", 1 / math.sqrt(hd), rows_h, rows_t)
+    shot = np.searchsorted(np.array(g2["shot_start"]), np.arange(n) // 24, side="right")
+    mask = torch.from_numpy(shot[:, None] == shot[None, :])
+    tq, tk, tv = (torch.from_numpy(t[0]).double() for t in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask).numpy()
+    np.testing.assert_allclose(a, ref, atol=1e-12)
+
+
+def test_stga_pair_counts_closed_form_hybrid_30s():
+    # 181 frames of 30x52 in 9 shots (8 x 20 + 21 frames), 15x13 windows, T=4, 2 boundary frames.
+    grid = dict(frames=181, height=30, width=52,
+                shot_start=[(181 * s) // 9 for s in range(10)], win_h=15, win_w=13, t_group=4,
+                aug_frames=2)
+    win = 15 * 13
+    own = 8 * (8 * 5 * (4 * win) ** 2 + 5 * (4 * win) ** 2 + win ** 2)
+    boundary = 8 * (8 * (4 * win) * (2 * win) + 8 * (4 * win) * (2 * win))
+    assert own + boundary == 258_265_800
+    assert oracle.stga_pairs(grid, "temporal") == 258_265_800
+    assert oracle.stga_pairs(grid, "frame") == 181 * 1560 ** 2 == 440_481_600
+
+
+# --------------------------------------------------------------------------- FLOP convention
+def test_flop_convention_reproduces_printed_pflops():
+    from sparse_attention_long_moga_amd.metrics import attention_flops
+    gold = json.load(open(os.path.join(GOLDEN, "pages_flop_convention.json")))
+    model = gold["assumed_model"]
+    heads, hd = 12, model["d_model"] // 12
+    for case in gold["cases"]:
+        n = case["latent_frames"] * case["tokens_per_frame"]
+        # full attention: one group, so the oracle's pair counter gives N^2 per head
+        per_layer = attention_flops(n * n, heads, hd)
+        total = model["layers"] * per_layer + 2 * n * model["params"]
+        assert abs(total / 1e15 - case["pflops_printed"]) < 0.006 * case["pflops_printed"]
