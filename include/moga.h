@@ -1,0 +1,187 @@
+/*
+ * moga.h - C ABI of libmoga.so: the Mixture-of-Groups Attention (MoGA) forward
+ * path with static spatial-temporal group attention (STGA), for AMD MI355X
+ * (gfx950).
+ *
+ * Sources (cited by site and section):
+ *   papernotes.org ICLR 2026 note "MoGA: Mixture-of-Groups Attention for
+ *     End-to-End Long Video Generation", 方法详解 / 关键设计 1-4 ("design 1" ...
+ *     "design 4" below);
+ *   jxzklqfsx.com Chinese translation of the paper, section 方法;
+ *   xugj520.cn MoGA blog, §2.2-2.3 (router), §3.2 and §9 (STGA boundary frames).
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller, unless a comment
+ *     says HOST.  The library never allocates, frees or synchronises.
+ *   - Attention tensors are bf16, row-major [H][rows][head_dim] (head-major: one
+ *     contiguous [rows][head_dim] block per head).
+ *   - `stream` is a hipStream_t (NULL: the legacy default stream).  Each call
+ *     validates its arguments, enqueues kernels on `stream` and returns; results
+ *     are valid once the stream has reached that point.
+ *   - Validation happens before any launch: a call that returns an error has
+ *     enqueued nothing.  Faults during kernel execution surface at the
+ *     caller's next synchronisation, not as a return code.
+ *   - `ws` is caller-owned device scratch of at least the size the matching
+ *     *_workspace_bytes function returns; calls that share a workspace must be
+ *     ordered on one stream.  Its contents need not be initialised.
+ *   - All outputs are bitwise reproducible from run to run (no floating-point
+ *     atomics, fixed reduction orders).
+ *   - moga_last_error() returns a thread-local description of the last
+ *     non-OK status on the calling thread.
+ */
+#ifndef MOGA_H
+#define MOGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOGA_OK = 0,
+    MOGA_ERR_ARG = 1,          /* a NULL required pointer, a size out of range, bad geometry */
+    MOGA_ERR_UNSUPPORTED = 2,  /* the current device is not gfx950, or a shape it does not cover */
+    MOGA_ERR_WORKSPACE = 3,    /* ws is NULL or ws_bytes is below the required size */
+    MOGA_ERR_HIP = 4           /* a HIP runtime call or launch failed; text in moga_last_error() */
+} moga_status;
+
+typedef enum { MOGA_F32 = 0, MOGA_BF16 = 1 } moga_dtype;
+
+/* Problem sizes shared by the calls.
+ *   n_tokens      N, 1 <= N < 2^31
+ *   d_model       router input width d (a multiple of 8 for bf16 x, of 4 for f32 x)
+ *   n_heads       H >= 1
+ *   head_dim      64 or 128
+ *   n_groups      M, 1 <= M <= 64
+ *   softmax_scale attention scale; <= 0 selects 1/sqrt(head_dim)
+ *   alpha         weight of the group-balancing loss (0.1 on the pages) */
+typedef struct {
+    int64_t n_tokens;
+    int32_t d_model;
+    int32_t n_heads;
+    int32_t head_dim;
+    int32_t n_groups;
+    float softmax_scale;
+    double alpha;
+} moga_dims;
+
+/* STGA geometry (design 4).  Tokens are frame-major: token = (f*height + y)*width + x,
+ * so N == frames*height*width.  shot_start is a HOST array of n_shots+1 strictly
+ * increasing frame indices, shot_start[0] == 0 and shot_start[n_shots] == frames;
+ * 1 <= n_shots <= 256.  Spatial windows are win_h x win_w and must tile the frame;
+ * temporal groups are t_group consecutive frames of one shot, starting at the
+ * shot's first frame (a shorter last chunk is its own group).  The keys and
+ * values of the first chunk of shot s > 0 also hold the last aug_frames frames
+ * of shot s-1, and those of the last chunk of shot s < n_shots-1 the first
+ * aug_frames frames of shot s+1 (same window; clipped to the neighbour shot's
+ * length).  Per-frame groups are whole frames. */
+typedef struct {
+    int32_t frames, height, width;
+    int32_t n_shots;
+    const int32_t *shot_start; /* HOST, n_shots + 1 entries */
+    int32_t win_h, win_w;
+    int32_t t_group;
+    int32_t aug_frames;
+} stga_layout;
+
+/* Inputs and outputs of moga_forward. */
+typedef struct {
+    const void *x;        /* [N][d_model], x_dtype */
+    moga_dtype x_dtype;
+    const float *w;       /* router weight [d_model][M] fp32, no bias */
+    const void *q, *k, *v;/* bf16 [H][N][head_dim], token order */
+    const int32_t *pin;   /* NULL or [N]: -1 = free, else the forced group of the token */
+} moga_inputs;
+
+typedef struct {
+    void *out;            /* required, bf16 [H][N][head_dim], token order */
+    double *loss;         /* required, one fp64 scalar: L_gb */
+    int32_t *group_id;    /* optional [N] */
+    float *p_sel;         /* optional [N]: p(g(x)|x) */
+    int32_t *cu_seqlens;  /* optional [M+1] */
+    int32_t *perm;        /* optional [N]: grouped row -> token */
+    int32_t *counts;      /* optional [M] */
+    double *prob_sum;     /* optional [M]: sum over tokens of p(i|x) */
+} moga_outputs;
+
+const char *moga_last_error(void);
+
+/* Workspace bytes needed by moga_forward, moga_route and moga_permute for these
+ * sizes (stga NULL: MoGA only; non-NULL also covers stga_group_attn).  Returns 0
+ * if the sizes are invalid. */
+size_t moga_workspace_bytes(const moga_dims *dims, const stga_layout *stga);
+
+/* Workspace bytes needed by moga_group_attn with n_seg segments and len_q query rows. */
+size_t moga_group_attn_workspace_bytes(const moga_dims *dims, int32_t n_seg, int64_t len_q);
+
+/* Router (design 1; blog §2.3): r = x W in fp32 (no bias), p = softmax(r),
+ * g = argmax r with the lowest index winning exact ties; pin[t] >= 0 overrides g.
+ * Writes group_id [N] (int32), p_sel [N] = p(g|x) (fp32), counts [M] (int32) and
+ * prob_sum [M] = sum over tokens of p(i|x) accumulated in fp64 in a fixed order.
+ * pin may be NULL.  ws: moga_workspace_bytes(dims, NULL). */
+moga_status moga_route(const void *x, moga_dtype x_dtype, const float *w, const int32_t *pin,
+                       const moga_dims *dims, int32_t *group_id, float *p_sel, int32_t *counts,
+                       double *prob_sum, void *ws, size_t ws_bytes, void *stream);
+
+/* Stable permute into contiguous groups, and its inverse (design 2).
+ *   inverse == 0: from group_id [N] (values in [0, M)) compute cu_seqlens [M+1]
+ *     (cu[0] = 0, cu[i+1] = cu[i] + n_i) and perm [N] (grouped row j -> token;
+ *     groups in ascending id, tokens in ascending order within a group), then
+ *     dst[i][h][j] = src[i][h][perm[j]] for each of the n_tensors bf16 tensors
+ *     [H][N][head_dim], and p_perm[j] = p_sel[perm[j]] if both are non-NULL.
+ *   inverse == 1: perm is an input (group_id and cu_seqlens may be NULL) and
+ *     dst[i][h][perm[j]] = src[i][h][j]; p_sel/p_perm are ignored.
+ * src and dst are HOST arrays of n_tensors device pointers, 0 <= n_tensors <= 4;
+ * dst must not overlap src.  Group ids outside [0, M) are an error the library
+ * cannot see: the results are then undefined (no out-of-bounds access occurs).
+ * ws: moga_workspace_bytes(dims, NULL). */
+moga_status moga_permute(int inverse, const int32_t *group_id, const moga_dims *dims,
+                         int32_t *cu_seqlens, int32_t *perm, const void *const *src,
+                         void *const *dst, int n_tensors, const float *p_sel, float *p_perm,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Variable-length group attention (design 1 and 2): for every head h and segment
+ * s, the query rows [cu_q[s], cu_q[s+1]) attend to the key rows [cu_k[s],
+ * cu_k[s+1]):  o = softmax(scale q K^T) V, computed with bf16 MFMA, fp32
+ * accumulation and an fp32 online softmax, then multiplied by row_scale[row]
+ * (if non-NULL) and rounded to bf16.  cu_q and cu_k are DEVICE arrays of
+ * n_seg+1 non-decreasing int32 with cu_q[n_seg] <= len_q and cu_k[n_seg] <= len_k
+ * (rows outside every segment are left untouched; a segment with no keys
+ * writes zeros).  q, o: [H][len_q][head_dim]; k, v: [H][len_k][head_dim];
+ * row_scale: NULL or fp32 [len_q].  ws: moga_group_attn_workspace_bytes. */
+moga_status moga_group_attn(const void *q, const void *k, const void *v, int64_t len_q,
+                            int64_t len_k, int32_t n_seg, const int32_t *cu_q,
+                            const int32_t *cu_k, const float *row_scale, const moga_dims *dims,
+                            void *o, void *ws, size_t ws_bytes, void *stream);
+
+/* STGA (design 4): temporal-window groups with boundary-frame K/V augmentation,
+ * written to o_temporal, and per-frame groups, written to o_frame, both bf16
+ * [H][N][head_dim] in token order and unscaled.  Either output may be NULL to
+ * skip that branch.  q, k, v: bf16 [H][N][head_dim], token order.
+ * ws: moga_workspace_bytes(dims, stga). */
+moga_status stga_group_attn(const void *q, const void *k, const void *v, const moga_dims *dims,
+                            const stga_layout *stga, void *o_temporal, void *o_frame, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* Group-balancing loss (design 3): F_i = counts_i / N, P_i = prob_sum_i / N,
+ * loss = alpha * M * sum_i F_i P_i, all fp64.  P_i is the mean of p(i|x) over
+ * all N tokens.  counts, prob_sum: [M] device inputs; loss: one device fp64;
+ * F, P: NULL or [M] device fp64. */
+moga_status moga_balance_loss(const int32_t *counts, const double *prob_sum,
+                              const moga_dims *dims, double *loss, double *F, double *P,
+                              void *stream);
+
+/* The whole forward: route -> permute -> group attention scaled by p(g|x) ->
+ * inverse permute, plus the balance loss; with stga non-NULL, out is the mean of
+ * the MoGA output and the two STGA outputs (computed in fp32, rounded once).
+ * ws: moga_workspace_bytes(dims, stga). */
+moga_status moga_forward(const moga_inputs *in, const moga_dims *dims, const stga_layout *stga,
+                         const moga_outputs *out, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOGA_H */

@@ -72,6 +72,9 @@ def _load():
     lib.oracle_stga_key_list.argtypes = [c_int, c_int, c_int, c_int, _i32p, c_int, c_int, c_int,
                                          c_int, c_int, c_i64, _i64p]
     lib.oracle_stga_key_list.restype = c_i64
+    lib.oracle_varlen_attn.argtypes = [_f32p, _f32p, _f32p, c_i64, c_i64, c_int, c_int, _i64p,
+                                       _i64p, vp, c_dbl, c_i64, _i32p, _i64p, _f64p]
+    lib.oracle_varlen_attn.restype = c_i64
     _lib = lib
     return lib
 
@@ -170,6 +173,26 @@ def moga_attn(q, k, v, group_id, m: int, p_sel, scale: float, rows_h, rows_t):
                                      rh, rt, out)
     if pairs < 0:
         raise ValueError("oracle_moga_attn failed")
+    return out, int(pairs)
+
+
+def varlen_attn(q, k, v, cu_q, cu_k, scale: float, rows_h, rows_i, row_scale=None):
+    """Segment attention: q row i of segment s attends to key rows [cu_k[s], cu_k[s+1]).
+
+    q: [Hs][Lq][hd], k/v: [Hs][Lk][hd].  Returns (out [rows][hd] f64, pair count).
+    """
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    _, lq, hd = q.shape
+    lk = k.shape[1]
+    cq = np.ascontiguousarray(cu_q, dtype=np.int64)
+    ck = np.ascontiguousarray(cu_k, dtype=np.int64)
+    rs = None if row_scale is None else np.ascontiguousarray(row_scale, dtype=np.float64)
+    rh, ri = _rows(rows_h, rows_i)
+    out = np.empty((rh.shape[0], hd))
+    pairs = _load().oracle_varlen_attn(q, k, v, lq, lk, hd, cq.shape[0] - 1, cq, ck, _ptr(rs),
+                                       float(scale), rh.shape[0], rh, ri, out)
+    if pairs < 0:
+        raise ValueError("oracle_varlen_attn: bad segments")
     return out, int(pairs)
 
 

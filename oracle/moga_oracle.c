@@ -303,3 +303,49 @@ int64_t oracle_stga_key_list(int frames, int height, int width, int n_shots,
     if (!grid_ok(&G)) return -1;
     return stga_keys(&G, mode, t, keys);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Variable-length segment attention ([N] key design 2: the grouped rows are   */
+/* handed to a varlen attention call described by per-segment offsets).        */
+/* Query row i of segment s (cu_q[s] <= i < cu_q[s+1]) attends to the key rows */
+/* [cu_k[s], cu_k[s+1]).  READING: a segment with no keys yields zeros.        */
+/* q holds [heads][len_q][hd], k and v [heads][len_k][hd].  Rows that belong   */
+/* to no segment return -1 in seg_of_row and are left as zeros.                */
+/* ------------------------------------------------------------------------- */
+int64_t oracle_varlen_attn(const float *q, const float *k, const float *v, int64_t len_q,
+                           int64_t len_k, int hd, int n_seg, const int64_t *cu_q,
+                           const int64_t *cu_k, const double *row_scale, double scale,
+                           int64_t n_rows, const int32_t *rows_h, const int64_t *rows_i,
+                           double *out)
+{
+    if (hd < 1 || n_seg < 1) return -1;
+    for (int s = 0; s < n_seg; ++s)
+        if (cu_q[s] > cu_q[s + 1] || cu_k[s] > cu_k[s + 1] || cu_q[s] < 0 || cu_k[s] < 0 ||
+            cu_q[s + 1] > len_q || cu_k[s + 1] > len_k)
+            return -1;
+    int64_t pairs = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(+ : pairs)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t i = rows_i[r];
+        double *o = out + r * (int64_t)hd;
+        for (int c = 0; c < hd; ++c) o[c] = 0.0;
+        int seg = -1;
+        for (int s = 0; s < n_seg; ++s)
+            if (cu_q[s] <= i && i < cu_q[s + 1]) { seg = s; break; }
+        if (seg < 0) continue;
+        const int64_t nk = cu_k[seg + 1] - cu_k[seg];
+        if (nk == 0) continue;
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)nk);
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)nk);
+        for (int64_t a = 0; a < nk; ++a) keys[a] = cu_k[seg] + a;
+        const int64_t h = rows_h[r];
+        attend_row(q + (h * len_q + i) * hd, k + h * len_k * hd, v + h * len_k * hd, hd, keys, nk,
+                   scale, s_buf, o);
+        if (row_scale)
+            for (int c = 0; c < hd; ++c) o[c] *= row_scale[i];
+        pairs += nk;
+        free(keys);
+        free(s_buf);
+    }
+    return pairs;
+}

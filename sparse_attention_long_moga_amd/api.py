@@ -1,0 +1,275 @@
+"""Torch-facing binding of libmoga.so.
+
+Argument marshalling only: each function checks device, dtype, shape and
+contiguity, allocates outputs (and a workspace unless one is passed) with
+torch, and calls the C entry point of the same name on the current HIP stream.
+Every step of the computation runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _capi
+from ._capi import MogaDims, MogaInputs, MogaOutputs, StgaLayout, check
+
+__all__ = ["make_dims", "make_stga_layout", "moga_workspace_bytes", "workspace", "moga_route",
+           "moga_permute", "moga_unpermute", "moga_group_attn", "stga_group_attn",
+           "moga_balance_loss", "moga_forward"]
+
+
+def _lib():
+    return _capi.load()
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_dims(n_tokens: int, d_model: int, n_heads: int, head_dim: int, n_groups: int,
+              alpha: float = 0.1, softmax_scale: float = 0.0) -> MogaDims:
+    return MogaDims(n_tokens, d_model, n_heads, head_dim, n_groups, softmax_scale, alpha)
+
+
+class _Layout:
+    """An stga_layout plus the host array it points into (kept alive here)."""
+
+    def __init__(self, frames, height, width, shot_start: Sequence[int], win_h, win_w, t_group,
+                 aug_frames):
+        self.shots = (ctypes.c_int32 * len(shot_start))(*[int(s) for s in shot_start])
+        self.c = StgaLayout(frames, height, width, len(shot_start) - 1,
+                            ctypes.cast(self.shots, ctypes.POINTER(ctypes.c_int32)), win_h, win_w,
+                            t_group, aug_frames)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def make_stga_layout(frames: int, height: int, width: int, shot_start: Sequence[int], win_h: int,
+                     win_w: int, t_group: int, aug_frames: int) -> _Layout:
+    return _Layout(frames, height, width, shot_start, win_h, win_w, t_group, aug_frames)
+
+
+def moga_workspace_bytes(dims: MogaDims, stga: Optional[_Layout] = None) -> int:
+    n = _lib().moga_workspace_bytes(ctypes.byref(dims), stga.ref() if stga else None)
+    if n == 0:
+        check(_capi.MOGA_ERR_ARG)
+    return int(n)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _ws(ws: Optional[torch.Tensor], nbytes: int, device) -> torch.Tensor:
+    if ws is None:
+        return workspace(nbytes, device)
+    _need(ws, "ws", torch.uint8)
+    return ws
+
+
+def moga_route(x: torch.Tensor, w: torch.Tensor, n_groups: int, pin: Optional[torch.Tensor] = None,
+               ws: Optional[torch.Tensor] = None) -> dict:
+    """Router: group_id [N] int32, p_sel [N] f32, counts [M] int32, prob_sum [M] f64."""
+    _need(x, "x", ndim=2)
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    n, d = x.shape
+    _need(w, "w", torch.float32, 2, x.device)
+    if tuple(w.shape) != (d, n_groups):
+        raise ValueError(f"w must be [{d}, {n_groups}]")
+    if pin is not None:
+        _need(pin, "pin", torch.int32, 1, x.device)
+    dims = make_dims(n, d, 1, 64, n_groups)
+    dev = x.device
+    out = dict(group_id=torch.empty(n, dtype=torch.int32, device=dev),
+               p_sel=torch.empty(n, dtype=torch.float32, device=dev),
+               counts=torch.empty(n_groups, dtype=torch.int32, device=dev),
+               prob_sum=torch.empty(n_groups, dtype=torch.float64, device=dev))
+    nb = moga_workspace_bytes(dims)
+    ws = _ws(ws, nb, dev)
+    check(_lib().moga_route(_ptr(x), _capi.MOGA_BF16 if x.dtype == torch.bfloat16 else _capi.MOGA_F32,
+                            _ptr(w), _ptr(pin), ctypes.byref(dims), _ptr(out["group_id"]),
+                            _ptr(out["p_sel"]), _ptr(out["counts"]), _ptr(out["prob_sum"]),
+                            _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def _heads_shape(ts: Sequence[torch.Tensor]):
+    h, n, hd = ts[0].shape
+    for i, t in enumerate(ts):
+        _need(t, f"tensor {i}", torch.bfloat16, 3, ts[0].device)
+        if tuple(t.shape) != (h, n, hd):
+            raise ValueError("all tensors must share one [H, N, head_dim] shape")
+    return h, n, hd
+
+
+def moga_permute(group_id: torch.Tensor, tensors: Sequence[torch.Tensor], n_groups: int,
+                 p_sel: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Stable permute into groups: returns (cu_seqlens, perm, permuted tensors, p_perm)."""
+    _need(group_id, "group_id", torch.int32, 1)
+    n = group_id.shape[0]
+    dev = group_id.device
+    if tensors:
+        h, nn, hd = _heads_shape(tensors)
+        if nn != n:
+            raise ValueError("tensors must have N rows per head")
+    else:
+        h, hd = 1, 64
+    dims = make_dims(n, 1, h, hd, n_groups)
+    cu = torch.empty(n_groups + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(n, dtype=torch.int32, device=dev)
+    outs = [torch.empty_like(t) for t in tensors]
+    p_perm = None
+    if p_sel is not None:
+        _need(p_sel, "p_sel", torch.float32, 1, dev)
+        p_perm = torch.empty_like(p_sel)
+    src = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in tensors])
+    dst = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in outs])
+    ws = _ws(ws, moga_workspace_bytes(dims), dev)
+    check(_lib().moga_permute(0, _ptr(group_id), ctypes.byref(dims), _ptr(cu), _ptr(perm), src, dst,
+                              len(tensors), _ptr(p_sel), _ptr(p_perm), _ptr(ws), ws.numel(),
+                              _stream()))
+    return cu, perm, outs, p_perm
+
+
+def moga_unpermute(perm: torch.Tensor, tensors: Sequence[torch.Tensor], n_groups: int = 1,
+                   ws: Optional[torch.Tensor] = None):
+    """Inverse permute: out[h][perm[j]] = t[h][j] for each tensor."""
+    _need(perm, "perm", torch.int32, 1)
+    h, n, hd = _heads_shape(tensors)
+    dims = make_dims(n, 1, h, hd, n_groups)
+    outs = [torch.empty_like(t) for t in tensors]
+    src = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in tensors])
+    dst = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in outs])
+    ws = _ws(ws, moga_workspace_bytes(dims), perm.device)
+    check(_lib().moga_permute(1, None, ctypes.byref(dims), None, _ptr(perm), src, dst, len(tensors),
+                              None, None, _ptr(ws), ws.numel(), _stream()))
+    return outs
+
+
+def moga_group_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_q: torch.Tensor,
+                    cu_k: torch.Tensor, row_scale: Optional[torch.Tensor] = None,
+                    softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Varlen group attention: q [H, Lq, hd], k/v [H, Lk, hd] bf16; cu_q/cu_k int32 [S+1]."""
+    _need(q, "q", torch.bfloat16, 3)
+    h, lq, hd = q.shape
+    _need(k, "k", torch.bfloat16, 3, q.device)
+    _need(v, "v", torch.bfloat16, 3, q.device)
+    lk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != h or k.shape[2] != hd:
+        raise ValueError("k and v must be [H, Lk, head_dim] matching q")
+    _need(cu_q, "cu_q", torch.int32, 1, q.device)
+    _need(cu_k, "cu_k", torch.int32, 1, q.device)
+    if cu_q.shape != cu_k.shape:
+        raise ValueError("cu_q and cu_k must have the same length")
+    n_seg = cu_q.shape[0] - 1
+    if row_scale is not None:
+        _need(row_scale, "row_scale", torch.float32, 1, q.device)
+        if row_scale.shape[0] != lq:
+            raise ValueError("row_scale must have len_q entries")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 3, q.device)
+    dims = make_dims(max(lq, 1), 1, h, hd, 1, softmax_scale=softmax_scale)
+    nb = _lib().moga_group_attn_workspace_bytes(ctypes.byref(dims), n_seg, lq)
+    if nb == 0:
+        check(_capi.MOGA_ERR_ARG)
+    ws = _ws(ws, nb, q.device)
+    check(_lib().moga_group_attn(_ptr(q), _ptr(k), _ptr(v), lq, lk, n_seg, _ptr(cu_q), _ptr(cu_k),
+                                 _ptr(row_scale), ctypes.byref(dims), _ptr(out), _ptr(ws),
+                                 ws.numel(), _stream()))
+    return out
+
+
+def stga_group_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: _Layout,
+                    temporal: bool = True, frame: bool = True, softmax_scale: float = 0.0,
+                    ws: Optional[torch.Tensor] = None):
+    """STGA branches in token order: returns (o_temporal or None, o_frame or None)."""
+    h, n, hd = _heads_shape([q, k, v])
+    dims = make_dims(n, 1, h, hd, 1, softmax_scale=softmax_scale)
+    o_t = torch.empty_like(q) if temporal else None
+    o_f = torch.empty_like(q) if frame else None
+    ws = _ws(ws, moga_workspace_bytes(dims, layout), q.device)
+    check(_lib().stga_group_attn(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(dims), layout.ref(),
+                                 _ptr(o_t), _ptr(o_f), _ptr(ws), ws.numel(), _stream()))
+    return o_t, o_f
+
+
+def moga_balance_loss(counts: torch.Tensor, prob_sum: torch.Tensor, n_tokens: int,
+                      alpha: float = 0.1):
+    """L_gb with F and P: returns (loss [1] f64, F [M] f64, P [M] f64) on the device."""
+    _need(counts, "counts", torch.int32, 1)
+    _need(prob_sum, "prob_sum", torch.float64, 1, counts.device)
+    m = counts.shape[0]
+    dims = make_dims(n_tokens, 1, 1, 64, m, alpha=alpha)
+    dev = counts.device
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    F = torch.empty(m, dtype=torch.float64, device=dev)
+    P = torch.empty(m, dtype=torch.float64, device=dev)
+    check(_lib().moga_balance_loss(_ptr(counts), _ptr(prob_sum), ctypes.byref(dims), _ptr(loss),
+                                   _ptr(F), _ptr(P), _stream()))
+    return loss, F, P
+
+
+def moga_forward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                 v: torch.Tensor, n_groups: int, alpha: float = 0.1,
+                 pin: Optional[torch.Tensor] = None, stga: Optional[_Layout] = None,
+                 softmax_scale: float = 0.0, ws: Optional[torch.Tensor] = None,
+                 out: Optional[dict] = None) -> dict:
+    """Whole forward.  Returns a dict with out, loss and the routing tensors
+    (group_id, p_sel, cu_seqlens, perm, counts, prob_sum).  Pass `out` (a dict of
+    preallocated tensors with those keys) and `ws` to run without allocating."""
+    _need(x, "x", ndim=2)
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    n, d = x.shape
+    _need(w, "w", torch.float32, 2, x.device)
+    h, nn, hd = _heads_shape([q, k, v])
+    if nn != n or tuple(w.shape) != (d, n_groups):
+        raise ValueError("shape mismatch between x, w and q/k/v")
+    if pin is not None:
+        _need(pin, "pin", torch.int32, 1, x.device)
+    dims = make_dims(n, d, h, hd, n_groups, alpha=alpha, softmax_scale=softmax_scale)
+    dev = x.device
+    if out is None:
+        out = dict(out=torch.empty_like(q), loss=torch.empty(1, dtype=torch.float64, device=dev),
+                   group_id=torch.empty(n, dtype=torch.int32, device=dev),
+                   p_sel=torch.empty(n, dtype=torch.float32, device=dev),
+                   cu_seqlens=torch.empty(n_groups + 1, dtype=torch.int32, device=dev),
+                   perm=torch.empty(n, dtype=torch.int32, device=dev),
+                   counts=torch.empty(n_groups, dtype=torch.int32, device=dev),
+                   prob_sum=torch.empty(n_groups, dtype=torch.float64, device=dev))
+    ws = _ws(ws, moga_workspace_bytes(dims, stga), dev)
+    ins = MogaInputs(x.data_ptr(), _capi.MOGA_BF16 if x.dtype == torch.bfloat16 else _capi.MOGA_F32,
+                     w.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                     pin.data_ptr() if pin is not None else None)
+    g = lambda key: out[key].data_ptr() if out.get(key) is not None else None
+    outs = MogaOutputs(g("out"), g("loss"), g("group_id"), g("p_sel"), g("cu_seqlens"), g("perm"),
+                       g("counts"), g("prob_sum"))
+    check(_lib().moga_forward(ctypes.byref(ins), ctypes.byref(dims), stga.ref() if stga else None,
+                              ctypes.byref(outs), _ptr(ws), ws.numel(), _stream()))
+    return out

@@ -1,0 +1,455 @@
+// Host side of the C ABI declared in include/moga.h: argument validation (always before
+// any launch), the gfx950 check, workspace carving and the launch sequences.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "moga.h"
+#include "moga_internal.h"
+
+using namespace moga;
+
+namespace {
+
+thread_local std::string g_err;
+
+moga_status fail(moga_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+moga_status hip_fail(hipError_t e, const char *what) {
+    return fail(MOGA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                          \
+    do {                                             \
+        hipError_t _e = (expr);                      \
+        if (_e != hipSuccess) return hip_fail(_e, what); \
+    } while (0)
+
+// ---------------------------------------------------------------- device check
+std::mutex g_dev_mu;
+int g_dev_state[64];  // 0 unknown, 1 gfx950, 2 other
+
+moga_status check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MOGA_ERR_UNSUPPORTED, "no HIP device: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(MOGA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_state[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+        g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    if (g_dev_state[dev] != 1) return fail(MOGA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return MOGA_OK;
+}
+
+// ---------------------------------------------------------------- validation
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moga_status check_dims(const moga_dims *d) {
+    if (!d) return fail(MOGA_ERR_ARG, "dims is NULL");
+    if (d->n_tokens < 1 || d->n_tokens >= (int64_t(1) << 31))
+        return fail(MOGA_ERR_ARG, "n_tokens %lld outside [1, 2^31)", (long long)d->n_tokens);
+    if (d->d_model < 1) return fail(MOGA_ERR_ARG, "d_model %d < 1", d->d_model);
+    if (d->n_heads < 1) return fail(MOGA_ERR_ARG, "n_heads %d < 1", d->n_heads);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(MOGA_ERR_ARG, "head_dim %d is not 64 or 128", d->head_dim);
+    if (d->n_groups < 1 || d->n_groups > kMaxGroups)
+        return fail(MOGA_ERR_ARG, "n_groups %d outside [1, %d]", d->n_groups, kMaxGroups);
+    if (!std::isfinite(d->softmax_scale)) return fail(MOGA_ERR_ARG, "softmax_scale is not finite");
+    if (!std::isfinite(d->alpha)) return fail(MOGA_ERR_ARG, "alpha is not finite");
+    return MOGA_OK;
+}
+
+float scale_of(const moga_dims *d) {
+    return d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
+}
+
+moga_status check_stga(const moga_dims *d, const stga_layout *s, StgaGeom *g) {
+    if (!s) return fail(MOGA_ERR_ARG, "stga layout is NULL");
+    if (s->frames < 1 || s->height < 1 || s->width < 1)
+        return fail(MOGA_ERR_ARG, "stga grid %dx%dx%d has an empty side", s->frames, s->height, s->width);
+    if ((int64_t)s->frames * s->height * s->width != d->n_tokens)
+        return fail(MOGA_ERR_ARG, "frames*height*width = %lld != n_tokens %lld",
+                    (long long)((int64_t)s->frames * s->height * s->width), (long long)d->n_tokens);
+    if (s->n_shots < 1 || s->n_shots > kMaxShots)
+        return fail(MOGA_ERR_ARG, "n_shots %d outside [1, %d]", s->n_shots, kMaxShots);
+    if (!s->shot_start) return fail(MOGA_ERR_ARG, "shot_start is NULL");
+    if (s->shot_start[0] != 0 || s->shot_start[s->n_shots] != s->frames)
+        return fail(MOGA_ERR_ARG, "shot_start must begin at 0 and end at frames");
+    for (int i = 0; i < s->n_shots; ++i)
+        if (s->shot_start[i + 1] <= s->shot_start[i])
+            return fail(MOGA_ERR_ARG, "shot_start is not strictly increasing at %d", i);
+    if (s->win_h < 1 || s->win_w < 1 || s->height % s->win_h || s->width % s->win_w)
+        return fail(MOGA_ERR_ARG, "window %dx%d does not tile the %dx%d frame", s->win_h, s->win_w,
+                    s->height, s->width);
+    if (s->t_group < 1) return fail(MOGA_ERR_ARG, "t_group %d < 1", s->t_group);
+    if (s->aug_frames < 0) return fail(MOGA_ERR_ARG, "aug_frames %d < 0", s->aug_frames);
+    std::memset(g, 0, sizeof *g);
+    g->frames = s->frames; g->height = s->height; g->width = s->width; g->n_shots = s->n_shots;
+    g->win_h = s->win_h; g->win_w = s->win_w; g->t_group = s->t_group; g->aug = s->aug_frames;
+    for (int i = 0; i <= s->n_shots; ++i) g->shot_start[i] = s->shot_start[i];
+    if (d->n_tokens + stga_extra_rows(*g) >= (int64_t(1) << 31))
+        return fail(MOGA_ERR_ARG, "n_tokens plus borrowed key rows reaches 2^31");
+    return MOGA_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct Carver {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    }
+};
+
+struct Layout {
+    // MoGA
+    size_t part_p, part_c, gid, psel, counts, probsum, cu, perm, table, base_rel, totals, pperm;
+    size_t qp, kp, vp, op, plan;
+    // STGA
+    size_t shot_info, cu_tq, cu_tk, cu_f, q_idx, kv_idx, ot, of;
+    int32_t plan_seg;
+    int64_t plan_items;
+    size_t total;
+};
+
+Layout make_layout(const moga_dims *d, const StgaGeom *g) {
+    Layout L{};
+    Carver c;
+    const int64_t n = d->n_tokens;
+    const int m = d->n_groups;
+    const int64_t nbr = route_blocks(n), nbp = permute_blocks(n);
+    const size_t tensor = (size_t)d->n_heads * n * d->head_dim * sizeof(uint16_t);
+    L.part_p = c.take(sizeof(double) * nbr * kMaxGroups);
+    L.part_c = c.take(sizeof(int32_t) * nbr * kMaxGroups);
+    L.gid = c.take(sizeof(int32_t) * n);
+    L.psel = c.take(sizeof(float) * n);
+    L.counts = c.take(sizeof(int32_t) * m);
+    L.probsum = c.take(sizeof(double) * m);
+    L.cu = c.take(sizeof(int32_t) * (m + 1));
+    L.perm = c.take(sizeof(int32_t) * n);
+    L.table = c.take(sizeof(int32_t) * nbp * m);
+    L.base_rel = c.take(sizeof(int32_t) * nbp * m);
+    L.totals = c.take(sizeof(int32_t) * m);
+    L.pperm = c.take(sizeof(float) * n);
+    L.qp = c.take(tensor);
+    L.kp = c.take(tensor);
+    L.vp = c.take(tensor);
+    L.op = c.take(tensor);
+    int32_t seg = m;
+    int64_t items = attn_max_items(d->n_heads, n, m);
+    if (g) {
+        const int32_t ng = stga_n_groups(*g);
+        const int64_t extra = stga_extra_rows(*g);
+        L.shot_info = c.take(sizeof(int32_t) * 6 * g->n_shots);
+        L.cu_tq = c.take(sizeof(int32_t) * (ng + 1));
+        L.cu_tk = c.take(sizeof(int32_t) * (ng + 1));
+        L.cu_f = c.take(sizeof(int32_t) * (g->frames + 1));
+        L.q_idx = c.take(sizeof(int32_t) * n);
+        L.kv_idx = c.take(sizeof(int32_t) * (n + extra));
+        L.ot = c.take(tensor);
+        L.of = c.take(tensor);
+        seg = std::max(seg, std::max(ng, g->frames));
+        items = std::max(items, std::max(attn_max_items(d->n_heads, n, ng),
+                                         attn_max_items(d->n_heads, n, g->frames)));
+    }
+    L.plan_seg = seg;
+    L.plan_items = items;
+    L.plan = c.take(attn_plan_bytes(seg, items));
+    L.total = c.off;
+    return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+moga_status check_ws(void *ws, size_t have, size_t need) {
+    if (!ws) return fail(MOGA_ERR_WORKSPACE, "workspace is NULL");
+    if (have < need)
+        return fail(MOGA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(MOGA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    return MOGA_OK;
+}
+
+moga_status check_route_args(const void *x, moga_dtype xt, const float *w, const moga_dims *d) {
+    if (!x || !w) return fail(MOGA_ERR_ARG, "x or w is NULL");
+    if (xt != MOGA_F32 && xt != MOGA_BF16) return fail(MOGA_ERR_ARG, "x_dtype %d unknown", (int)xt);
+    const int vec = xt == MOGA_BF16 ? 8 : 4;
+    if (d->d_model % vec)
+        return fail(MOGA_ERR_UNSUPPORTED, "d_model %d is not a multiple of %d", d->d_model, vec);
+    if (!aligned16(x)) return fail(MOGA_ERR_ARG, "x is not 16-byte aligned");
+    return MOGA_OK;
+}
+
+moga_status run_route(const void *x, moga_dtype xt, const float *w, const int32_t *pin,
+                      const moga_dims *d, int32_t *gid, float *psel, int32_t *counts,
+                      double *prob_sum, void *ws, const Layout &L, hipStream_t s) {
+    RouteLaunch r{};
+    r.x = x; r.x_is_bf16 = xt == MOGA_BF16; r.w = w; r.pin = pin; r.n = d->n_tokens;
+    r.d = d->d_model; r.m = d->n_groups; r.group_id = gid; r.p_sel = psel;
+    r.part_p = at<double>(ws, L.part_p); r.part_c = at<int32_t>(ws, L.part_c);
+    r.counts = counts; r.prob_sum = prob_sum;
+    HIP_TRY(launch_route(r, s), "route launch");
+    return MOGA_OK;
+}
+
+moga_status run_perm_index(const int32_t *gid, const moga_dims *d, int32_t *cu, int32_t *perm,
+                           void *ws, const Layout &L, hipStream_t s) {
+    PermuteLaunch p{};
+    p.group_id = gid; p.n = d->n_tokens; p.m = d->n_groups;
+    p.table = at<int32_t>(ws, L.table); p.base_rel = at<int32_t>(ws, L.base_rel);
+    p.totals = at<int32_t>(ws, L.totals); p.cu = cu; p.perm = perm;
+    HIP_TRY(launch_perm_index(p, s), "permute index launch");
+    return MOGA_OK;
+}
+
+moga_status run_gather(int inverse, const int32_t *perm, const moga_dims *d,
+                       const void *const *src, void *const *dst, int nt, const float *p_sel,
+                       float *p_perm, hipStream_t s) {
+    GatherLaunch g{};
+    for (int i = 0; i < nt; ++i) { g.src[i] = src[i]; g.dst[i] = dst[i]; }
+    g.n_tensors = nt; g.perm = perm; g.n = d->n_tokens; g.n_heads = d->n_heads;
+    g.head_dim = d->head_dim; g.inverse = inverse; g.p_sel = p_sel; g.p_perm = p_perm;
+    HIP_TRY(launch_gather(g, s), "gather launch");
+    return MOGA_OK;
+}
+
+moga_status run_attn(const void *q, const void *k, const void *v, void *o, const int32_t *cu_q,
+                     const int32_t *cu_k, int32_t n_seg, const int32_t *q_idx,
+                     const int32_t *kv_idx, const float *row_scale, int64_t len_q, int64_t len_k,
+                     int64_t q_rows, int64_t kv_rows, int64_t o_rows, const moga_dims *d,
+                     void *plan_mem, int32_t plan_seg, int64_t plan_items, hipStream_t s) {
+    AttnLaunch a{};
+    a.q = static_cast<const bf16 *>(q); a.k = static_cast<const bf16 *>(k);
+    a.v = static_cast<const bf16 *>(v); a.o = static_cast<bf16 *>(o);
+    a.cu_q = cu_q; a.cu_k = cu_k; a.n_seg = n_seg; a.q_idx = q_idx; a.kv_idx = kv_idx;
+    a.row_scale = row_scale; a.len_q = len_q; a.len_k = len_k;
+    a.q_rows = q_rows; a.kv_rows = kv_rows; a.o_rows = o_rows;
+    a.n_heads = d->n_heads; a.head_dim = d->head_dim; a.scale = scale_of(d);
+    a.max_items = attn_max_items(d->n_heads, len_q, n_seg);
+    if (a.max_items > plan_items || n_seg > plan_seg)
+        return fail(MOGA_ERR_WORKSPACE, "attention plan larger than its workspace region");
+    attn_plan_carve(a.plan, plan_mem, n_seg, a.max_items);
+    HIP_TRY(launch_attention(a, s), "attention launch");
+    return MOGA_OK;
+}
+
+moga_status run_stga(const void *q, const void *k, const void *v, const moga_dims *d,
+                     const StgaGeom &g, void *o_t, void *o_f, void *ws, const Layout &L,
+                     hipStream_t s) {
+    StgaBuffers b{};
+    b.shot_info = at<int32_t>(ws, L.shot_info); b.cu_tq = at<int32_t>(ws, L.cu_tq);
+    b.cu_tk = at<int32_t>(ws, L.cu_tk); b.cu_f = at<int32_t>(ws, L.cu_f);
+    b.q_idx = at<int32_t>(ws, L.q_idx); b.kv_idx = at<int32_t>(ws, L.kv_idx);
+    HIP_TRY(launch_stga_index(g, b, s), "stga index launch");
+    const int64_t n = d->n_tokens;
+    void *plan = at<char>(ws, L.plan);
+    if (o_t) {
+        const int32_t ng = stga_n_groups(g);
+        moga_status st = run_attn(q, k, v, o_t, b.cu_tq, b.cu_tk, ng, b.q_idx, b.kv_idx, nullptr, n,
+                                  n + stga_extra_rows(g), n, n, n, d, plan, L.plan_seg,
+                                  L.plan_items, s);
+        if (st != MOGA_OK) return st;
+    }
+    if (o_f) {
+        moga_status st = run_attn(q, k, v, o_f, b.cu_f, b.cu_f, g.frames, nullptr, nullptr, nullptr,
+                                  n, n, n, n, n, d, plan, L.plan_seg, L.plan_items, s);
+        if (st != MOGA_OK) return st;
+    }
+    return MOGA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moga_last_error(void) { return g_err.c_str(); }
+
+size_t moga_workspace_bytes(const moga_dims *dims, const stga_layout *stga) {
+    if (check_dims(dims) != MOGA_OK) return 0;
+    StgaGeom g;
+    if (stga && check_stga(dims, stga, &g) != MOGA_OK) return 0;
+    return make_layout(dims, stga ? &g : nullptr).total;
+}
+
+size_t moga_group_attn_workspace_bytes(const moga_dims *dims, int32_t n_seg, int64_t len_q) {
+    if (check_dims(dims) != MOGA_OK || n_seg < 1 || len_q < 0) return 0;
+    return attn_plan_bytes(n_seg, attn_max_items(dims->n_heads, len_q, n_seg));
+}
+
+moga_status moga_route(const void *x, moga_dtype x_dtype, const float *w, const int32_t *pin,
+                       const moga_dims *dims, int32_t *group_id, float *p_sel, int32_t *counts,
+                       double *prob_sum, void *ws, size_t ws_bytes, void *stream) {
+    moga_status st = check_dims(dims);
+    if (st != MOGA_OK) return st;
+    if ((st = check_route_args(x, x_dtype, w, dims)) != MOGA_OK) return st;
+    if (!group_id || !p_sel || !counts || !prob_sum)
+        return fail(MOGA_ERR_ARG, "an output pointer is NULL");
+    const Layout L = make_layout(dims, nullptr);
+    if ((st = check_ws(ws, ws_bytes, L.gid)) != MOGA_OK) return st;  // the router partials only
+    if ((st = check_device()) != MOGA_OK) return st;
+    return run_route(x, x_dtype, w, pin, dims, group_id, p_sel, counts, prob_sum, ws, L,
+                     static_cast<hipStream_t>(stream));
+}
+
+moga_status moga_permute(int inverse, const int32_t *group_id, const moga_dims *dims,
+                         int32_t *cu_seqlens, int32_t *perm, const void *const *src,
+                         void *const *dst, int n_tensors, const float *p_sel, float *p_perm,
+                         void *ws, size_t ws_bytes, void *stream) {
+    moga_status st = check_dims(dims);
+    if (st != MOGA_OK) return st;
+    if (inverse != 0 && inverse != 1) return fail(MOGA_ERR_ARG, "inverse must be 0 or 1");
+    if (!perm) return fail(MOGA_ERR_ARG, "perm is NULL");
+    if (!inverse && (!group_id || !cu_seqlens))
+        return fail(MOGA_ERR_ARG, "group_id or cu_seqlens is NULL");
+    if (n_tensors < 0 || n_tensors > 4) return fail(MOGA_ERR_ARG, "n_tensors %d outside [0, 4]", n_tensors);
+    if (n_tensors > 0 && (!src || !dst)) return fail(MOGA_ERR_ARG, "src or dst is NULL");
+    for (int i = 0; i < n_tensors; ++i) {
+        if (!src[i] || !dst[i]) return fail(MOGA_ERR_ARG, "tensor %d pointer is NULL", i);
+        if (!aligned16(src[i]) || !aligned16(dst[i]))
+            return fail(MOGA_ERR_ARG, "tensor %d is not 16-byte aligned", i);
+        if (src[i] == dst[i]) return fail(MOGA_ERR_ARG, "tensor %d: dst aliases src", i);
+    }
+    const Layout L = make_layout(dims, nullptr);
+    if ((st = check_ws(ws, ws_bytes, L.pperm)) != MOGA_OK) return st;  // up to the scan tables
+    if ((st = check_device()) != MOGA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!inverse && (st = run_perm_index(group_id, dims, cu_seqlens, perm, ws, L, s)) != MOGA_OK)
+        return st;
+    return run_gather(inverse, perm, dims, src, dst, n_tensors, inverse ? nullptr : p_sel,
+                      inverse ? nullptr : p_perm, s);
+}
+
+moga_status moga_group_attn(const void *q, const void *k, const void *v, int64_t len_q,
+                            int64_t len_k, int32_t n_seg, const int32_t *cu_q,
+                            const int32_t *cu_k, const float *row_scale, const moga_dims *dims,
+                            void *o, void *ws, size_t ws_bytes, void *stream) {
+    moga_status st = check_dims(dims);
+    if (st != MOGA_OK) return st;
+    if (!q || !k || !v || !o || !cu_q || !cu_k) return fail(MOGA_ERR_ARG, "a required pointer is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(MOGA_ERR_ARG, "q, k, v and o must be 16-byte aligned");
+    if (len_q < 0 || len_q >= (int64_t(1) << 31) || len_k < 0 || len_k >= (int64_t(1) << 31))
+        return fail(MOGA_ERR_ARG, "len_q/len_k outside [0, 2^31)");
+    if (n_seg < 1) return fail(MOGA_ERR_ARG, "n_seg %d < 1", n_seg);
+    const int64_t items = attn_max_items(dims->n_heads, len_q, n_seg);
+    if (items >= (int64_t(1) << 31)) return fail(MOGA_ERR_ARG, "too many work items");
+    const size_t need = attn_plan_bytes(n_seg, items);
+    if ((st = check_ws(ws, ws_bytes, need)) != MOGA_OK) return st;
+    if ((st = check_device()) != MOGA_OK) return st;
+    return run_attn(q, k, v, o, cu_q, cu_k, n_seg, nullptr, nullptr, row_scale, len_q, len_k, len_q,
+                    len_k, len_q, dims, ws, n_seg, items, static_cast<hipStream_t>(stream));
+}
+
+moga_status stga_group_attn(const void *q, const void *k, const void *v, const moga_dims *dims,
+                            const stga_layout *stga, void *o_temporal, void *o_frame, void *ws,
+                            size_t ws_bytes, void *stream) {
+    moga_status st = check_dims(dims);
+    if (st != MOGA_OK) return st;
+    StgaGeom g;
+    if ((st = check_stga(dims, stga, &g)) != MOGA_OK) return st;
+    if (!q || !k || !v) return fail(MOGA_ERR_ARG, "q, k or v is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_temporal) ||
+        !aligned16(o_frame))
+        return fail(MOGA_ERR_ARG, "tensors must be 16-byte aligned");
+    const Layout L = make_layout(dims, &g);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != MOGA_OK) return st;
+    if ((st = check_device()) != MOGA_OK) return st;
+    return run_stga(q, k, v, dims, g, o_temporal, o_frame, ws, L, static_cast<hipStream_t>(stream));
+}
+
+moga_status moga_balance_loss(const int32_t *counts, const double *prob_sum,
+                              const moga_dims *dims, double *loss, double *F, double *P,
+                              void *stream) {
+    moga_status st = check_dims(dims);
+    if (st != MOGA_OK) return st;
+    if (!counts || !prob_sum || !loss) return fail(MOGA_ERR_ARG, "counts, prob_sum or loss is NULL");
+    if ((st = check_device()) != MOGA_OK) return st;
+    HIP_TRY(launch_balance_loss(counts, prob_sum, dims->n_tokens, dims->n_groups, dims->alpha, loss,
+                                F, P, static_cast<hipStream_t>(stream)),
+            "loss launch");
+    return MOGA_OK;
+}
+
+moga_status moga_forward(const moga_inputs *in, const moga_dims *dims, const stga_layout *stga,
+                         const moga_outputs *out, void *ws, size_t ws_bytes, void *stream) {
+    moga_status st = check_dims(dims);
+    if (st != MOGA_OK) return st;
+    if (!in || !out) return fail(MOGA_ERR_ARG, "inputs or outputs is NULL");
+    if ((st = check_route_args(in->x, in->x_dtype, in->w, dims)) != MOGA_OK) return st;
+    if (!in->q || !in->k || !in->v) return fail(MOGA_ERR_ARG, "q, k or v is NULL");
+    if (!out->out || !out->loss) return fail(MOGA_ERR_ARG, "out or loss is NULL");
+    if (!aligned16(in->q) || !aligned16(in->k) || !aligned16(in->v) || !aligned16(out->out))
+        return fail(MOGA_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+    StgaGeom g;
+    if (stga && (st = check_stga(dims, stga, &g)) != MOGA_OK) return st;
+    const Layout L = make_layout(dims, stga ? &g : nullptr);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != MOGA_OK) return st;
+    if ((st = check_device()) != MOGA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = dims->n_tokens;
+
+    int32_t *gid = out->group_id ? out->group_id : at<int32_t>(ws, L.gid);
+    float *psel = out->p_sel ? out->p_sel : at<float>(ws, L.psel);
+    int32_t *counts = out->counts ? out->counts : at<int32_t>(ws, L.counts);
+    double *probsum = out->prob_sum ? out->prob_sum : at<double>(ws, L.probsum);
+    int32_t *cu = out->cu_seqlens ? out->cu_seqlens : at<int32_t>(ws, L.cu);
+    int32_t *perm = out->perm ? out->perm : at<int32_t>(ws, L.perm);
+    float *pperm = at<float>(ws, L.pperm);
+    void *qp = at<char>(ws, L.qp), *kp = at<char>(ws, L.kp), *vp = at<char>(ws, L.vp);
+    void *op = at<char>(ws, L.op);
+
+    // 1 route  2 histogram/scan/stable permutation  3 gather Q,K,V and p by perm
+    if ((st = run_route(in->x, in->x_dtype, in->w, in->pin, dims, gid, psel, counts, probsum, ws,
+                        L, s)) != MOGA_OK)
+        return st;
+    if ((st = run_perm_index(gid, dims, cu, perm, ws, L, s)) != MOGA_OK) return st;
+    const void *src[3] = {in->q, in->k, in->v};
+    void *dst[3] = {qp, kp, vp};
+    if ((st = run_gather(0, perm, dims, src, dst, 3, psel, pperm, s)) != MOGA_OK) return st;
+    // 4 varlen group attention scaled by p(g|x)  5 back to token order
+    if ((st = run_attn(qp, kp, vp, op, cu, cu, dims->n_groups, nullptr, nullptr, pperm, n, n, n, n,
+                       n, dims, at<char>(ws, L.plan), L.plan_seg, L.plan_items, s)) != MOGA_OK)
+        return st;
+    const void *osrc[1] = {op};
+    void *odst[1] = {out->out};
+    if ((st = run_gather(1, perm, dims, osrc, odst, 1, nullptr, nullptr, s)) != MOGA_OK) return st;
+    // 6 group-balancing loss
+    HIP_TRY(launch_balance_loss(counts, probsum, n, dims->n_groups, dims->alpha, out->loss, nullptr,
+                                nullptr, s),
+            "loss launch");
+    if (!stga) return MOGA_OK;
+    // 7 STGA branches and the mean of the three outputs
+    void *ot = at<char>(ws, L.ot), *of = at<char>(ws, L.of);
+    if ((st = run_stga(in->q, in->k, in->v, dims, g, ot, of, ws, L, s)) != MOGA_OK) return st;
+    HIP_TRY(launch_combine3(static_cast<const bf16 *>(out->out), static_cast<const bf16 *>(ot),
+                            static_cast<const bf16 *>(of), static_cast<bf16 *>(out->out),
+                            (int64_t)dims->n_heads * n * dims->head_dim, s),
+            "combine launch");
+    return MOGA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Internal declarations shared by the HIP translation units of libmoga.so.
+// Not part of the public ABI (that is include/moga.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moga {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxGroups = 64;    // M <= 64
+constexpr int kMaxShots = 256;    // STGA shots passed by value
+constexpr int kAttnBQ = 128;      // query rows per attention work item (4 waves x 32)
+constexpr int kAttnThreads = 256;
+constexpr int kPermTokensPerBlock = 2048;
+constexpr int kRouteTokensPerBlock = 256;
+constexpr int kPlanSortMax = 4096; // segments sorted by key length up to this count
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- router
+struct RouteLaunch {
+    const void *x;
+    int x_is_bf16;
+    const float *w;
+    const int32_t *pin;
+    int64_t n;
+    int d, m;
+    int32_t *group_id;
+    float *p_sel;
+    double *part_p;   // [nblk][kMaxGroups]
+    int32_t *part_c;  // [nblk][kMaxGroups]
+    int32_t *counts;  // [m]
+    double *prob_sum; // [m]
+};
+int64_t route_blocks(int64_t n);
+hipError_t launch_route(const RouteLaunch &a, hipStream_t s);
+
+// ---------------------------------------------------------------- permute
+struct PermuteLaunch {
+    const int32_t *group_id;
+    int64_t n;
+    int m;
+    int32_t *table;     // [nblk][m] per-block counts
+    int32_t *base_rel;  // [nblk][m] exclusive prefix over blocks, per group
+    int32_t *totals;    // [m]
+    int32_t *cu;        // [m+1]
+    int32_t *perm;      // [n]
+};
+int64_t permute_blocks(int64_t n);
+hipError_t launch_perm_index(const PermuteLaunch &a, hipStream_t s);
+
+// dst[i][h][j] = src[i][h][perm[j]] (inverse == 0) or dst[i][h][perm[j]] = src[i][h][j]
+struct GatherLaunch {
+    const void *src[4];
+    void *dst[4];
+    int n_tensors;
+    const int32_t *perm;
+    int64_t n;
+    int n_heads, head_dim;
+    int inverse;
+    const float *p_sel;  // optional gather of one fp32 value per row (inverse == 0 only)
+    float *p_perm;
+};
+hipError_t launch_gather(const GatherLaunch &a, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnPlan {
+    int32_t *seg_klen;   // [n_seg]
+    int32_t *seg_ntile;  // [n_seg]
+    int32_t *order;      // [n_seg] segments by descending key length
+    int32_t *item_base;  // [n_seg + 1]
+    int4 *items;         // [max_items] (segment, head, q tile, 0)
+    int32_t *counter;    // [2]: dispatch counter, item count
+};
+size_t attn_plan_bytes(int32_t n_seg, int64_t max_items);
+int64_t attn_max_items(int n_heads, int64_t len_q, int32_t n_seg);
+void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items);
+
+struct AttnLaunch {
+    const bf16 *q, *k, *v;
+    bf16 *o;
+    const int32_t *cu_q, *cu_k;
+    int32_t n_seg;
+    const int32_t *q_idx;    // NULL or logical q row -> physical row of q, o and row_scale
+    const int32_t *kv_idx;   // NULL or logical kv row -> physical row of k, v
+    const float *row_scale;  // NULL or [physical q rows]
+    int64_t len_q, len_k;    // logical rows
+    int64_t q_rows, kv_rows, o_rows;  // physical rows per head
+    int n_heads, head_dim;
+    float scale;
+    AttnPlan plan;
+    int64_t max_items;
+};
+hipError_t launch_attention(const AttnLaunch &a, hipStream_t s);
+
+// ---------------------------------------------------------------- STGA
+struct StgaGeom {
+    int32_t frames, height, width, n_shots, win_h, win_w, t_group, aug;
+    int32_t shot_start[kMaxShots + 1];
+};
+struct StgaBuffers {
+    int32_t *shot_info;  // [n_shots][6]: start, len, chunk_base, aug_base, aug_prev, aug_next
+    int32_t *cu_tq;      // [n_groups + 1]
+    int32_t *cu_tk;      // [n_groups + 1]
+    int32_t *cu_f;       // [frames + 1]
+    int32_t *q_idx;      // [N]
+    int32_t *kv_idx;     // [N + extra]
+};
+int32_t stga_n_groups(const StgaGeom &g);
+int64_t stga_extra_rows(const StgaGeom &g);
+hipError_t launch_stga_index(const StgaGeom &g, const StgaBuffers &b, hipStream_t s);
+
+hipError_t launch_combine3(const bf16 *a, const bf16 *b, const bf16 *c, bf16 *out, int64_t n_elem,
+                           hipStream_t s);
+
+// ---------------------------------------------------------------- loss
+hipError_t launch_balance_loss(const int32_t *counts, const double *prob_sum, int64_t n, int m,
+                               double alpha, double *loss, double *F, double *P, hipStream_t s);
+
+}  // namespace moga

@@ -1,0 +1,189 @@
+// Group histogram, scan and stable permutation (papernotes.org MoGA note, 关键设计 2:
+// tokens of one group are made contiguous before a varlen attention call described by
+// per-group offsets, and put back in token order afterwards).
+//
+// A counting sort with no atomics deciding positions:
+//   hist    - block b counts the group ids of its kPermTokensPerBlock tokens with wave
+//             ballots (lane i accumulates group i) -> table[b][i];
+//   scan    - one block per group: exclusive prefix of table[.][i] over blocks;
+//   scatter - cu = prefix of group totals; every token's position is
+//             cu[g] + (tokens of g in earlier blocks) + (earlier in this block), the
+//             in-block part from ballots and popcounts, so equal ids keep token order.
+// The row gathers then move whole head_dim rows (128 or 256 bytes) with 16-byte lanes.
+#include "moga_internal.h"
+
+namespace moga {
+namespace {
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t *gid, int64_t n, int m,
+                                                    int32_t *table) {
+    __shared__ int wc[4][kMaxGroups];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t b0 = (int64_t)blockIdx.x * kPermTokensPerBlock;
+    int cnt = 0;  // lane i counts group i
+    for (int64_t t = b0 + threadIdx.x; t < b0 + kPermTokensPerBlock; t += 256) {
+        const int g = t < n ? gid[t] : -1;
+        for (int i = 0; i < m; ++i) {
+            const uint64_t bal = __ballot(g == i);
+            if (lane == i) cnt += __popcll(bal);
+        }
+    }
+    wc[wave][lane] = cnt;
+    __syncthreads();
+    if (threadIdx.x < m)
+        table[(int64_t)blockIdx.x * m + threadIdx.x] =
+            wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] + wc[3][threadIdx.x];
+}
+
+// Block i: base_rel[b][i] = sum_{b' < b} table[b'][i]; totals[i] = sum over all blocks.
+__global__ __launch_bounds__(256) void scan_kernel(const int32_t *table, int64_t nblk, int m,
+                                                    int32_t *base_rel, int32_t *totals) {
+    __shared__ int s[256];
+    const int g = blockIdx.x;
+    int carry = 0;
+    for (int64_t c0 = 0; c0 < nblk; c0 += 256) {
+        const int64_t b = c0 + threadIdx.x;
+        const int v = b < nblk ? table[b * m + g] : 0;
+        s[threadIdx.x] = v;
+        __syncthreads();
+        // Hillis-Steele inclusive scan over 256 entries
+        for (int off = 1; off < 256; off <<= 1) {
+            const int add = threadIdx.x >= off ? s[threadIdx.x - off] : 0;
+            __syncthreads();
+            s[threadIdx.x] += add;
+            __syncthreads();
+        }
+        if (b < nblk) base_rel[b * m + g] = carry + s[threadIdx.x] - v;
+        carry += s[255];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) totals[g] = carry;
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t *gid, int64_t n, int m,
+                                                       const int32_t *base_rel,
+                                                       const int32_t *totals, int32_t *cu,
+                                                       int32_t *perm) {
+    __shared__ int base[kMaxGroups];
+    __shared__ int wc[4][kMaxGroups];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0) {
+        int acc = 0;
+        for (int i = 0; i < m; ++i) {
+            base[i] = acc + base_rel[(int64_t)blockIdx.x * m + i];
+            if (blockIdx.x == 0) cu[i] = acc;
+            acc += totals[i];
+        }
+        if (blockIdx.x == 0) cu[m] = acc;
+    }
+    __syncthreads();
+    const int64_t b0 = (int64_t)blockIdx.x * kPermTokensPerBlock;
+    for (int64_t c0 = b0; c0 < b0 + kPermTokensPerBlock; c0 += 256) {
+        const int64_t t = c0 + threadIdx.x;
+        const int g = t < n ? gid[t] : -1;
+        int rank = 0;
+        for (int i = 0; i < m; ++i) {
+            const uint64_t bal = __ballot(g == i);
+            if (g == i) rank = __popcll(bal & lanemask_lt(lane));
+            if (lane == i) wc[wave][i] = __popcll(bal);
+        }
+        __syncthreads();
+        if (g >= 0 && g < m) {
+            int pos = base[g] + rank;
+            for (int w = 0; w < wave; ++w) pos += wc[w][g];
+            perm[pos] = (int32_t)t;
+        }
+        __syncthreads();
+        if (threadIdx.x < m)
+            base[threadIdx.x] += wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] +
+                                 wc[3][threadIdx.x];
+        __syncthreads();
+    }
+}
+
+// Row gather/scatter.  grid = (row blocks, heads, tensors); each thread moves 16 bytes.
+template <int HD>
+__global__ __launch_bounds__(256) void gather_kernel(GatherLaunch a) {
+    constexpr int CH = HD * 2 / 16;         // 16-byte chunks per row
+    constexpr int ROWS = 256 / CH;          // rows per block pass
+    constexpr int PASSES = 8;
+    const int tensor = blockIdx.z, h = blockIdx.y;
+    const int64_t head_off = (int64_t)h * a.n * HD;
+    const bf16 *src = static_cast<const bf16 *>(a.src[tensor]) + head_off;
+    bf16 *dst = static_cast<bf16 *>(a.dst[tensor]) + head_off;
+    const int r_in = threadIdx.x / CH, ch = threadIdx.x % CH;
+    const int64_t j0 = (int64_t)blockIdx.x * ROWS * PASSES;
+    uint4 buf[PASSES];
+    int64_t dst_row[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int64_t j = j0 + p * ROWS + r_in;
+        dst_row[p] = -1;
+        // perm entries are range-checked: with ids outside [0, m) part of perm is never
+        // written, and stale workspace values must not become addresses
+        const int64_t pj = j < a.n ? (int64_t)a.perm[j] : -1;
+        if (pj >= 0 && pj < a.n) {
+            const int64_t s_row = a.inverse ? j : pj;
+            dst_row[p] = a.inverse ? pj : j;
+            buf[p] = *reinterpret_cast<const uint4 *>(src + s_row * HD + ch * 8);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+        if (dst_row[p] >= 0) *reinterpret_cast<uint4 *>(dst + dst_row[p] * HD + ch * 8) = buf[p];
+}
+
+__global__ __launch_bounds__(256) void gather_scalar_kernel(const float *src, const int32_t *perm,
+                                                             int64_t n, float *dst) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j < n) {
+        const int32_t pj = perm[j];
+        dst[j] = (pj >= 0 && pj < n) ? src[pj] : 0.0f;
+    }
+}
+
+}  // namespace
+
+int64_t permute_blocks(int64_t n) {
+    return (n + kPermTokensPerBlock - 1) / kPermTokensPerBlock;
+}
+
+hipError_t launch_perm_index(const PermuteLaunch &a, hipStream_t s) {
+    const int64_t nblk = permute_blocks(a.n);
+    hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nblk), dim3(256), 0, s, a.group_id, a.n, a.m,
+                       a.table);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scan_kernel, dim3(a.m), dim3(256), 0, s, a.table, nblk, a.m, a.base_rel,
+                       a.totals);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nblk), dim3(256), 0, s, a.group_id, a.n, a.m,
+                       a.base_rel, a.totals, a.cu, a.perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherLaunch &a, hipStream_t s) {
+    if (a.n_tensors > 0) {
+        const int ch = a.head_dim * 2 / 16;
+        const int64_t rows_per_block = (256 / ch) * 8;
+        dim3 grid((unsigned)((a.n + rows_per_block - 1) / rows_per_block), a.n_heads, a.n_tensors);
+        if (a.head_dim == 128)
+            hipLaunchKernelGGL(gather_kernel<128>, grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(gather_kernel<64>, grid, dim3(256), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!a.inverse && a.p_sel && a.p_perm) {
+        hipLaunchKernelGGL(gather_scalar_kernel, dim3((unsigned)((a.n + 255) / 256)), dim3(256), 0,
+                           s, a.p_sel, a.perm, a.n, a.p_perm);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace moga

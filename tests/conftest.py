@@ -26,3 +26,11 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _seed_torch():
+    """Every test draws from a seeded generator."""
+    import torch
+    torch.manual_seed(1234)
+    yield

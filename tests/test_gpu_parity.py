@@ -1,0 +1,256 @@
+"""GPU parity of every entry point against the CPU oracle, on seeded inputs that span
+several tiles and a ragged tail, plus edge cases.  All calls go through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from sparse_attention_long_moga_amd import api
+from tests.helpers import assert_close_bf16, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _announce(what, **kw):
+    print(f"[case] {what} {kw}", flush=True)
+
+
+def _router_case(n, d, m, seed, x_dtype="bf16", dirichlet=None):
+    wl = workloads.small(f"route_{n}_{d}_{m}", n, d, 1, 64, m, seed=seed, x_dtype=x_dtype,
+                         mixture="normal" if x_dtype == "f32" else "gaussian",
+                         dirichlet=dirichlet)
+    return wl, workloads.make_x(wl, DEV), workloads.make_w(wl, DEV)
+
+
+# ------------------------------------------------------------------------------- router
+@pytest.mark.parametrize("n, d, m, x_dtype, seed", [
+    (4096, 256, 4, "f32", 1),        # the tiny workload's router shape
+    (5000, 384, 5, "bf16", 2),       # several blocks and a ragged tail
+    (3001, 1536, 5, "bf16", 3),
+    (2500, 512, 20, "bf16", 4),
+    (700, 512, 64, "bf16", 5),       # W larger than the LDS budget: chunked over d
+    (1, 64, 3, "bf16", 6),           # a single token
+    (333, 128, 1, "f32", 7),         # one group: p == 1
+])
+def test_route_parity(n, d, m, x_dtype, seed):
+    _announce("route", n=n, d=d, m=m, x_dtype=x_dtype)
+    wl, x, w = _router_case(n, d, m, seed, x_dtype)
+    ref = oracle.route(host(x), host(w))
+    pin = torch.from_numpy(oracle.near_tie_pins(ref)).to(DEV)
+    got = api.moga_route(x, w, m, pin=pin)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got["group_id"]), ref["group_id"])
+    np.testing.assert_array_equal(host(got["counts"]), ref["counts"])  # F_i exact
+    np.testing.assert_allclose(host(got["p_sel"]), ref["p_sel"], rtol=0, atol=2e-6)
+    P_gpu, P_ref = host(got["prob_sum"]) / n, ref["prob_sum"] / n
+    assert np.abs(P_gpu - P_ref).max() < 1e-6
+    if m == 1:
+        assert np.all(host(got["p_sel"]) == 1.0)
+
+
+def test_route_pins_force_groups():
+    _announce("route_pins")
+    wl, x, w = _router_case(1000, 256, 4, 9)
+    pin = torch.full((1000,), -1, dtype=torch.int32, device=DEV)
+    pin[::7] = 2
+    got = api.moga_route(x, w, 4, pin=pin)
+    ref = oracle.route(host(x), host(w), pin=host(pin))
+    free = ref["gap"] >= 1e-5
+    gid = host(got["group_id"])
+    assert np.all(gid[::7] == 2)
+    np.testing.assert_array_equal(gid[free], ref["group_id"][free])
+    np.testing.assert_allclose(host(got["p_sel"])[::7], ref["p_sel"][::7], atol=2e-6)
+
+
+# ------------------------------------------------------------------------------- permute
+@pytest.mark.parametrize("n, m, hd, case", [
+    (5000, 5, 128, "random"), (4097, 7, 64, "empty_group"), (2048, 1, 128, "one_group"),
+    (3000, 4, 64, "collapse"), (1, 3, 64, "single"), (6000, 64, 64, "random"),
+])
+def test_permute_parity_and_round_trip(n, m, hd, case):
+    _announce("permute", n=n, m=m, hd=hd, case=case)
+    rng = np.random.Generator(np.random.PCG64(n + m))
+    g = rng.integers(0, m, n).astype(np.int32)
+    if case == "empty_group":
+        g[g == 3] = 4
+    if case == "collapse":
+        g[:] = 2
+    gid = torch.from_numpy(g).to(DEV)
+    h = 3
+    q = torch.randn((h, n, hd), device=DEV, dtype=torch.bfloat16)
+    k = torch.randn((h, n, hd), device=DEV, dtype=torch.bfloat16)
+    p = torch.rand(n, device=DEV, dtype=torch.float32)
+    cu, perm, (qp, kp), pp = api.moga_permute(gid, [q, k], m, p_sel=p)
+    torch.cuda.synchronize()
+    cu_ref, perm_ref = oracle.groups(g, m)
+    np.testing.assert_array_equal(host(cu), cu_ref)
+    np.testing.assert_array_equal(host(perm), perm_ref)
+    pl = perm.long()
+    assert torch.equal(qp, q[:, pl]) and torch.equal(kp, k[:, pl])
+    assert torch.equal(pp, p[pl])
+    back = api.moga_unpermute(perm, [qp, kp], m)
+    torch.cuda.synchronize()
+    assert torch.equal(back[0], q) and torch.equal(back[1], k)
+
+
+# ------------------------------------------------------------------------------- varlen attention
+def _segments(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("case", ["mixed", "q_ne_k", "tiny_segments"])
+def test_group_attn_parity(hd, case):
+    _announce("group_attn", hd=hd, case=case)
+    rng = np.random.Generator(np.random.PCG64(hd * 7 + len(case)))
+    if case == "mixed":
+        ql = np.array([700, 0, 1, 129, 64, 1000, 33])
+        kl = ql.copy()
+    elif case == "q_ne_k":
+        ql = np.array([780, 195, 300, 1, 77])
+        kl = np.array([1560, 585, 0, 5, 64])   # one segment with queries but no keys
+    else:
+        ql = rng.integers(0, 5, 40)
+        kl = rng.integers(1, 6, 40)
+    cu_q, cu_k = _segments(ql), _segments(kl)
+    h = 2
+    lq, lk = int(cu_q[-1]), int(cu_k[-1])
+    q = torch.randn((h, lq, hd), device=DEV, dtype=torch.bfloat16)
+    k = torch.randn((h, lk, hd), device=DEV, dtype=torch.bfloat16)
+    v = torch.randn((h, lk, hd), device=DEV, dtype=torch.bfloat16)
+    rs = torch.rand(lq, device=DEV, dtype=torch.float32) + 0.5
+    out = api.moga_group_attn(q, k, v, torch.from_numpy(cu_q).to(DEV),
+                              torch.from_numpy(cu_k).to(DEV), row_scale=rs)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(hd)
+    rows_h, rows_i = np.repeat(np.arange(h), lq), np.tile(np.arange(lq), h)
+    ref, pairs = oracle.varlen_attn(host(q), host(k), host(v), cu_q, cu_k, scale, rows_h, rows_i,
+                                    row_scale=host(rs))
+    assert_close_bf16(host(out).reshape(-1, hd), ref, f"group_attn {case} hd={hd}")
+
+
+def test_group_attn_leaves_rows_outside_segments():
+    _announce("group_attn_untouched")
+    h, hd = 1, 64
+    cu = torch.tensor([10, 200, 300], dtype=torch.int32, device=DEV)  # rows 0-9, 300+ untouched
+    q = torch.randn((h, 400, hd), device=DEV, dtype=torch.bfloat16)
+    k = torch.randn((h, 400, hd), device=DEV, dtype=torch.bfloat16)
+    out = torch.full_like(q, 7.0)
+    api.moga_group_attn(q, k, k, cu, cu, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out[:, :10] == 7.0) and torch.all(out[:, 300:] == 7.0)
+    assert not torch.any(out[:, 10:300] == 7.0)
+
+
+# ------------------------------------------------------------------------------- STGA
+STGA_CASES = {
+    "small_hd64": dict(frames=10, height=6, width=8, shot_start=[0, 3, 4, 8, 10], win_h=3,
+                       win_w=4, t_group=2, aug_frames=2, heads=2, hd=64),
+    "multi_tile_hd128": dict(frames=12, height=10, width=16, shot_start=[0, 5, 9, 12], win_h=5,
+                             win_w=8, t_group=4, aug_frames=2, heads=2, hd=128),
+    "one_shot_no_aug": dict(frames=6, height=4, width=8, shot_start=[0, 6], win_h=4, win_w=8,
+                            t_group=3, aug_frames=0, heads=1, hd=64),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STGA_CASES))
+def test_stga_parity(name):
+    c = dict(STGA_CASES[name])
+    h, hd = c.pop("heads"), c.pop("hd")
+    _announce("stga", name=name)
+    n = c["frames"] * c["height"] * c["width"]
+    lay = api.make_stga_layout(**c)
+    q, k, v = (torch.randn((h, n, hd), device=DEV, dtype=torch.bfloat16) for _ in range(3))
+    o_t, o_f = api.stga_group_attn(q, k, v, lay)
+    torch.cuda.synchronize()
+    rows_h, rows_t = np.repeat(np.arange(h), n), np.tile(np.arange(n), h)
+    scale = 1 / math.sqrt(hd)
+    for mode, o in (("temporal", o_t), ("frame", o_f)):
+        ref, _ = oracle.stga_attn(host(q), host(k), host(v), c, mode, scale, rows_h, rows_t)
+        assert_close_bf16(host(o).reshape(-1, hd), ref, f"stga {name} {mode}")
+
+
+# ------------------------------------------------------------------------------- whole forward
+def _forward_case(n_frames, h, hd, m, seed, hybrid, d=256):
+    n = n_frames * 8 * 12
+    wl = workloads.small(f"fwd_{n}", n, d, h, hd, m, seed=seed)
+    x, w = workloads.make_x(wl, DEV), workloads.make_w(wl, DEV)
+    q, k, v = workloads.make_qkv(wl, DEV)
+    grid = dict(frames=n_frames, height=8, width=12,
+                shot_start=workloads.even_shots(n_frames, 3), win_h=4, win_w=6, t_group=2,
+                aug_frames=2) if hybrid else None
+    return wl, x, w, q, k, v, grid
+
+
+@pytest.mark.parametrize("hybrid", [False, True])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_forward_parity(hybrid, hd):
+    _announce("forward", hybrid=hybrid, hd=hd)
+    wl, x, w, q, k, v, grid = _forward_case(20, 2, hd, 5, 11 + hd, hybrid)
+    n, m = wl.n_tokens, wl.n_groups
+    ref_r = oracle.route(host(x), host(w))
+    pin_np = oracle.near_tie_pins(ref_r)
+    pin = torch.from_numpy(pin_np).to(DEV)
+    lay = api.make_stga_layout(**grid) if hybrid else None
+    got = api.moga_forward(x, w, q, k, v, m, alpha=0.1, pin=pin, stga=lay)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got["group_id"]), ref_r["group_id"])
+    cu_ref, perm_ref = oracle.groups(ref_r["group_id"], m)
+    np.testing.assert_array_equal(host(got["cu_seqlens"]), cu_ref)
+    np.testing.assert_array_equal(host(got["perm"]), perm_ref)
+    loss_ref, F_ref, P_ref = oracle.balance_loss(ref_r["counts"], ref_r["prob_sum"], n, 0.1)
+    assert abs(float(got["loss"].item()) - loss_ref) < 1e-6
+    scale = 1 / math.sqrt(hd)
+    h = q.shape[0]
+    rows_h, rows_t = np.repeat(np.arange(h), n), np.tile(np.arange(n), h)
+    qh, kh, vh = host(q), host(k), host(v)
+    ref, _ = oracle.moga_attn(qh, kh, vh, ref_r["group_id"], m, ref_r["p_sel"], scale, rows_h,
+                              rows_t)
+    if hybrid:
+        rt, _ = oracle.stga_attn(qh, kh, vh, grid, "temporal", scale, rows_h, rows_t)
+        rf, _ = oracle.stga_attn(qh, kh, vh, grid, "frame", scale, rows_h, rows_t)
+        ref = (ref + rt + rf) / 3.0
+    assert_close_bf16(host(got["out"]).reshape(-1, hd), ref, f"forward hybrid={hybrid}")
+
+
+def test_forward_collapse_and_single_group():
+    _announce("forward_collapse")
+    wl, x, w, q, k, v, _ = _forward_case(6, 1, 64, 4, 21, False)
+    n = wl.n_tokens
+    pin = torch.zeros(n, dtype=torch.int32, device=DEV)  # every token forced into group 0
+    got = api.moga_forward(x, w, q, k, v, 4, pin=pin)
+    torch.cuda.synchronize()
+    ref_r = oracle.route(host(x), host(w), pin=np.zeros(n, np.int32))
+    assert host(got["cu_seqlens"]).tolist() == [0, n, n, n, n]
+    rows = np.arange(n)
+    ref, _ = oracle.moga_attn(host(q), host(k), host(v), ref_r["group_id"], 4, ref_r["p_sel"],
+                              1 / 8, np.zeros(n), rows)
+    assert_close_bf16(host(got["out"])[0], ref, "collapse")
+    loss_ref = 0.1 * 4 * ref_r["prob_sum"][0] / n
+    assert abs(float(got["loss"].item()) - loss_ref) < 1e-6
+
+
+def test_forward_is_deterministic():
+    _announce("determinism")
+    wl, x, w, q, k, v, grid = _forward_case(12, 2, 128, 5, 31, True)
+    lay = api.make_stga_layout(**grid)
+    a = api.moga_forward(x, w, q, k, v, 5, stga=lay)
+    b = api.moga_forward(x, w, q, k, v, 5, stga=lay)
+    torch.cuda.synchronize()
+    for key in ("out", "group_id", "perm", "cu_seqlens", "p_sel", "prob_sum", "loss"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_balance_loss_parity():
+    _announce("balance_loss")
+    counts = torch.tensor([10, 0, 30, 60], dtype=torch.int32, device=DEV)
+    ps = torch.tensor([20.5, 3.25, 30.0, 46.25], dtype=torch.float64, device=DEV)
+    loss, F, P = api.moga_balance_loss(counts, ps, 100, alpha=0.1)
+    l_ref, F_ref, P_ref = oracle.balance_loss(host(counts), host(ps), 100, 0.1)
+    assert float(loss.item()) == pytest.approx(l_ref, abs=1e-15)
+    np.testing.assert_array_equal(host(F), F_ref)
+    np.testing.assert_allclose(host(P), P_ref, atol=1e-16)

@@ -1,0 +1,121 @@
+"""The C-ABI library: it builds, loads, exports what include/moga.h declares, and its
+argument checks return the documented status before touching a GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_long_moga_amd import _capi
+from sparse_attention_long_moga_amd.api import make_dims, make_stga_layout, moga_workspace_bytes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_capi.LIB_PATH):
+        from sparse_attention_long_moga_amd import build
+        build.build(verbose=False)
+    return _capi.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "moga.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:moga|stga)_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree(lib):
+    names = declared_functions()
+    assert names == sorted(_capi.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), f"libmoga.so does not export {n}"
+
+
+def test_exports_are_c_symbols(lib):
+    for n in _capi.EXPORTS:
+        ctypes.cast(getattr(lib, n), ctypes.c_void_p)  # resolvable by its plain C name
+
+
+def _dims(**kw):
+    base = dict(n_tokens=4096, d_model=256, n_heads=4, head_dim=64, n_groups=4)
+    base.update(kw)
+    return make_dims(**base)
+
+
+@pytest.mark.parametrize("kw, msg", [
+    (dict(n_tokens=0), "n_tokens"), (dict(n_tokens=1 << 31), "n_tokens"),
+    (dict(head_dim=96), "head_dim"), (dict(n_groups=0), "n_groups"),
+    (dict(n_groups=65), "n_groups"), (dict(n_heads=0), "n_heads"), (dict(d_model=0), "d_model"),
+])
+def test_bad_dims_rejected(lib, kw, msg):
+    d = _dims(**kw)
+    st = lib.moga_route(ctypes.c_void_p(16), 0, ctypes.c_void_p(16), None, ctypes.byref(d),
+                        ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                        ctypes.c_void_p(16), ctypes.c_void_p(256), 1 << 30, None)
+    assert st == _capi.MOGA_ERR_ARG
+    assert msg in lib.moga_last_error().decode()
+    assert lib.moga_workspace_bytes(ctypes.byref(d), None) == 0
+
+
+def test_null_and_workspace_errors(lib):
+    d = _dims()
+    p = ctypes.c_void_p(256)
+    assert lib.moga_route(None, 0, p, None, ctypes.byref(d), p, p, p, p, p, 1 << 30, None) == \
+        _capi.MOGA_ERR_ARG
+    assert lib.moga_route(p, 0, p, None, ctypes.byref(d), p, p, p, p, None, 0, None) == \
+        _capi.MOGA_ERR_WORKSPACE
+    assert lib.moga_route(p, 0, p, None, ctypes.byref(d), p, p, p, p, p, 16, None) == \
+        _capi.MOGA_ERR_WORKSPACE
+    assert "workspace" in lib.moga_last_error().decode()
+    # misaligned x, odd d_model for bf16
+    assert lib.moga_route(ctypes.c_void_p(258), 0, p, None, ctypes.byref(d), p, p, p, p, p,
+                          1 << 30, None) == _capi.MOGA_ERR_ARG
+    d2 = _dims(d_model=260)
+    assert lib.moga_route(p, 1, p, None, ctypes.byref(d2), p, p, p, p, p, 1 << 30, None) == \
+        _capi.MOGA_ERR_UNSUPPORTED
+    # permute: too many tensors, aliasing
+    src = (ctypes.c_void_p * 4)(256, 512, 768, 1024)
+    assert lib.moga_permute(0, p, ctypes.byref(d), p, p, src, src, 5, None, None, p, 1 << 30,
+                            None) == _capi.MOGA_ERR_ARG
+    assert lib.moga_permute(0, p, ctypes.byref(d), p, p, src, src, 1, None, None, p, 1 << 30,
+                            None) == _capi.MOGA_ERR_ARG
+    assert "aliases" in lib.moga_last_error().decode()
+    # group attention: no segments
+    assert lib.moga_group_attn(p, p, p, 10, 10, 0, p, p, None, ctypes.byref(d), p, p, 1 << 20,
+                               None) == _capi.MOGA_ERR_ARG
+
+
+def test_stga_geometry_checks(lib):
+    n = 4 * 6 * 8
+    d = _dims(n_tokens=n)
+    ok = make_stga_layout(4, 6, 8, [0, 2, 4], 3, 4, 2, 2)
+    assert moga_workspace_bytes(d, ok) > moga_workspace_bytes(d)
+    bad = [make_stga_layout(4, 6, 8, [0, 2, 3], 3, 4, 2, 2),   # does not end at frames
+           make_stga_layout(4, 6, 8, [0, 2, 2, 4], 3, 4, 2, 2),  # not strictly increasing
+           make_stga_layout(4, 6, 8, [0, 4], 4, 4, 2, 2),        # window does not tile 6 rows
+           make_stga_layout(4, 6, 8, [0, 4], 3, 4, 0, 2),        # t_group < 1
+           make_stga_layout(4, 6, 8, [0, 4], 3, 4, 2, -1),       # aug < 0
+           make_stga_layout(5, 6, 8, [0, 5], 3, 4, 2, 2)]        # 5*6*8 != n_tokens
+    p = ctypes.c_void_p(256)
+    for lay in bad:
+        assert lib.moga_workspace_bytes(ctypes.byref(d), lay.ref()) == 0
+        assert lib.stga_group_attn(p, p, p, ctypes.byref(d), lay.ref(), p, p, p, 1 << 40,
+                                   None) == _capi.MOGA_ERR_ARG
+
+
+def test_workspace_sizes_scale_with_problem(lib):
+    small = moga_workspace_bytes(_dims())
+    big = moga_workspace_bytes(_dims(n_tokens=8192))
+    assert big > small > 4 * 4 * 4096 * 64 * 2  # at least the permuted Q/K/V/O
+
+
+def test_no_device_reported_as_unsupported(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    d = _dims()
+    p = ctypes.c_void_p(256)
+    st = lib.moga_balance_loss(p, p, ctypes.byref(d), p, None, None, None)
+    assert st == _capi.MOGA_ERR_UNSUPPORTED

@@ -197,6 +197,38 @@ def test_singleton_group_and_identical_keys():
                                    atol=1e-14)
 
 
+def test_varlen_matches_bruteforce_and_moga_rows():
+    h, hd = 2, 16
+    cu_q = np.array([0, 5, 5, 40, 41, 90])
+    cu_k = np.array([0, 9, 12, 12, 30, 77])  # segment 2 has queries but no keys
+    lq, lk = 90, 77
+    q, k, v = _rand((h, lq, hd), 70), _rand((h, lk, hd), 71), _rand((h, lk, hd), 72)
+    rs = np.linspace(0.5, 1.5, lq)
+    rows_h, rows_i = np.repeat(np.arange(h), lq), np.tile(np.arange(lq), h)
+    out, pairs = oracle.varlen_attn(q, k, v, cu_q, cu_k, 0.25, rows_h, rows_i, row_scale=rs)
+    out = out.reshape(h, lq, hd)
+    seg_q = np.searchsorted(cu_q, np.arange(lq), side="right") - 1
+    seg_k = np.searchsorted(cu_k, np.arange(lk), side="right") - 1
+    mask = seg_q[:, None] == seg_k[None, :]
+    for i in range(h):
+        has = mask.any(1)
+        ref = bf.masked_attention(q[i][has], k[i], v[i], mask[has], 0.25) * rs[has, None]
+        np.testing.assert_allclose(out[i][has], ref, atol=1e-13)
+        assert np.all(out[i][~has] == 0.0)
+    qlen, klen = np.diff(cu_q), np.diff(cu_k)
+    assert pairs == h * int((qlen * klen).sum())
+    # varlen over the grouped rows equals the MoGA rows (the permute is only a reordering)
+    n, m = 120, 3
+    x, w = _rand((n, 6), 73), _rand((6, m), 74)
+    qq, kk, vv = (_rand((1, n, hd), 75 + i) for i in range(3))
+    r = oracle.route(x, w)
+    cu, perm = oracle.groups(r["group_id"], m)
+    a, _ = oracle.varlen_attn(qq[:, perm], kk[:, perm], vv[:, perm], cu, cu, 0.3, np.zeros(n),
+                              np.arange(n), row_scale=r["p_sel"][perm])
+    b, _ = oracle.moga_attn(qq, kk, vv, r["group_id"], m, r["p_sel"], 0.3, np.zeros(n), perm)
+    np.testing.assert_allclose(a, b, atol=1e-15)
+
+
 # --------------------------------------------------------------------------- STGA
 TINY_GRID = dict(frames=6, height=4, width=6, shot_start=[0, 2, 5, 6], win_h=2, win_w=3,
                  t_group=2, aug_frames=2)
