@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoGA forward on one MI355X.
+
+A step is one whole forward (route -> histogram/scan/permute -> varlen group attention
+scaled by p(g|x) -> inverse permute -> balance loss; plus STGA and the 3-way mean for the
+hybrid workloads) over one synthetic batch already resident in HBM.  The default
+workload is the 30 s, 282,360-token, M = 5 layer with Dirichlet(0.5)-skewed routing.
+
+Prints one JSON line: tokens/s of the whole forward (value), the group-attention
+TFLOP/s, per-stage times, the roofline fraction of the dominant kernel (the attention
+kernel, measured with HIP events on the stream it runs on) and the CPU oracle's rate on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+DEFAULT_WORKLOAD = "wan1.3b_30s_skewed_N282360_M5"
+METRIC = "MoGA fwd tokens/s + group-attn TFLOP/s (% bf16 MFMA peak) at N=282k, M=5"
+
+# HBM traffic calibration: bytes the FETCH_SIZE / WRITE_SIZE counters report per byte
+# actually moved, measured on a plain copy kernel (see profiles/).  None until measured.
+ATTN_TRAFFIC_BYTES = None
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-stages", action="store_true")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; the multi-GPU (sequence- "
+                          "parallel) path is a design, not an implementation; run --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from sparse_attention_long_moga_amd import api, metrics
+
+    if not os.path.exists(os.path.join(ROOT, "sparse_attention_long_moga_amd", "libmoga.so")):
+        from sparse_attention_long_moga_amd import build
+        build.build()
+
+    wl = workloads.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n, h, hd, m = wl.n_tokens, wl.n_heads, wl.head_dim, wl.n_groups
+    log(f"workload {wl.name}: generating inputs on {dev}")
+    x, w = workloads.make_x(wl, dev), workloads.make_w(wl, dev)
+    q, k, v = workloads.make_qkv(wl, dev)
+    lay = None
+    if wl.hybrid:
+        lay = api.make_stga_layout(wl.frames, wl.height, wl.width, wl.shot_start, wl.win_h,
+                                   wl.win_w, wl.t_group, wl.aug_frames)
+    dims = api.make_dims(n, wl.d_model, h, hd, m, alpha=wl.alpha)
+    ws = api.workspace(api.moga_workspace_bytes(dims, lay), dev)
+    out = dict(out=torch.empty_like(q), loss=torch.empty(1, dtype=torch.float64, device=dev),
+               group_id=torch.empty(n, dtype=torch.int32, device=dev),
+               p_sel=torch.empty(n, dtype=torch.float32, device=dev),
+               cu_seqlens=torch.empty(m + 1, dtype=torch.int32, device=dev),
+               perm=torch.empty(n, dtype=torch.int32, device=dev),
+               counts=torch.empty(m, dtype=torch.int32, device=dev),
+               prob_sum=torch.empty(m, dtype=torch.float64, device=dev))
+    torch.cuda.synchronize()
+
+    def step():
+        api.moga_forward(x, w, q, k, v, m, alpha=wl.alpha, stga=lay, ws=ws, out=out)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    tokens_per_s = n / (ms_per_step / 1e3)
+    log(f"{ms_per_step:.3f} ms/step  ({wall / args.steps * 1e3:.3f} ms wall)  "
+        f"{tokens_per_s / 1e6:.3f} M tokens/s")
+
+    counts = out["counts"].cpu().numpy().astype(np.int64)
+    pairs_moga = metrics.moga_pairs(counts)
+    attn_flops = metrics.attention_flops(pairs_moga, h, hd)
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(wl.describe(), group_sizes=counts.tolist(),
+                       sum_n_sq_over_n_sq=pairs_moga / float(n) ** 2, parallelism="single-gpu"),
+    }
+
+    if not args.no_stages:
+        result.update(stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops))
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, x, w, q, k, v, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
+    """Time each stage through its own C-ABI call (the same kernels moga_forward
+    launches), with HIP events on the stream the kernels run on."""
+    import numpy as np
+    import torch
+
+    from sparse_attention_long_moga_amd import api, metrics
+
+    n, h, hd, m = wl.n_tokens, wl.n_heads, wl.head_dim, wl.n_groups
+    stream = torch.cuda.current_stream()
+    names = ["route", "permute", "group_attn", "unpermute", "loss"] + (["stga"] if lay else [])
+    acc = {s: [] for s in names}
+    log(f"stage breakdown over {args.steps} steps")
+    for it in range(args.steps + 1):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        ev[0].record(stream)
+        r = api.moga_route(x, w, m, ws=ws)
+        ev[1].record(stream)
+        cu, perm, (qp, kp, vp), pp = api.moga_permute(r["group_id"], [q, k, v], m,
+                                                      p_sel=r["p_sel"], ws=ws)
+        ev[2].record(stream)
+        op = api.moga_group_attn(qp, kp, vp, cu, cu, row_scale=pp, ws=ws)
+        ev[3].record(stream)
+        api.moga_unpermute(perm, [op], m, ws=ws)
+        ev[4].record(stream)
+        api.moga_balance_loss(r["counts"], r["prob_sum"], n, wl.alpha)
+        ev[5].record(stream)
+        if lay:
+            api.stga_group_attn(q, k, v, lay, ws=ws)
+            ev[6].record(stream)
+        torch.cuda.synchronize()
+        if it == 0:
+            continue  # first pass warms the allocator
+        for i, s in enumerate(names):
+            acc[s].append(ev[i].elapsed_time(ev[i + 1]))
+        del r, cu, perm, qp, kp, vp, pp, op
+    ms = {s: float(np.mean(v)) for s, v in acc.items()}
+    e_bytes = h * n * hd * 2
+    x_bytes = n * wl.d_model * (2 if wl.x_dtype == "bf16" else 4)
+    route_bytes = x_bytes + wl.d_model * m * 4 + n * 8
+    permute_bytes = 6 * e_bytes + n * 4 * 2 + n * 8
+    unpermute_bytes = 2 * e_bytes + n * 4
+    attn_tflops = attn_flops / (ms["group_attn"] / 1e3) / 1e12
+    stages = {
+        "stage_ms": ms,
+        "attn_tflops": attn_tflops,
+        "attn_frac_of_bf16_peak": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
+        "route_gbs": route_bytes / (ms["route"] / 1e3) / 1e9,
+        "permute_gbs": permute_bytes / (ms["permute"] / 1e3) / 1e9,
+        "unpermute_gbs": unpermute_bytes / (ms["unpermute"] / 1e3) / 1e9,
+    }
+    stages["route_frac_of_hbm"] = stages["route_gbs"] / HBM_PEAK_GBS
+    stages["permute_frac_of_hbm"] = stages["permute_gbs"] / HBM_PEAK_GBS
+    stages["unpermute_frac_of_hbm"] = stages["unpermute_gbs"] / HBM_PEAK_GBS
+    stages["roofline"] = {
+        "bound": "mfma", "kernel": "attn_kernel<128> (group_attn stage)",
+        "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": ATTN_TRAFFIC_BYTES,
+        "algorithmic_flops_per_launch": attn_flops,
+        "launch_ms": ms["group_attn"],
+    }
+    if lay:
+        g = dict(frames=wl.frames, height=wl.height, width=wl.width,
+                 shot_start=list(wl.shot_start), win_h=wl.win_h, win_w=wl.win_w,
+                 t_group=wl.t_group, aug_frames=wl.aug_frames)
+        pt = stga_pairs_closed_form(g)
+        stages["stga_tflops"] = metrics.attention_flops(pt, h, hd) / (ms["stga"] / 1e3) / 1e12
+    log(f"stages (ms): {ms}  attn {attn_tflops:.1f} TFLOP/s")
+    return stages
+
+
+def stga_pairs_closed_form(g):
+    """Temporal + per-frame (query, key) pairs per head from the geometry."""
+    starts = g["shot_start"]
+    wt = g["win_h"] * g["win_w"]
+    nwin = (g["height"] // g["win_h"]) * (g["width"] // g["win_w"])
+    pairs = 0
+    S = len(starts) - 1
+    for s in range(S):
+        length = starts[s + 1] - starts[s]
+        nch = -(-length // g["t_group"])
+        ap = min(g["aug_frames"], starts[s] - starts[s - 1]) if s > 0 else 0
+        an = min(g["aug_frames"], starts[s + 2] - starts[s + 1]) if s + 1 < S else 0
+        for c in range(nch):
+            tf = min(g["t_group"], length - c * g["t_group"])
+            kf = tf + (ap if c == 0 else 0) + (an if c == nch - 1 else 0)
+            pairs += nwin * (tf * wt) * (kf * wt)
+    hw = g["height"] * g["width"]
+    return pairs + g["frames"] * hw * hw
+
+
+def cpu_baseline(wl, x, w, q, k, v, target_s):
+    """Oracle rate on a bounded sample: routing, groups and loss on every token, MoGA
+    attention on seeded (head, token) rows, extrapolated by row count."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    n, h, hd, m = wl.n_tokens, wl.n_heads, wl.head_dim, wl.n_groups
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    log(f"cpu baseline: oracle with {threads} threads")
+    xh = x.float().cpu().numpy()
+    wh = w.cpu().numpy()
+    t0 = time.perf_counter()
+    r = oracle.route(xh, wh)
+    cu, perm = oracle.groups(r["group_id"], m)
+    oracle.balance_loss(r["counts"], r["prob_sum"], n, wl.alpha)
+    t_route = time.perf_counter() - t0
+    del xh
+    heads = [0, h - 1] if h > 1 else [0]
+    qh = np.stack([q[i].float().cpu().numpy() for i in heads])
+    kh = np.stack([k[i].float().cpu().numpy() for i in heads])
+    vh = np.stack([v[i].float().cpu().numpy() for i in heads])
+    scale = 1.0 / np.sqrt(hd)
+    # calibrate on a few rows, then size the sample to the CPU-time target
+    rows = 64
+    used = 0.0
+    timed_rows = 0
+    seed = 0
+    while True:
+        rt = workloads.random_rows(n, rows, 1000 + seed)
+        rh = np.arange(rt.shape[0]) % len(heads)
+        t1 = time.perf_counter()
+        oracle.moga_attn(qh, kh, vh, r["group_id"], m, r["p_sel"], scale, rh, rt)
+        dt = time.perf_counter() - t1
+        used += dt
+        timed_rows += rt.shape[0]
+        seed += 1
+        remaining = target_s - t_route - used
+        if remaining <= 0.5 or timed_rows >= n:
+            break
+        rows = int(min(n, max(64, rows * remaining / max(dt, 1e-3) * 0.8)))
+    per_row = used / timed_rows
+    total = t_route + per_row * h * n
+    return {
+        "value": n / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"route + groups + loss on all {n} tokens ({t_route:.1f} s); MoGA attention "
+                   f"on {timed_rows} seeded (head, token) rows of {h * n} ({used:.1f} s), "
+                   f"extrapolated by row count to {total:.0f} s for the whole forward"),
+        "measured_s": t_route + used,
+    }
+
+
+if __name__ == "__main__":
+    main()
