@@ -20,6 +20,8 @@
 // share (segment, head), so the blocks running at one time stream the same K/V through L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "moga_internal.h"
 
 namespace moga {
@@ -40,7 +42,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // ---------------------------------------------------------------------------- planning
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const int32_t *cu_k,
                                                      int n_seg, int64_t len_q, int64_t len_k,
-                                                     int n_heads, AttnPlan p) {
+                                                     int n_heads, int64_t max_items, AttnPlan p) {
     __shared__ int s_klen[kPlanSortMax];
     __shared__ int s_order[kPlanSortMax];
     __shared__ int s_scan[1024];
@@ -95,7 +97,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const i
     if (tid == 0) {
         p.item_base[n_seg] = carry;
         p.counter[0] = 0;
-        p.counter[1] = carry;
+        // overlapping (non-monotone) offsets could ask for more items than the list holds
+        p.counter[1] = carry < max_items ? carry : (int)max_items;
     }
 }
 
@@ -126,7 +129,24 @@ struct Tile {
     static constexpr int VUNITS = XN / 2;   // 4x4 V blocks per thread
 };
 
-template <int HD>
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Rescale the running output only when the row maximum has grown by more than 2^8 in
+// exp2 units; until then probabilities are formed against the stale maximum (they stay
+// <= 256), which changes no result beyond rounding because numerator and denominator
+// use the same reference.
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int HD, bool IDX>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
     using T = Tile<HD>;
     __shared__ __attribute__((aligned(16))) bf16 ks[2][KT * T::KP];
@@ -135,36 +155,50 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, hh = lane >> 5;
-    const int total = a.plan.counter[1];
+    const int total = uniform(a.plan.counter[1]);
     const float c = a.scale * kLog2e;
+    const float thr = kRescaleLog2 / c;
+
+    // per-thread constant parts of the tile loads
+    int k_row[T::KLOADS], k_col[T::KLOADS];
+#pragma unroll
+    for (int i = 0; i < T::KLOADS; ++i) {
+        const int cidx = tid + kAttnThreads * i;
+        k_row[i] = cidx / (HD / 8);
+        k_col[i] = cidx % (HD / 8);
+    }
+    int v_ax[T::VUNITS], v_bx[T::VUNITS];
+#pragma unroll
+    for (int u = 0; u < T::VUNITS; ++u) {
+        const int combo = u * 8 + wave * 2 + hh;
+        v_ax[u] = (lane & 7) + 8 * (combo % T::XN);
+        v_bx[u] = ((lane >> 3) & 3) + 4 * (combo / T::XN);
+    }
 
     for (;;) {
         if (tid == 0) s_item = atomicAdd(a.plan.counter, 1);
         __syncthreads();
-        const int item = s_item;
+        const int item = uniform(s_item);
         __syncthreads();
         if (item >= total) break;
         const int4 itm = a.plan.items[item];
-        const int seg = itm.x, h = itm.y, qt = itm.z;
-        const int64_t qb = clamp64(a.cu_q[seg], 0, a.len_q);
-        const int64_t qe = clamp64(a.cu_q[seg + 1], qb, a.len_q);
-        const int64_t kb = clamp64(a.cu_k[seg], 0, a.len_k);
-        const int64_t ke = clamp64(a.cu_k[seg + 1], kb, a.len_k);
-        const int klen = (int)(ke - kb);
+        const int seg = uniform(itm.x), h = uniform(itm.y), qt = uniform(itm.z);
+        const int qb = uniform((int)clamp64(a.cu_q[seg], 0, a.len_q));
+        const int qe = uniform((int)clamp64(a.cu_q[seg + 1], qb, a.len_q));
+        const int kb = uniform((int)clamp64(a.cu_k[seg], 0, a.len_k));
+        const int ke = uniform((int)clamp64(a.cu_k[seg + 1], kb, a.len_k));
+        const int klen = ke - kb;
 
         // ---- Q^T fragments (B operand): lane (query j, half hh) holds q[16s + 8hh .. +8)
-        const int64_t qrow = qb + (int64_t)qt * kAttnBQ + wave * 32 + j;
+        const int qrow = qb + qt * kAttnBQ + wave * 32 + j;
         const bool qvalid = qrow < qe;
-        int64_t qphys = 0;
-        if (qvalid) qphys = a.q_idx ? (int64_t)a.q_idx[qrow] : qrow;
+        const int qrow_c = qvalid ? qrow : qe - 1;   // qe > qb for every item
+        const int64_t qphys = IDX ? (int64_t)a.q_idx[qrow_c] : (int64_t)qrow_c;
         bf16x8 qf[T::NS];
         {
             const bf16 *qp = a.q + (int64_t)h * a.q_rows * HD + qphys * HD + 8 * hh;
 #pragma unroll
-            for (int s = 0; s < T::NS; ++s) {
-                if (qvalid) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
-                else qf[s] = bf16x8{};
-            }
+            for (int s = 0; s < T::NS; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
         }
 
         const bf16 *kbase = a.k + (int64_t)h * a.kv_rows * HD;
@@ -173,61 +207,67 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
 
         uint4 kreg[T::KLOADS];
         uint2 vreg[T::VUNITS][4];
-        auto phys_row = [&](int key) -> int64_t {
-            return a.kv_idx ? (int64_t)a.kv_idx[kb + key] : kb + key;
-        };
         auto load_tile = [&](int t) {
             const int key0 = t * KT;
+            if constexpr (!IDX) {
+                // rows [kb + key0, ke) of this head; rows past ke read as zeros
+                const uint32_t bytes = (uint32_t)(klen - key0) * HD * 2;
+                const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)(kb + key0) * HD, bytes);
+                const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)(kb + key0) * HD, bytes);
 #pragma unroll
-            for (int i = 0; i < T::KLOADS; ++i) {
-                const int cidx = tid + kAttnThreads * i;
-                const int row = cidx / (HD / 8), col = cidx % (HD / 8);
-                const int key = key0 + row;
-                if (key < klen)
-                    kreg[i] = *reinterpret_cast<const uint4 *>(kbase + phys_row(key) * HD + col * 8);
-                else
-                    kreg[i] = make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int u = 0; u < T::VUNITS; ++u) {
-                const int combo = u * 8 + wave * 2 + hh;
-                const int ax = (lane & 7) + 8 * (combo % T::XN);
-                const int bx = ((lane >> 3) & 3) + 4 * (combo / T::XN);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = key0 + 4 * bx + r;
-                    if (key < klen)
-                        vreg[u][r] =
-                            *reinterpret_cast<const uint2 *>(vbase + phys_row(key) * HD + 4 * ax);
-                    else
-                        vreg[u][r] = make_uint2(0, 0);
+                for (int i = 0; i < T::KLOADS; ++i) {
+                    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+                        rk, (k_row[i] * HD + k_col[i] * 8) * 2, 0, 0);
+                    kreg[i] = make_uint4(w[0], w[1], w[2], w[3]);
                 }
+#pragma unroll
+                for (int u = 0; u < T::VUNITS; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(
+                            rv, ((4 * v_bx[u] + r) * HD + 4 * v_ax[u]) * 2, 0, 0);
+                        vreg[u][r] = make_uint2(w[0], w[1]);
+                    }
+            } else {
+                // gathered rows; rows past the segment are clamped to its last row (finite
+                // data: their scores are masked and their probabilities are zero)
+                const int last = klen - 1;
+#pragma unroll
+                for (int i = 0; i < T::KLOADS; ++i) {
+                    const int key = min(key0 + k_row[i], last);
+                    const int64_t row = a.kv_idx[kb + key];
+                    kreg[i] = *reinterpret_cast<const uint4 *>(kbase + row * HD + k_col[i] * 8);
+                }
+#pragma unroll
+                for (int u = 0; u < T::VUNITS; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = min(key0 + 4 * v_bx[u] + r, last);
+                        const int64_t row = a.kv_idx[kb + key];
+                        vreg[u][r] = *reinterpret_cast<const uint2 *>(vbase + row * HD + 4 * v_ax[u]);
+                    }
             }
         };
         auto store_tile = [&](int buf) {
 #pragma unroll
-            for (int i = 0; i < T::KLOADS; ++i) {
-                const int cidx = tid + kAttnThreads * i;
-                const int row = cidx / (HD / 8), col = cidx % (HD / 8);
-                *reinterpret_cast<uint4 *>(&ks[buf][row * T::KP + col * 8]) = kreg[i];
-            }
+            for (int i = 0; i < T::KLOADS; ++i)
+                *reinterpret_cast<uint4 *>(&ks[buf][k_row[i] * T::KP + k_col[i] * 8]) = kreg[i];
 #pragma unroll
             for (int u = 0; u < T::VUNITS; ++u) {
-                const int combo = u * 8 + wave * 2 + hh;
-                const int ax = (lane & 7) + 8 * (combo % T::XN);
-                const int bx = ((lane >> 3) & 3) + 4 * (combo / T::XN);
                 const uint2 v0 = vreg[u][0], v1 = vreg[u][1], v2 = vreg[u][2], v3 = vreg[u][3];
                 // column cc of the 4 rows -> one 8-byte run of V^T row (4*ax + cc)
                 uint2 w[4];
-                w[0] = make_uint2((v0.x & 0xffffu) | (v1.x << 16), (v2.x & 0xffffu) | (v3.x << 16));
-                w[1] = make_uint2((v0.x >> 16) | (v1.x & 0xffff0000u),
-                                  (v2.x >> 16) | (v3.x & 0xffff0000u));
-                w[2] = make_uint2((v0.y & 0xffffu) | (v1.y << 16), (v2.y & 0xffffu) | (v3.y << 16));
-                w[3] = make_uint2((v0.y >> 16) | (v1.y & 0xffff0000u),
-                                  (v2.y >> 16) | (v3.y & 0xffff0000u));
+                w[0] = make_uint2(__builtin_amdgcn_perm(v1.x, v0.x, 0x05040100u),
+                                  __builtin_amdgcn_perm(v3.x, v2.x, 0x05040100u));
+                w[1] = make_uint2(__builtin_amdgcn_perm(v1.x, v0.x, 0x07060302u),
+                                  __builtin_amdgcn_perm(v3.x, v2.x, 0x07060302u));
+                w[2] = make_uint2(__builtin_amdgcn_perm(v1.y, v0.y, 0x05040100u),
+                                  __builtin_amdgcn_perm(v3.y, v2.y, 0x05040100u));
+                w[3] = make_uint2(__builtin_amdgcn_perm(v1.y, v0.y, 0x07060302u),
+                                  __builtin_amdgcn_perm(v3.y, v2.y, 0x07060302u));
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc)
-                    *reinterpret_cast<uint2 *>(&vt[buf][(4 * ax + cc) * T::VP + 4 * bx]) = w[cc];
+                    *reinterpret_cast<uint2 *>(&vt[buf][(4 * v_ax[u] + cc) * T::VP + 4 * v_bx[u]]) = w[cc];
             }
         };
 
@@ -236,9 +276,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
 #pragma unroll
         for (int ti = 0; ti < T::NT; ++ti) o[ti] = f32x16{};
 
-        if (ntiles > 0) load_tile(0);
-        for (int t = 0; t < ntiles; ++t) {
-            const int buf = t & 1;
+        // one tile: publish the prefetched registers into LDS buffer BUF, prefetch the next
+        // tile, then S^T, softmax and O^T += V^T P^T.  BUF is a compile-time constant so all
+        // LDS addresses fold into immediate offsets.
+        auto tile = [&](auto bufc, int t) {
+            constexpr int buf = decltype(bufc)::value;
             store_tile(buf);
             __syncthreads();
             if (t + 1 < ntiles) load_tile(t + 1);
@@ -246,15 +288,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
             // S^T for two 32-key sub-blocks
             f32x16 sacc[2];
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                sacc[sb] = f32x16{};
-                const bf16 *krow = &ks[buf][(sb * 32 + j) * T::KP + 8 * hh];
+            for (int sb = 0; sb < 2; ++sb) sacc[sb] = f32x16{};
 #pragma unroll
-                for (int s = 0; s < T::NS; ++s) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + 16 * s);
+            for (int s = 0; s < T::NS; ++s)
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
+                        &ks[buf][(sb * 32 + j) * T::KP + 8 * hh + 16 * s]);
                     sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sb], 0, 0, 0);
                 }
-            }
             const int key0 = t * KT;
             if (key0 + KT > klen) {
 #pragma unroll
@@ -269,17 +311,20 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[sb][v]);
+                for (int v = 0; v < 16; v += 2) tmax = fmaxf(tmax, fmaxf(sacc[sb][v], sacc[sb][v + 1]));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float m_new = fmaxf(m_run, tmax);
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-            m_run = m_new;
-            const float mc = m_new * c;
-            l_run *= alpha;
+            const bool up = tmax > m_run + thr;
+            if (__ballot(up)) {
+                const float m_new = up ? tmax : m_run;
+                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+                m_run = m_new;
+                l_run *= alpha;
 #pragma unroll
-            for (int ti = 0; ti < T::NT; ++ti)
+                for (int ti = 0; ti < T::NT; ++ti)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) o[ti][v] *= alpha;
+                    for (int v = 0; v < 16; ++v) o[ti][v] *= alpha;
+            }
+            const float mc = m_run * c;
 
             bf16x8 pf[4];
 #pragma unroll
@@ -297,16 +342,21 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
                     pf[sb * 2 + half] = __builtin_bit_cast(bf16x8, packed);
                 }
 #pragma unroll
-            for (int ti = 0; ti < T::NT; ++ti) {
-                const bf16 *vrow = &vt[buf][(32 * ti + j) * T::VP + 4 * hh];
+            for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
-                for (int ch = 0; ch < 4; ++ch) {
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + 16 * ch);
-                    const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16 * ch + 8);
+                for (int ti = 0; ti < T::NT; ++ti) {
+                    const bf16 *vrow = &vt[buf][(32 * ti + j) * T::VP + 4 * hh + 16 * ch];
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 8);
                     const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
                     o[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ch], o[ti], 0, 0, 0);
                 }
-            }
+        };
+
+        if (ntiles > 0) load_tile(0);
+        for (int t = 0; t < ntiles; t += 2) {
+            tile(std::integral_constant<int, 0>{}, t);
+            if (t + 1 < ntiles) tile(std::integral_constant<int, 1>{}, t + 1);
         }
 
         // ---- epilogue: 1/l, optional per-row scale, bf16, 8-byte stores of 4 head channels
@@ -357,7 +407,7 @@ void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items) 
 hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     if (a.n_seg <= 0) return hipSuccess;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_q, a.cu_k, a.n_seg, a.len_q,
-                       a.len_k, a.n_heads, a.plan);
+                       a.len_k, a.n_heads, a.max_items, a.plan);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t fill_blocks = (a.max_items + 255) / 256;
@@ -373,10 +423,18 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
         g_num_cus = n;
     }
     const unsigned grid = (unsigned)(g_num_cus * 2);
-    if (a.head_dim == 128)
-        hipLaunchKernelGGL(attn_kernel<128>, dim3(grid), dim3(kAttnThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(attn_kernel<64>, dim3(grid), dim3(kAttnThreads), 0, s, a);
+    const dim3 blk(kAttnThreads);
+    if (a.head_dim == 128) {
+        if (a.kv_idx || a.q_idx)
+            hipLaunchKernelGGL((attn_kernel<128, true>), dim3(grid), blk, 0, s, a);
+        else
+            hipLaunchKernelGGL((attn_kernel<128, false>), dim3(grid), blk, 0, s, a);
+    } else {
+        if (a.kv_idx || a.q_idx)
+            hipLaunchKernelGGL((attn_kernel<64, true>), dim3(grid), blk, 0, s, a);
+        else
+            hipLaunchKernelGGL((attn_kernel<64, false>), dim3(grid), blk, 0, s, a);
+    }
     return hipGetLastError();
 }
 
