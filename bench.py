@@ -42,6 +42,9 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-stages", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (calibrates the HBM byte "
+                        "counters against a known size) and exit")
     return p.parse_args()
 
 
@@ -59,6 +62,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n_bytes = args.copy_calibration << 20
+        src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes}))
+        return
 
     import workloads
     from sparse_attention_long_moga_amd import api, metrics
