@@ -56,6 +56,9 @@ def load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
                            "(python -m sparse_attention_long_moga_amd.build)")
+    # torch ships its own HIP runtime under the same soname; loading torch first makes the
+    # library bind to that one instead of pulling a second runtime into the process
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, sz, st, i32, i64 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int32,
                             ctypes.c_int64)

@@ -24,13 +24,19 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "
          "-Wall", "-Wno-unused-function"]
 
 
+# Per-file flags.  attn.hip: attention scores are finite or -inf by construction, so the
+# row maximum needs no NaN-propagating max (without this flag every operand of v_max is
+# canonicalized first, doubling the maximum's VALU cost); infinities are still honoured.
+EXTRA_FLAGS = {"attn.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

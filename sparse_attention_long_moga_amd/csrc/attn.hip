@@ -42,7 +42,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // ---------------------------------------------------------------------------- planning
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const int32_t *cu_k,
                                                      int n_seg, int64_t len_q, int64_t len_k,
-                                                     int n_heads, int64_t max_items, AttnPlan p) {
+                                                     int n_heads, int bq, int64_t max_items,
+                                                     AttnPlan p) {
     __shared__ int s_klen[kPlanSortMax];
     __shared__ int s_order[kPlanSortMax];
     __shared__ int s_scan[1024];
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const i
         const int64_t kb = clamp64(cu_k[s], 0, len_k), ke = clamp64(cu_k[s + 1], kb, len_k);
         const int klen = (int)(ke - kb);
         p.seg_klen[s] = klen;
-        p.seg_ntile[s] = (int)((qe - qb + kAttnBQ - 1) / kAttnBQ);
+        p.seg_ntile[s] = (int)((qe - qb + bq - 1) / bq);
         if (sorted) s_klen[s] = klen;
     }
     __syncthreads();
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const i
         if (r < n_seg) {
             const int s = sorted ? s_order[r] : r;
             const int64_t qb = clamp64(cu_q[s], 0, len_q), qe = clamp64(cu_q[s + 1], qb, len_q);
-            v = n_heads * (int)((qe - qb + kAttnBQ - 1) / kAttnBQ);
+            v = n_heads * (int)((qe - qb + bq - 1) / bq);
         }
         s_scan[tid] = v;
         __syncthreads();
@@ -118,15 +119,17 @@ __global__ __launch_bounds__(256) void fill_items_kernel(AttnPlan p, int n_seg) 
 }
 
 // ---------------------------------------------------------------------------- attention
-template <int HD>
+template <int HD, int WAVES>
 struct Tile {
+    static constexpr int THREADS = 64 * WAVES;
     static constexpr int KP = HD + 8;       // K tile row pitch (bf16): rows shift 4 banks
     static constexpr int VP = KT + 4;       // V^T tile row pitch (bf16): 34 dwords
     static constexpr int NS = HD / 16;      // MFMA k-steps of S^T = K Q^T
     static constexpr int NT = HD / 32;      // 32-row tiles of O^T
-    static constexpr int KLOADS = KT * HD / 8 / kAttnThreads;   // 16-byte K chunks per thread
+    static constexpr int KLOADS = KT * HD / 8 / THREADS;   // 16-byte K chunks per thread
     static constexpr int XN = HD / 32;      // groups of 8 d-quads
-    static constexpr int VUNITS = XN / 2;   // 4x4 V blocks per thread
+    static constexpr int VCOMBOS = 4 * XN;  // 4x4 V blocks per tile, in units of 32 lanes
+    static constexpr int VUNITS = (VCOMBOS + 2 * WAVES - 1) / (2 * WAVES);
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -146,9 +149,13 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // use the same reference.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int HD, bool IDX>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
-    using T = Tile<HD>;
+// WAVES waves per block, 32 query rows each; every K/V tile brought into LDS serves all of
+// them, so 8 waves (256 rows, one block per CU, two waves per SIMD) halve the K/V traffic
+// from L2 and the per-wave load work relative to 4.
+template <int HD, bool IDX, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel(AttnLaunch a) {
+    using T = Tile<HD, WAVES>;
+    constexpr int BQ = 32 * WAVES;
     __shared__ __attribute__((aligned(16))) bf16 ks[2][KT * T::KP];
     __shared__ __attribute__((aligned(16))) bf16 vt[2][HD * T::VP];
     __shared__ int s_item;
@@ -163,16 +170,21 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
     int k_row[T::KLOADS], k_col[T::KLOADS];
 #pragma unroll
     for (int i = 0; i < T::KLOADS; ++i) {
-        const int cidx = tid + kAttnThreads * i;
+        const int cidx = tid + T::THREADS * i;
         k_row[i] = cidx / (HD / 8);
         k_col[i] = cidx % (HD / 8);
     }
+    // V: a "combo" is 32 lanes moving 4x4 blocks; lanes of one combo cover 8 d-quads x
+    // 4 key-quads, which keeps the transposed LDS writes bank-conflict free
     int v_ax[T::VUNITS], v_bx[T::VUNITS];
+    bool v_on[T::VUNITS];
 #pragma unroll
     for (int u = 0; u < T::VUNITS; ++u) {
-        const int combo = u * 8 + wave * 2 + hh;
-        v_ax[u] = (lane & 7) + 8 * (combo % T::XN);
-        v_bx[u] = ((lane >> 3) & 3) + 4 * (combo / T::XN);
+        const int combo = u * 2 * WAVES + wave * 2 + hh;
+        v_on[u] = combo < T::VCOMBOS;
+        const int cb = v_on[u] ? combo : 0;
+        v_ax[u] = (lane & 7) + 8 * (cb % T::XN);
+        v_bx[u] = ((lane >> 3) & 3) + 4 * (cb / T::XN);
     }
 
     for (;;) {
@@ -190,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
         const int klen = ke - kb;
 
         // ---- Q^T fragments (B operand): lane (query j, half hh) holds q[16s + 8hh .. +8)
-        const int qrow = qb + qt * kAttnBQ + wave * 32 + j;
+        const int qrow = qb + qt * BQ + wave * 32 + j;
         const bool qvalid = qrow < qe;
         const int qrow_c = qvalid ? qrow : qe - 1;   // qe > qb for every item
         const int64_t qphys = IDX ? (int64_t)a.q_idx[qrow_c] : (int64_t)qrow_c;
@@ -205,28 +217,32 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
         const bf16 *vbase = a.v + (int64_t)h * a.kv_rows * HD;
         const int ntiles = (klen + KT - 1) / KT;
 
-        uint4 kreg[T::KLOADS];
-        uint2 vreg[T::VUNITS][4];
-        auto load_tile = [&](int t) {
+        // two register sets: tile t+2 is requested while tile t is computed, so every load
+        // has two tiles of compute to arrive
+        uint4 kreg[2][T::KLOADS];
+        uint2 vreg[2][T::VUNITS][4];
+        auto load_tile = [&](auto rc, int t) {
+            constexpr int R = decltype(rc)::value;
             const int key0 = t * KT;
             if constexpr (!IDX) {
                 // rows [kb + key0, ke) of this head; rows past ke read as zeros
-                const uint32_t bytes = (uint32_t)(klen - key0) * HD * 2;
+                const uint32_t bytes = (uint32_t)max(klen - key0, 0) * HD * 2;
                 const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)(kb + key0) * HD, bytes);
                 const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)(kb + key0) * HD, bytes);
 #pragma unroll
                 for (int i = 0; i < T::KLOADS; ++i) {
                     const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
                         rk, (k_row[i] * HD + k_col[i] * 8) * 2, 0, 0);
-                    kreg[i] = make_uint4(w[0], w[1], w[2], w[3]);
+                    kreg[R][i] = make_uint4(w[0], w[1], w[2], w[3]);
                 }
 #pragma unroll
                 for (int u = 0; u < T::VUNITS; ++u)
+                    if (v_on[u])
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(
                             rv, ((4 * v_bx[u] + r) * HD + 4 * v_ax[u]) * 2, 0, 0);
-                        vreg[u][r] = make_uint2(w[0], w[1]);
+                        vreg[R][u][r] = make_uint2(w[0], w[1]);
                     }
             } else {
                 // gathered rows; rows past the segment are clamped to its last row (finite
@@ -236,25 +252,28 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
                 for (int i = 0; i < T::KLOADS; ++i) {
                     const int key = min(key0 + k_row[i], last);
                     const int64_t row = a.kv_idx[kb + key];
-                    kreg[i] = *reinterpret_cast<const uint4 *>(kbase + row * HD + k_col[i] * 8);
+                    kreg[R][i] = *reinterpret_cast<const uint4 *>(kbase + row * HD + k_col[i] * 8);
                 }
 #pragma unroll
                 for (int u = 0; u < T::VUNITS; ++u)
+                    if (v_on[u])
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int key = min(key0 + 4 * v_bx[u] + r, last);
                         const int64_t row = a.kv_idx[kb + key];
-                        vreg[u][r] = *reinterpret_cast<const uint2 *>(vbase + row * HD + 4 * v_ax[u]);
+                        vreg[R][u][r] = *reinterpret_cast<const uint2 *>(vbase + row * HD + 4 * v_ax[u]);
                     }
             }
         };
         auto store_tile = [&](int buf) {
 #pragma unroll
             for (int i = 0; i < T::KLOADS; ++i)
-                *reinterpret_cast<uint4 *>(&ks[buf][k_row[i] * T::KP + k_col[i] * 8]) = kreg[i];
+                *reinterpret_cast<uint4 *>(&ks[buf][k_row[i] * T::KP + k_col[i] * 8]) = kreg[buf][i];
 #pragma unroll
             for (int u = 0; u < T::VUNITS; ++u) {
-                const uint2 v0 = vreg[u][0], v1 = vreg[u][1], v2 = vreg[u][2], v3 = vreg[u][3];
+                if (!v_on[u]) continue;
+                const uint2 v0 = vreg[buf][u][0], v1 = vreg[buf][u][1], v2 = vreg[buf][u][2],
+                            v3 = vreg[buf][u][3];
                 // column cc of the 4 rows -> one 8-byte run of V^T row (4*ax + cc)
                 uint2 w[4];
                 w[0] = make_uint2(__builtin_amdgcn_perm(v1.x, v0.x, 0x05040100u),
@@ -279,11 +298,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
         // one tile: publish the prefetched registers into LDS buffer BUF, prefetch the next
         // tile, then S^T, softmax and O^T += V^T P^T.  BUF is a compile-time constant so all
         // LDS addresses fold into immediate offsets.
-        auto tile = [&](auto bufc, int t) {
+        auto tile = [&](auto bufc, auto maskc, int t) {
             constexpr int buf = decltype(bufc)::value;
+            constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
             store_tile(buf);
             __syncthreads();
-            if (t + 1 < ntiles) load_tile(t + 1);
+            if (t + 2 < ntiles) load_tile(bufc, t + 2);
 
             // S^T for two 32-key sub-blocks
             f32x16 sacc[2];
@@ -298,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
                     sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sb], 0, 0, 0);
                 }
             const int key0 = t * KT;
-            if (key0 + KT > klen) {
+            if constexpr (MASK) {
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -353,10 +373,26 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
                 }
         };
 
-        if (ntiles > 0) load_tile(0);
-        for (int t = 0; t < ntiles; t += 2) {
-            tile(std::integral_constant<int, 0>{}, t);
-            if (t + 1 < ntiles) tile(std::integral_constant<int, 1>{}, t + 1);
+        if (ntiles > 0) load_tile(std::integral_constant<int, 0>{}, 0);
+        if (ntiles > 1) load_tile(std::integral_constant<int, 1>{}, 1);
+        // full tiles without any masking code, then the partial last tile (if any) masked
+        const int nfull = klen / KT;
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        using NoMask = std::integral_constant<bool, false>;
+        using Mask = std::integral_constant<bool, true>;
+        int t = 0;
+        for (; t + 1 < nfull; t += 2) {
+            tile(B0{}, NoMask{}, t);
+            tile(B1{}, NoMask{}, t + 1);
+        }
+        if (t < nfull) {  // odd number of full tiles: t is even, buffer 0
+            tile(B0{}, NoMask{}, t);
+            ++t;
+        }
+        if (t < ntiles) {  // the partial tile; its buffer is t & 1
+            if (t & 1) tile(B1{}, Mask{}, t);
+            else tile(B0{}, Mask{}, t);
         }
 
         // ---- epilogue: 1/l, optional per-row scale, bf16, 8-byte stores of 4 head channels
@@ -378,12 +414,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnLaunch a) {
     }
 }
 
-int g_num_cus = 0;
+int g_num_cus[64];  // per device
 
 }  // namespace
 
 int64_t attn_max_items(int n_heads, int64_t len_q, int32_t n_seg) {
-    return (int64_t)n_heads * ((len_q + kAttnBQ - 1) / kAttnBQ + n_seg);
+    // sized for the smallest query tile any launch uses (128 rows)
+    return (int64_t)n_heads * ((len_q + kAttnBQMin - 1) / kAttnBQMin + n_seg);
 }
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -406,34 +443,41 @@ void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items) 
 
 hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     if (a.n_seg <= 0) return hipSuccess;
+    // Permuted MoGA groups are long: 8 waves (256 query rows) share every K/V tile.  Gathered
+    // STGA segments are short (195-1560 rows): 4 waves (128 rows) keep the padded tail small.
+    const bool indexed = a.kv_idx || a.q_idx;
+    const int waves = indexed ? 4 : 8;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_q, a.cu_k, a.n_seg, a.len_q,
-                       a.len_k, a.n_heads, a.max_items, a.plan);
+                       a.len_k, a.n_heads, 32 * waves, a.max_items, a.plan);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t fill_blocks = (a.max_items + 255) / 256;
     hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, s, a.plan,
                        a.n_seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (g_num_cus == 0) {
-        int dev = 0, n = 0;
-        if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (g_num_cus[dev] == 0) {
+        int n = 0;
         if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) !=
             hipSuccess)
             return e;
-        g_num_cus = n;
+        g_num_cus[dev] = n;
     }
-    const unsigned grid = (unsigned)(g_num_cus * 2);
-    const dim3 blk(kAttnThreads);
+    // persistent grid: two waves per SIMD either way
+    const dim3 grid((unsigned)(g_num_cus[dev] * (8 / waves)));
+    const dim3 blk((unsigned)(64 * waves));
     if (a.head_dim == 128) {
-        if (a.kv_idx || a.q_idx)
-            hipLaunchKernelGGL((attn_kernel<128, true>), dim3(grid), blk, 0, s, a);
+        if (indexed)
+            hipLaunchKernelGGL((attn_kernel<128, true, 4>), grid, blk, 0, s, a);
         else
-            hipLaunchKernelGGL((attn_kernel<128, false>), dim3(grid), blk, 0, s, a);
+            hipLaunchKernelGGL((attn_kernel<128, false, 8>), grid, blk, 0, s, a);
     } else {
-        if (a.kv_idx || a.q_idx)
-            hipLaunchKernelGGL((attn_kernel<64, true>), dim3(grid), blk, 0, s, a);
+        if (indexed)
+            hipLaunchKernelGGL((attn_kernel<64, true, 4>), grid, blk, 0, s, a);
         else
-            hipLaunchKernelGGL((attn_kernel<64, false>), dim3(grid), blk, 0, s, a);
+            hipLaunchKernelGGL((attn_kernel<64, false, 8>), grid, blk, 0, s, a);
     }
     return hipGetLastError();
 }

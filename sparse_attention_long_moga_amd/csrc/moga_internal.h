@@ -14,7 +14,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxGroups = 64;    // M <= 64
 constexpr int kMaxShots = 256;    // STGA shots passed by value
-constexpr int kAttnBQ = 128;      // query rows per attention work item (4 waves x 32)
+constexpr int kAttnBQMin = 128;   // smallest query rows per attention work item (4 waves x 32)
 constexpr int kAttnThreads = 256;
 constexpr int kPermTokensPerBlock = 2048;
 constexpr int kRouteTokensPerBlock = 256;
