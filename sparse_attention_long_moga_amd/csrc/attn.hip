@@ -414,6 +414,238 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel(AttnLaunch 
     }
 }
 
+// ---------------------------------------------------------------------------- attention,
+// head_dim 128, contiguous segments: K and V tiles go from HBM straight into LDS
+//
+// The permuted MoGA groups are contiguous rows, so each 16-byte chunk of a tile can be
+// fetched with a buffer load that writes LDS directly (no register staging, no LDS store
+// instructions).  Such a load places lane l's 16 bytes at base + 16*l, so the row layout
+// is chosen on the global side: LDS chunk c of row r holds global chunk c ^ sw(r).
+//   K: sw(r) = r & 15.  The A operand of S^T = K Q^T reads row j, chunk (2s + hh); 16
+//      consecutive rows then hit 16 different chunk positions, so each ds_read_b128 is
+//      bank-conflict free.
+//   V: natural [key][d] layout, sw(r) = 4 * (r & 3).  The A operand of O^T += V^T P^T is
+//      read with two ds_read_b64_tr_b16: within a group of 16 lanes, output lane 4a+b
+//      receives element b of the 8-byte pieces addressed by lanes a, a+4, a+8, a+12.  Lane
+//      s of group g points at row kc + 4*(g/2) + s/4 (+8 for the second read), columns
+//      32*ti + 16*(g%2) + 4*(s%4); lane d of the MFMA layout then holds V[4 keys][d], in
+//      the same key order as the probabilities.  The four rows a half-wave reads fall on
+//      four different 64-byte column ranges, so these reads are conflict free too.
+// LDS-side helpers of the direct-load kernel (kept out of lambdas: the host compilation
+// pass must not see the address-space-3 builtins)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char *lds_base,
+                                           int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset, 0, 0, 0);
+}
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(AttnLaunch a) {
+    constexpr int HD = 128;
+    constexpr int NS = HD / 16, NT = HD / 32;
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int BQ = 32 * WAVES;
+    constexpr int ROWB = HD * 2;                 // bytes per K or V row
+    constexpr int TILEB = KT * ROWB;             // bytes per K or V tile (16 KB)
+    constexpr int LOADS = TILEB / 16 / THREADS;  // direct 16-byte loads per thread per tile
+    static_assert(LOADS * THREADS * 16 == TILEB, "tile must split into whole wave loads");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2][2][TILEB];  // [buf][K, V]
+    __shared__ int s_item;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 31, hh = lane >> 5;
+    const int total = uniform(a.plan.counter[1]);
+    const float c = a.scale * kLog2e;
+    const float thr = kRescaleLog2 / c;
+
+    // per-lane LDS byte offsets of the MFMA operands within a tile
+    int koff[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) koff[s] = j * ROWB + (((2 * s + hh) ^ (j & 15)) << 4);
+    const int s16 = lane & 15, g = lane >> 4;
+    int voff[NT];
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti)
+        voff[ti] = (4 * (g >> 1) + (s16 >> 2)) * ROWB +
+                   ((((ti ^ (s16 >> 2)) << 2) + 2 * (g & 1) + ((s16 & 3) >> 1)) << 4) + (s16 & 1) * 8;
+    // per-lane global byte offsets of the direct loads within a tile
+    int kgo[LOADS], vgo[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int r = (i * WAVES + wave) * 4 + (lane >> 4);
+        kgo[i] = r * ROWB + ((s16 ^ (r & 15)) << 4);
+        vgo[i] = r * ROWB + ((s16 ^ (4 * (r & 3))) << 4);
+    }
+
+    for (;;) {
+        if (tid == 0) s_item = atomicAdd(a.plan.counter, 1);
+        __syncthreads();
+        const int item = uniform(s_item);
+        __syncthreads();
+        if (item >= total) break;
+        const int4 itm = a.plan.items[item];
+        const int seg = uniform(itm.x), h = uniform(itm.y), qt = uniform(itm.z);
+        const int qb = uniform((int)clamp64(a.cu_q[seg], 0, a.len_q));
+        const int qe = uniform((int)clamp64(a.cu_q[seg + 1], qb, a.len_q));
+        const int kb = uniform((int)clamp64(a.cu_k[seg], 0, a.len_k));
+        const int ke = uniform((int)clamp64(a.cu_k[seg + 1], kb, a.len_k));
+        const int klen = ke - kb;
+
+        const int qrow = qb + qt * BQ + wave * 32 + j;
+        const bool qvalid = qrow < qe;
+        const int64_t qphys = qvalid ? qrow : qe - 1;
+        bf16x8 qf[NS];
+        {
+            const bf16 *qp = a.q + (int64_t)h * a.q_rows * HD + qphys * HD + 8 * hh;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
+        }
+        const bf16 *kbase = a.k + (int64_t)h * a.kv_rows * HD;
+        const bf16 *vbase = a.v + (int64_t)h * a.kv_rows * HD;
+        const int ntiles = (klen + KT - 1) / KT;
+
+        // tile t -> LDS buffer BUF; rows past the segment read as zeros
+        auto issue = [&](auto bufc, int t) {
+            constexpr int buf = decltype(bufc)::value;
+            const int key0 = t * KT;
+            const uint32_t bytes = (uint32_t)max(klen - key0, 0) * ROWB;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)(kb + key0) * HD, bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)(kb + key0) * HD, bytes);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int slot = (i * WAVES + wave) * 1024;
+                load_lds16(rk, &lds[buf][0][slot], kgo[i]);
+                load_lds16(rv, &lds[buf][1][slot], vgo[i]);
+            }
+        };
+
+        float m_run = -INFINITY, l_run = 0.0f;
+        f32x16 o[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) o[ti] = f32x16{};
+
+        auto tile = [&](auto bufc, auto maskc, int t) {
+            constexpr int buf = decltype(bufc)::value;
+            constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
+            if (t + 1 < ntiles) issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
+            const unsigned char *kt = lds[buf][0];
+            const unsigned char *vt_ = lds[buf][1];
+
+            f32x16 sacc[2];
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) sacc[sb] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kt + sb * 32 * ROWB + koff[s]);
+                    sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sb], 0, 0, 0);
+                }
+            if constexpr (MASK) {
+                const int key0 = t * KT;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = key0 + sb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+                        if (key >= klen) sacc[sb][v] = -INFINITY;
+                    }
+            }
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) tmax = fmaxf(tmax, fmaxf(sacc[sb][v], sacc[sb][v + 1]));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const bool up = tmax > m_run + thr;
+            if (__ballot(up)) {
+                const float m_new = up ? tmax : m_run;
+                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[ti][v] *= alpha;
+            }
+            const float mc = m_run * c;
+            bf16x8 pf[4];
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    float pv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][half * 8 + e], c, -mc));
+                        l_run += pv[e];
+                    }
+                    const uint4 packed = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                                    pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+                    pf[sb * 2 + half] = __builtin_bit_cast(bf16x8, packed);
+                }
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti) {
+                    const unsigned char *vp = vt_ + ch * 16 * ROWB + voff[ti];
+                    const uint2 ulo = lds_read_tr16(vp), uhi = lds_read_tr16(vp + 8 * ROWB);
+                    const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+                    o[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ch], o[ti], 0, 0, 0);
+                }
+            // the next tile's direct loads must have landed before anyone reads them
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+            __syncthreads();
+        };
+
+        if (ntiles > 0) {
+            issue(std::integral_constant<int, 0>{}, 0);
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+            __syncthreads();
+        }
+        const int nfull = klen / KT;
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        using NoMask = std::integral_constant<bool, false>;
+        using Mask = std::integral_constant<bool, true>;
+        int t = 0;
+        for (; t + 1 < nfull; t += 2) {
+            tile(B0{}, NoMask{}, t);
+            tile(B1{}, NoMask{}, t + 1);
+        }
+        if (t < nfull) {
+            tile(B0{}, NoMask{}, t);
+            ++t;
+        }
+        if (t < ntiles) {
+            if (t & 1) tile(B1{}, Mask{}, t);
+            else tile(B0{}, Mask{}, t);
+        }
+
+        const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+        if (qvalid) {
+            float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            if (a.row_scale) inv *= a.row_scale[qphys];
+            bf16 *op = a.o + (int64_t)h * a.o_rows * HD + qphys * HD + 4 * hh;
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) {
+                    const uint2 w = make_uint2(
+                        pack_bf16x2(o[ti][kq * 4 + 0] * inv, o[ti][kq * 4 + 1] * inv),
+                        pack_bf16x2(o[ti][kq * 4 + 2] * inv, o[ti][kq * 4 + 3] * inv));
+                    *reinterpret_cast<uint2 *>(op + 32 * ti + 8 * kq) = w;
+                }
+        }
+    }
+}
+
 int g_num_cus[64];  // per device
 
 }  // namespace
@@ -472,7 +704,7 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
         if (indexed)
             hipLaunchKernelGGL((attn_kernel<128, true, 4>), grid, blk, 0, s, a);
         else
-            hipLaunchKernelGGL((attn_kernel<128, false, 8>), grid, blk, 0, s, a);
+            hipLaunchKernelGGL((attn_kernel_direct<8>), grid, blk, 0, s, a);
     } else {
         if (indexed)
             hipLaunchKernelGGL((attn_kernel<64, true, 4>), grid, blk, 0, s, a);
