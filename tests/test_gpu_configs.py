@@ -1,0 +1,86 @@
+"""Parity at the full sizes of the five workloads, in the launch configuration the benchmark
+times (one moga_forward call through the C ABI).
+
+Routing, cu_seqlens, perm, counts (F_i), P_i and the loss are compared on every token.
+Attention outputs are compared on seeded samples of output rows, which the oracle computes
+one by one: two heads and up to 64 tokens per group (and, for the hybrid workloads, tokens
+in the frames on either side of every shot boundary, where keys/values borrow frames)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from sparse_attention_long_moga_amd import api
+from tests.helpers import assert_close_bf16, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _sample_rows(wl, group_id, heads, per_group, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    toks = []
+    for gidx in range(wl.n_groups):
+        members = np.flatnonzero(group_id == gidx)
+        if members.size:
+            toks.append(rng.choice(members, size=min(per_group, members.size), replace=False))
+    if wl.hybrid:
+        hw = wl.height * wl.width
+        for s in wl.shot_start[1:-1]:  # last frame before and first frame after each cut
+            for f in (s - 1, s):
+                toks.append(f * hw + rng.choice(hw, size=4, replace=False))
+    t = np.unique(np.concatenate(toks))
+    rows_h = np.repeat(np.arange(len(heads)), t.size)
+    rows_t = np.tile(t, len(heads))
+    return rows_h, rows_t
+
+
+@pytest.mark.parametrize("wl", workloads.CONFIGS, ids=[w.name for w in workloads.CONFIGS])
+def test_full_size_forward(wl):
+    print(f"[case] full-size forward {wl.name}", flush=True)
+    x, w = workloads.make_x(wl, DEV), workloads.make_w(wl, DEV)
+    q, k, v = workloads.make_qkv(wl, DEV)
+    n, m, hd = wl.n_tokens, wl.n_groups, wl.head_dim
+    xh = host(x)
+    ref = oracle.route(xh, host(w))
+    del xh
+    pin = torch.from_numpy(oracle.near_tie_pins(ref)).to(DEV)
+    lay = None
+    grid = None
+    if wl.hybrid:
+        grid = oracle.grid_of(wl)
+        lay = api.make_stga_layout(**grid)
+    got = api.moga_forward(x, w, q, k, v, m, alpha=wl.alpha, pin=pin, stga=lay)
+    torch.cuda.synchronize()
+    del x
+
+    # routing, groups, loss: every token
+    np.testing.assert_array_equal(host(got["group_id"]), ref["group_id"])
+    np.testing.assert_array_equal(host(got["counts"]), ref["counts"])
+    cu_ref, perm_ref = oracle.groups(ref["group_id"], m)
+    np.testing.assert_array_equal(host(got["cu_seqlens"]), cu_ref)
+    np.testing.assert_array_equal(host(got["perm"]), perm_ref)
+    assert np.abs(host(got["prob_sum"]) / n - ref["prob_sum"] / n).max() < 1e-6
+    loss_ref = oracle.balance_loss(ref["counts"], ref["prob_sum"], n, wl.alpha)[0]
+    assert abs(float(got["loss"].item()) - loss_ref) < 1e-6
+
+    # attention: sampled rows of two heads
+    heads = [0, wl.n_heads - 1]
+    rows_h, rows_t = _sample_rows(wl, ref["group_id"], heads, 64 if m <= 5 else 16, wl.seed + 7)
+    qh = np.stack([host(q[i]) for i in heads])
+    kh = np.stack([host(k[i]) for i in heads])
+    vh = np.stack([host(v[i]) for i in heads])
+    scale = 1.0 / math.sqrt(hd)
+    want, _ = oracle.moga_attn(qh, kh, vh, ref["group_id"], m, ref["p_sel"], scale, rows_h, rows_t)
+    if wl.hybrid:
+        wt, _ = oracle.stga_attn(qh, kh, vh, grid, "temporal", scale, rows_h, rows_t)
+        wf, _ = oracle.stga_attn(qh, kh, vh, grid, "frame", scale, rows_h, rows_t)
+        want = (want + wt + wf) / 3.0
+    out = got["out"]
+    gh = torch.tensor([heads[i] for i in rows_h], device=DEV)
+    gt = torch.from_numpy(rows_t).to(DEV)
+    have = host(out[gh, gt])
+    assert_close_bf16(have, want, f"{wl.name} sampled rows ({rows_t.size // len(heads)} tokens x 2 heads)")
