@@ -180,6 +180,16 @@ moga_status moga_balance_loss(const int32_t *counts, const double *prob_sum,
 moga_status moga_forward(const moga_inputs *in, const moga_dims *dims, const stga_layout *stga,
                          const moga_outputs *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Permute-free variant of moga_forward, for the same inputs and outputs: the attention
+ * kernel reads the query, key and value rows of each group through perm and writes every
+ * output row straight back to its token, so the permuted copies of Q, K, V and O and the
+ * two row gathers are skipped.  Keys are visited in the same order, so every output is
+ * bitwise identical to moga_forward's.  perm and cu_seqlens are still computed (and
+ * returned if requested).  ws: moga_workspace_bytes(dims, stga). */
+moga_status moga_forward_fused(const moga_inputs *in, const moga_dims *dims,
+                               const stga_layout *stga, const moga_outputs *out, void *ws,
+                               size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

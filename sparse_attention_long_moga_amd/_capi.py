@@ -14,7 +14,7 @@ STATUS_NAMES = {0: "MOGA_OK", 1: "MOGA_ERR_ARG", 2: "MOGA_ERR_UNSUPPORTED",
 
 EXPORTS = ["moga_last_error", "moga_workspace_bytes", "moga_group_attn_workspace_bytes",
            "moga_route", "moga_permute", "moga_group_attn", "stga_group_attn",
-           "moga_balance_loss", "moga_forward"]
+           "moga_balance_loss", "moga_forward", "moga_forward_fused"]
 
 
 class MogaDims(ctypes.Structure):
@@ -83,6 +83,8 @@ def load(path: str = LIB_PATH):
     lib.moga_forward.argtypes = [ctypes.POINTER(MogaInputs), pdims, pstga,
                                  ctypes.POINTER(MogaOutputs), vp, sz, vp]
     lib.moga_forward.restype = st
+    lib.moga_forward_fused.argtypes = lib.moga_forward.argtypes
+    lib.moga_forward_fused.restype = st
     _lib = lib
     return lib
 

@@ -17,7 +17,7 @@ from ._capi import MogaDims, MogaInputs, MogaOutputs, StgaLayout, check
 
 __all__ = ["make_dims", "make_stga_layout", "moga_workspace_bytes", "workspace", "moga_route",
            "moga_permute", "moga_unpermute", "moga_group_attn", "stga_group_attn",
-           "moga_balance_loss", "moga_forward"]
+           "moga_balance_loss", "moga_forward", "moga_forward_fused"]
 
 
 def _lib():
@@ -239,10 +239,12 @@ def moga_forward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Ten
                  v: torch.Tensor, n_groups: int, alpha: float = 0.1,
                  pin: Optional[torch.Tensor] = None, stga: Optional[_Layout] = None,
                  softmax_scale: float = 0.0, ws: Optional[torch.Tensor] = None,
-                 out: Optional[dict] = None) -> dict:
+                 out: Optional[dict] = None, fused: bool = False) -> dict:
     """Whole forward.  Returns a dict with out, loss and the routing tensors
     (group_id, p_sel, cu_seqlens, perm, counts, prob_sum).  Pass `out` (a dict of
-    preallocated tensors with those keys) and `ws` to run without allocating."""
+    preallocated tensors with those keys) and `ws` to run without allocating.
+    fused=True calls moga_forward_fused (rows read through perm inside the attention
+    kernel; bitwise identical results)."""
     _need(x, "x", ndim=2)
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("x must be float32 or bfloat16")
@@ -270,6 +272,12 @@ def moga_forward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Ten
     g = lambda key: out[key].data_ptr() if out.get(key) is not None else None
     outs = MogaOutputs(g("out"), g("loss"), g("group_id"), g("p_sel"), g("cu_seqlens"), g("perm"),
                        g("counts"), g("prob_sum"))
-    check(_lib().moga_forward(ctypes.byref(ins), ctypes.byref(dims), stga.ref() if stga else None,
-                              ctypes.byref(outs), _ptr(ws), ws.numel(), _stream()))
+    fn = _lib().moga_forward_fused if fused else _lib().moga_forward
+    check(fn(ctypes.byref(ins), ctypes.byref(dims), stga.ref() if stga else None,
+             ctypes.byref(outs), _ptr(ws), ws.numel(), _stream()))
     return out
+
+
+def moga_forward_fused(*args, **kwargs) -> dict:
+    """moga_forward with the permutation applied inside the attention kernel."""
+    return moga_forward(*args, fused=True, **kwargs)

@@ -241,7 +241,8 @@ moga_status run_attn(const void *q, const void *k, const void *v, void *o, const
                      const int32_t *cu_k, int32_t n_seg, const int32_t *q_idx,
                      const int32_t *kv_idx, const float *row_scale, int64_t len_q, int64_t len_k,
                      int64_t q_rows, int64_t kv_rows, int64_t o_rows, const moga_dims *d,
-                     void *plan_mem, int32_t plan_seg, int64_t plan_items, hipStream_t s) {
+                     void *plan_mem, int32_t plan_seg, int64_t plan_items, int waves,
+                     hipStream_t s) {
     AttnLaunch a{};
     a.q = static_cast<const bf16 *>(q); a.k = static_cast<const bf16 *>(k);
     a.v = static_cast<const bf16 *>(v); a.o = static_cast<bf16 *>(o);
@@ -250,6 +251,7 @@ moga_status run_attn(const void *q, const void *k, const void *v, void *o, const
     a.q_rows = q_rows; a.kv_rows = kv_rows; a.o_rows = o_rows;
     a.n_heads = d->n_heads; a.head_dim = d->head_dim; a.scale = scale_of(d);
     a.max_items = attn_max_items(d->n_heads, len_q, n_seg);
+    a.waves = waves;
     if (a.max_items > plan_items || n_seg > plan_seg)
         return fail(MOGA_ERR_WORKSPACE, "attention plan larger than its workspace region");
     attn_plan_carve(a.plan, plan_mem, n_seg, a.max_items);
@@ -271,12 +273,12 @@ moga_status run_stga(const void *q, const void *k, const void *v, const moga_dim
         const int32_t ng = stga_n_groups(g);
         moga_status st = run_attn(q, k, v, o_t, b.cu_tq, b.cu_tk, ng, b.q_idx, b.kv_idx, nullptr, n,
                                   n + stga_extra_rows(g), n, n, n, d, plan, L.plan_seg,
-                                  L.plan_items, s);
+                                  L.plan_items, 4, s);
         if (st != MOGA_OK) return st;
     }
     if (o_f) {
         moga_status st = run_attn(q, k, v, o_f, b.cu_f, b.cu_f, g.frames, nullptr, nullptr, nullptr,
-                                  n, n, n, n, n, d, plan, L.plan_seg, L.plan_items, s);
+                                  n, n, n, n, n, d, plan, L.plan_seg, L.plan_items, 4, s);
         if (st != MOGA_OK) return st;
     }
     return MOGA_OK;
@@ -360,8 +362,10 @@ moga_status moga_group_attn(const void *q, const void *k, const void *v, int64_t
     const size_t need = attn_plan_bytes(n_seg, items);
     if ((st = check_ws(ws, ws_bytes, need)) != MOGA_OK) return st;
     if ((st = check_device()) != MOGA_OK) return st;
+    // long segments on average: 256-row query tiles; short ones: 128
+    const int waves = len_q / n_seg >= 1024 ? 8 : 4;
     return run_attn(q, k, v, o, cu_q, cu_k, n_seg, nullptr, nullptr, row_scale, len_q, len_k, len_q,
-                    len_k, len_q, dims, ws, n_seg, items, static_cast<hipStream_t>(stream));
+                    len_k, len_q, dims, ws, n_seg, items, waves, static_cast<hipStream_t>(stream));
 }
 
 moga_status stga_group_attn(const void *q, const void *k, const void *v, const moga_dims *dims,
@@ -394,8 +398,9 @@ moga_status moga_balance_loss(const int32_t *counts, const double *prob_sum,
     return MOGA_OK;
 }
 
-moga_status moga_forward(const moga_inputs *in, const moga_dims *dims, const stga_layout *stga,
-                         const moga_outputs *out, void *ws, size_t ws_bytes, void *stream) {
+static moga_status forward_impl(const moga_inputs *in, const moga_dims *dims, const stga_layout *stga,
+                         const moga_outputs *out, void *ws, size_t ws_bytes, void *stream,
+                         bool fused) {
     moga_status st = check_dims(dims);
     if (st != MOGA_OK) return st;
     if (!in || !out) return fail(MOGA_ERR_ARG, "inputs or outputs is NULL");
@@ -418,25 +423,35 @@ moga_status moga_forward(const moga_inputs *in, const moga_dims *dims, const stg
     double *probsum = out->prob_sum ? out->prob_sum : at<double>(ws, L.probsum);
     int32_t *cu = out->cu_seqlens ? out->cu_seqlens : at<int32_t>(ws, L.cu);
     int32_t *perm = out->perm ? out->perm : at<int32_t>(ws, L.perm);
-    float *pperm = at<float>(ws, L.pperm);
-    void *qp = at<char>(ws, L.qp), *kp = at<char>(ws, L.kp), *vp = at<char>(ws, L.vp);
-    void *op = at<char>(ws, L.op);
+    void *plan = at<char>(ws, L.plan);
 
-    // 1 route  2 histogram/scan/stable permutation  3 gather Q,K,V and p by perm
+    // 1 route  2 histogram/scan/stable permutation
     if ((st = run_route(in->x, in->x_dtype, in->w, in->pin, dims, gid, psel, counts, probsum, ws,
                         L, s)) != MOGA_OK)
         return st;
     if ((st = run_perm_index(gid, dims, cu, perm, ws, L, s)) != MOGA_OK) return st;
-    const void *src[3] = {in->q, in->k, in->v};
-    void *dst[3] = {qp, kp, vp};
-    if ((st = run_gather(0, perm, dims, src, dst, 3, psel, pperm, s)) != MOGA_OK) return st;
-    // 4 varlen group attention scaled by p(g|x)  5 back to token order
-    if ((st = run_attn(qp, kp, vp, op, cu, cu, dims->n_groups, nullptr, nullptr, pperm, n, n, n, n,
-                       n, dims, at<char>(ws, L.plan), L.plan_seg, L.plan_items, s)) != MOGA_OK)
-        return st;
-    const void *osrc[1] = {op};
-    void *odst[1] = {out->out};
-    if ((st = run_gather(1, perm, dims, osrc, odst, 1, nullptr, nullptr, s)) != MOGA_OK) return st;
+    if (fused) {
+        // 3-5 in one pass: rows are read through perm and written back in token order
+        if ((st = run_attn(in->q, in->k, in->v, out->out, cu, cu, dims->n_groups, perm, perm, psel,
+                           n, n, n, n, n, dims, plan, L.plan_seg, L.plan_items, 8, s)) != MOGA_OK)
+            return st;
+    } else {
+        // 3 gather Q, K, V and p by perm  4 varlen group attention scaled by p(g|x)
+        // 5 back to token order
+        float *pperm = at<float>(ws, L.pperm);
+        void *qp = at<char>(ws, L.qp), *kp = at<char>(ws, L.kp), *vp = at<char>(ws, L.vp);
+        void *op = at<char>(ws, L.op);
+        const void *src[3] = {in->q, in->k, in->v};
+        void *dst[3] = {qp, kp, vp};
+        if ((st = run_gather(0, perm, dims, src, dst, 3, psel, pperm, s)) != MOGA_OK) return st;
+        if ((st = run_attn(qp, kp, vp, op, cu, cu, dims->n_groups, nullptr, nullptr, pperm, n, n, n,
+                           n, n, dims, plan, L.plan_seg, L.plan_items, 8, s)) != MOGA_OK)
+            return st;
+        const void *osrc[1] = {op};
+        void *odst[1] = {out->out};
+        if ((st = run_gather(1, perm, dims, osrc, odst, 1, nullptr, nullptr, s)) != MOGA_OK)
+            return st;
+    }
     // 6 group-balancing loss
     HIP_TRY(launch_balance_loss(counts, probsum, n, dims->n_groups, dims->alpha, out->loss, nullptr,
                                 nullptr, s),
@@ -450,6 +465,17 @@ moga_status moga_forward(const moga_inputs *in, const moga_dims *dims, const stg
                             (int64_t)dims->n_heads * n * dims->head_dim, s),
             "combine launch");
     return MOGA_OK;
+}
+
+moga_status moga_forward(const moga_inputs *in, const moga_dims *dims, const stga_layout *stga,
+                         const moga_outputs *out, void *ws, size_t ws_bytes, void *stream) {
+    return forward_impl(in, dims, stga, out, ws, ws_bytes, stream, false);
+}
+
+moga_status moga_forward_fused(const moga_inputs *in, const moga_dims *dims,
+                               const stga_layout *stga, const moga_outputs *out, void *ws,
+                               size_t ws_bytes, void *stream) {
+    return forward_impl(in, dims, stga, out, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

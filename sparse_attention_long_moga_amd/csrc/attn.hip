@@ -205,7 +205,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel(AttnLaunch 
         const int qrow = qb + qt * BQ + wave * 32 + j;
         const bool qvalid = qrow < qe;
         const int qrow_c = qvalid ? qrow : qe - 1;   // qe > qb for every item
-        const int64_t qphys = IDX ? (int64_t)a.q_idx[qrow_c] : (int64_t)qrow_c;
+        // indexed rows are clamped to the head so a bad map cannot address outside it
+        const int64_t qphys = IDX ? min(max((int64_t)a.q_idx[qrow_c], (int64_t)0), a.q_rows - 1)
+                                  : (int64_t)qrow_c;
         bf16x8 qf[T::NS];
         {
             const bf16 *qp = a.q + (int64_t)h * a.q_rows * HD + qphys * HD + 8 * hh;
@@ -445,7 +447,9 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-template <int WAVES>
+// IDX: rows are read through the index maps (STGA groups, or the permutation itself for
+// the permute-free MoGA variant); each lane then fetches its chunk's row index first.
+template <int WAVES, bool IDX>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(AttnLaunch a) {
     constexpr int HD = 128;
     constexpr int NS = HD / 16, NT = HD / 32;
@@ -475,12 +479,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         voff[ti] = (4 * (g >> 1) + (s16 >> 2)) * ROWB +
                    ((((ti ^ (s16 >> 2)) << 2) + 2 * (g & 1) + ((s16 & 3) >> 1)) << 4) + (s16 & 1) * 8;
     // per-lane global byte offsets of the direct loads within a tile
-    int kgo[LOADS], vgo[LOADS];
+    int kgo[LOADS], vgo[LOADS], lrow[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
         const int r = (i * WAVES + wave) * 4 + (lane >> 4);
-        kgo[i] = r * ROWB + ((s16 ^ (r & 15)) << 4);
-        vgo[i] = r * ROWB + ((s16 ^ (4 * (r & 3))) << 4);
+        lrow[i] = r;
+        kgo[i] = ((s16 ^ (r & 15)) << 4) + (IDX ? 0 : r * ROWB);
+        vgo[i] = ((s16 ^ (4 * (r & 3))) << 4) + (IDX ? 0 : r * ROWB);
     }
 
     for (;;) {
@@ -499,7 +504,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
 
         const int qrow = qb + qt * BQ + wave * 32 + j;
         const bool qvalid = qrow < qe;
-        const int64_t qphys = qvalid ? qrow : qe - 1;
+        const int qrow_c = qvalid ? qrow : qe - 1;  // qe > qb for every item
+        // indexed rows are clamped to the head so a bad map cannot address outside it
+        const int64_t qphys = IDX ? min(max((int64_t)a.q_idx[qrow_c], (int64_t)0), a.q_rows - 1)
+                                  : (int64_t)qrow_c;
         bf16x8 qf[NS];
         {
             const bf16 *qp = a.q + (int64_t)h * a.q_rows * HD + qphys * HD + 8 * hh;
@@ -510,18 +518,35 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         const bf16 *vbase = a.v + (int64_t)h * a.kv_rows * HD;
         const int ntiles = (klen + KT - 1) / KT;
 
-        // tile t -> LDS buffer BUF; rows past the segment read as zeros
+        // whole-head descriptors for gathered rows (every index is a row of this head)
+        const __amdgpu_buffer_rsrc_t rk_head = make_rsrc(kbase, (uint32_t)(a.kv_rows * ROWB));
+        const __amdgpu_buffer_rsrc_t rv_head = make_rsrc(vbase, (uint32_t)(a.kv_rows * ROWB));
+
+        // tile t -> LDS buffer BUF.  Contiguous rows: rows past the segment read as zeros.
+        // Gathered rows: rows past the segment are clamped to its last row (finite data whose
+        // scores are masked and whose probabilities are zero).
         auto issue = [&](auto bufc, int t) {
             constexpr int buf = decltype(bufc)::value;
             const int key0 = t * KT;
-            const uint32_t bytes = (uint32_t)max(klen - key0, 0) * ROWB;
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)(kb + key0) * HD, bytes);
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)(kb + key0) * HD, bytes);
+            if constexpr (!IDX) {
+                const uint32_t bytes = (uint32_t)max(klen - key0, 0) * ROWB;
+                const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)(kb + key0) * HD, bytes);
+                const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)(kb + key0) * HD, bytes);
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int slot = (i * WAVES + wave) * 1024;
-                load_lds16(rk, &lds[buf][0][slot], kgo[i]);
-                load_lds16(rv, &lds[buf][1][slot], vgo[i]);
+                for (int i = 0; i < LOADS; ++i) {
+                    const int slot = (i * WAVES + wave) * 1024;
+                    load_lds16(rk, &lds[buf][0][slot], kgo[i]);
+                    load_lds16(rv, &lds[buf][1][slot], vgo[i]);
+                }
+            } else {
+                const int last = klen - 1;
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    const int slot = (i * WAVES + wave) * 1024;
+                    const int row = a.kv_idx[kb + min(key0 + lrow[i], last)];
+                    load_lds16(rk_head, &lds[buf][0][slot], row * ROWB + kgo[i]);
+                    load_lds16(rv_head, &lds[buf][1][slot], row * ROWB + vgo[i]);
+                }
             }
         };
 
@@ -675,12 +700,15 @@ void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items) 
 
 hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     if (a.n_seg <= 0) return hipSuccess;
-    // Permuted MoGA groups are long: 8 waves (256 query rows) share every K/V tile.  Gathered
-    // STGA segments are short (195-1560 rows): 4 waves (128 rows) keep the padded tail small.
+    // MoGA groups are long: 8 waves (256 query rows) share every K/V tile.  STGA segments are
+    // short (195-1560 rows): 4 waves (128 rows) keep the padded tail small.  Heads whose K/V
+    // exceed the 32-bit buffer offset range take the generic kernel.
     const bool indexed = a.kv_idx || a.q_idx;
-    const int waves = indexed ? 4 : 8;
+    const bool direct = a.head_dim == 128 && a.kv_rows * 256 < (int64_t(1) << 31);
+    const int waves = a.waves == 4 ? 4 : 8;
+    const int bq = direct ? 32 * waves : (indexed ? 128 : 256);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_q, a.cu_k, a.n_seg, a.len_q,
-                       a.len_k, a.n_heads, 32 * waves, a.max_items, a.plan);
+                       a.len_k, a.n_heads, bq, a.max_items, a.plan);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t fill_blocks = (a.max_items + 255) / 256;
@@ -697,19 +725,24 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
             return e;
         g_num_cus[dev] = n;
     }
-    // persistent grid: two waves per SIMD either way
-    const dim3 grid((unsigned)(g_num_cus[dev] * (8 / waves)));
-    const dim3 blk((unsigned)(64 * waves));
-    if (a.head_dim == 128) {
-        if (indexed)
-            hipLaunchKernelGGL((attn_kernel<128, true, 4>), grid, blk, 0, s, a);
-        else
-            hipLaunchKernelGGL((attn_kernel_direct<8>), grid, blk, 0, s, a);
+    // persistent grids: two waves per SIMD in every configuration
+    const dim3 grid((unsigned)(g_num_cus[dev] * (8 / waves))), blk((unsigned)(64 * waves));
+    const dim3 grid4((unsigned)(g_num_cus[dev] * 2)), blk4(256u);
+    const dim3 grid8((unsigned)g_num_cus[dev]), blk8(512u);
+    if (direct) {
+        if (indexed) {
+            if (waves == 8) hipLaunchKernelGGL((attn_kernel_direct<8, true>), grid, blk, 0, s, a);
+            else hipLaunchKernelGGL((attn_kernel_direct<4, true>), grid, blk, 0, s, a);
+        } else {
+            if (waves == 8) hipLaunchKernelGGL((attn_kernel_direct<8, false>), grid, blk, 0, s, a);
+            else hipLaunchKernelGGL((attn_kernel_direct<4, false>), grid, blk, 0, s, a);
+        }
+    } else if (a.head_dim == 128) {
+        if (indexed) hipLaunchKernelGGL((attn_kernel<128, true, 4>), grid4, blk4, 0, s, a);
+        else hipLaunchKernelGGL((attn_kernel<128, false, 8>), grid8, blk8, 0, s, a);
     } else {
-        if (indexed)
-            hipLaunchKernelGGL((attn_kernel<64, true, 4>), grid, blk, 0, s, a);
-        else
-            hipLaunchKernelGGL((attn_kernel<64, false, 8>), grid, blk, 0, s, a);
+        if (indexed) hipLaunchKernelGGL((attn_kernel<64, true, 4>), grid4, blk4, 0, s, a);
+        else hipLaunchKernelGGL((attn_kernel<64, false, 8>), grid8, blk8, 0, s, a);
     }
     return hipGetLastError();
 }

@@ -95,6 +95,7 @@ struct AttnLaunch {
     float scale;
     AttnPlan plan;
     int64_t max_items;
+    int waves;               // 8: long segments (MoGA groups), 4: short ones (STGA)
 };
 hipError_t launch_attention(const AttnLaunch &a, hipStream_t s);
 

@@ -254,3 +254,28 @@ def test_balance_loss_parity():
     assert float(loss.item()) == pytest.approx(l_ref, abs=1e-15)
     np.testing.assert_array_equal(host(F), F_ref)
     np.testing.assert_allclose(host(P), P_ref, atol=1e-16)
+
+
+@pytest.mark.parametrize("hybrid", [False, True])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_fused_forward_is_bitwise_the_explicit_one(hybrid, hd):
+    _announce("fused_vs_explicit", hybrid=hybrid, hd=hd)
+    wl, x, w, q, k, v, grid = _forward_case(18, 2, hd, 5, 41 + hd, hybrid)
+    lay = api.make_stga_layout(**grid) if hybrid else None
+    a = api.moga_forward(x, w, q, k, v, 5, stga=lay)
+    b = api.moga_forward_fused(x, w, q, k, v, 5, stga=lay)
+    torch.cuda.synchronize()
+    for key in ("out", "group_id", "perm", "cu_seqlens", "p_sel", "prob_sum", "counts", "loss"):
+        assert torch.equal(a[key], b[key]), key
+    # and against the oracle
+    n, m = wl.n_tokens, wl.n_groups
+    ref_r = oracle.route(host(x), host(w))
+    scale = 1 / math.sqrt(hd)
+    rows_h, rows_t = np.repeat(np.arange(2), n), np.tile(np.arange(n), 2)
+    qh, kh, vh = host(q), host(k), host(v)
+    ref, _ = oracle.moga_attn(qh, kh, vh, ref_r["group_id"], m, ref_r["p_sel"], scale, rows_h,
+                              rows_t)
+    if hybrid:
+        ref = (ref + oracle.stga_attn(qh, kh, vh, grid, "temporal", scale, rows_h, rows_t)[0]
+               + oracle.stga_attn(qh, kh, vh, grid, "frame", scale, rows_h, rows_t)[0]) / 3.0
+    assert_close_bf16(host(b["out"]).reshape(-1, hd), ref, f"fused hybrid={hybrid}")
