@@ -124,7 +124,7 @@ struct Carver {
 
 struct Layout {
     // MoGA
-    size_t part_p, part_c, gid, psel, counts, probsum, cu, perm, table, base_rel, totals, pperm;
+    size_t part_p, part_c, wsplit, gid, psel, counts, probsum, cu, perm, table, base_rel, totals, pperm;
     size_t qp, kp, vp, op, plan;
     // STGA
     size_t shot_info, cu_tq, cu_tk, cu_f, q_idx, kv_idx, ot, of;
@@ -138,10 +138,11 @@ Layout make_layout(const moga_dims *d, const StgaGeom *g) {
     Carver c;
     const int64_t n = d->n_tokens;
     const int m = d->n_groups;
-    const int64_t nbr = route_blocks(n), nbp = permute_blocks(n);
+    const int64_t nbr = route_partials(n), nbp = permute_blocks(n);
     const size_t tensor = (size_t)d->n_heads * n * d->head_dim * sizeof(uint16_t);
     L.part_p = c.take(sizeof(double) * nbr * kMaxGroups);
     L.part_c = c.take(sizeof(int32_t) * nbr * kMaxGroups);
+    L.wsplit = c.take(route_split_bytes(d->d_model, m));
     L.gid = c.take(sizeof(int32_t) * n);
     L.psel = c.take(sizeof(float) * n);
     L.counts = c.take(sizeof(int32_t) * m);
@@ -211,7 +212,7 @@ moga_status run_route(const void *x, moga_dtype xt, const float *w, const int32_
     r.x = x; r.x_is_bf16 = xt == MOGA_BF16; r.w = w; r.pin = pin; r.n = d->n_tokens;
     r.d = d->d_model; r.m = d->n_groups; r.group_id = gid; r.p_sel = psel;
     r.part_p = at<double>(ws, L.part_p); r.part_c = at<int32_t>(ws, L.part_c);
-    r.counts = counts; r.prob_sum = prob_sum;
+    r.counts = counts; r.prob_sum = prob_sum; r.wsplit = at<void>(ws, L.wsplit);
     HIP_TRY(launch_route(r, s), "route launch");
     return MOGA_OK;
 }

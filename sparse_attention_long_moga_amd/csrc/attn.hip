@@ -675,6 +675,22 @@ int g_num_cus[64];  // per device
 
 }  // namespace
 
+hipError_t device_cus(int *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (g_num_cus[dev] == 0) {
+        int n = 0;
+        if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) !=
+            hipSuccess)
+            return e;
+        g_num_cus[dev] = n;
+    }
+    *out = g_num_cus[dev];
+    return hipSuccess;
+}
+
 int64_t attn_max_items(int n_heads, int64_t len_q, int32_t n_seg) {
     // sized for the smallest query tile any launch uses (128 rows)
     return (int64_t)n_heads * ((len_q + kAttnBQMin - 1) / kAttnBQMin + n_seg);
@@ -715,20 +731,12 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, s, a.plan,
                        a.n_seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    int dev = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (g_num_cus[dev] == 0) {
-        int n = 0;
-        if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) !=
-            hipSuccess)
-            return e;
-        g_num_cus[dev] = n;
-    }
+    int cus = 0;
+    if ((e = device_cus(&cus)) != hipSuccess) return e;
     // persistent grids: two waves per SIMD in every configuration
-    const dim3 grid((unsigned)(g_num_cus[dev] * (8 / waves))), blk((unsigned)(64 * waves));
-    const dim3 grid4((unsigned)(g_num_cus[dev] * 2)), blk4(256u);
-    const dim3 grid8((unsigned)g_num_cus[dev]), blk8(512u);
+    const dim3 grid((unsigned)(cus * (8 / waves))), blk((unsigned)(64 * waves));
+    const dim3 grid4((unsigned)(cus * 2)), blk4(256u);
+    const dim3 grid8((unsigned)cus), blk8(512u);
     if (direct) {
         if (indexed) {
             if (waves == 8) hipLaunchKernelGGL((attn_kernel_direct<8, true>), grid, blk, 0, s, a);

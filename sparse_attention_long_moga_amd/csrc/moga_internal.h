@@ -22,6 +22,9 @@ constexpr int kPlanSortMax = 4096; // segments sorted by key length up to this c
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int *n);
+
 // ---------------------------------------------------------------- router
 struct RouteLaunch {
     const void *x;
@@ -36,8 +39,11 @@ struct RouteLaunch {
     int32_t *part_c;  // [nblk][kMaxGroups]
     int32_t *counts;  // [m]
     double *prob_sum; // [m]
+    void *wsplit;     // route_split_bytes(d, m): W split into bf16 MFMA fragments (bf16 x)
 };
 int64_t route_blocks(int64_t n);
+int64_t route_partials(int64_t n);  // part_p / part_c hold route_partials(n) * kMaxGroups entries
+size_t route_split_bytes(int d, int m);  // wsplit: fragments plus a work-queue counter
 hipError_t launch_route(const RouteLaunch &a, hipStream_t s);
 
 // ---------------------------------------------------------------- permute

@@ -108,33 +108,46 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *gid, int64_
 // Row gather/scatter.  grid = (row blocks, heads, tensors); each thread moves 16 bytes.
 template <int HD>
 __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch a) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
     constexpr int CH = HD * 2 / 16;         // 16-byte chunks per row
     constexpr int ROWS = 256 / CH;          // rows per block pass
     constexpr int PASSES = 8;
     const int tensor = blockIdx.z, h = blockIdx.y;
-    const int64_t head_off = (int64_t)h * a.n * HD;
-    const bf16 *src = static_cast<const bf16 *>(a.src[tensor]) + head_off;
-    bf16 *dst = static_cast<bf16 *>(a.dst[tensor]) + head_off;
+    const int64_t n = a.n;
+    const int64_t head_off = (int64_t)h * n * HD;
+    // select by comparisons: indexing the by-value pointer arrays with a runtime value
+    // would place the whole argument struct in per-lane scratch memory
+    const void *sv = a.src[0];
+    void *dv = a.dst[0];
+    if (tensor == 1) { sv = a.src[1]; dv = a.dst[1]; }
+    if (tensor == 2) { sv = a.src[2]; dv = a.dst[2]; }
+    if (tensor == 3) { sv = a.src[3]; dv = a.dst[3]; }
+    const bf16 *src = static_cast<const bf16 *>(sv) + head_off;
+    bf16 *dst = static_cast<bf16 *>(dv) + head_off;
     const int r_in = threadIdx.x / CH, ch = threadIdx.x % CH;
-    const int64_t j0 = (int64_t)blockIdx.x * ROWS * PASSES;
-    uint4 buf[PASSES];
-    int64_t dst_row[PASSES];
+    const int64_t j0 = (int64_t)blockIdx.x * ROWS * PASSES + r_in;
+    // every load is unconditional (clamped indices), so all of them are in flight together;
+    // perm entries are range-checked, since with ids outside [0, m) part of perm is never
+    // written and stale workspace values must not become addresses
+    int32_t pj[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) pj[p] = a.perm[min(j0 + p * ROWS, n - 1)];
+    i32x4 buf[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-        const int64_t j = j0 + p * ROWS + r_in;
-        dst_row[p] = -1;
-        // perm entries are range-checked: with ids outside [0, m) part of perm is never
-        // written, and stale workspace values must not become addresses
-        const int64_t pj = j < a.n ? (int64_t)a.perm[j] : -1;
-        if (pj >= 0 && pj < a.n) {
-            const int64_t s_row = a.inverse ? j : pj;
-            dst_row[p] = a.inverse ? pj : j;
-            buf[p] = *reinterpret_cast<const uint4 *>(src + s_row * HD + ch * 8);
-        }
+        const int64_t j = j0 + p * ROWS;
+        const bool ok = j < n && pj[p] >= 0 && pj[p] < n;
+        const int64_t s_row = ok ? (a.inverse ? j : (int64_t)pj[p]) : 0;
+        buf[p] = *reinterpret_cast<const i32x4 *>(src + s_row * HD + ch * 8);
     }
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p)
-        if (dst_row[p] >= 0) *reinterpret_cast<uint4 *>(dst + dst_row[p] * HD + ch * 8) = buf[p];
+    for (int p = 0; p < PASSES; ++p) {
+        const int64_t j = j0 + p * ROWS;
+        if (j < n && pj[p] >= 0 && pj[p] < n) {
+            const int64_t d_row = a.inverse ? (int64_t)pj[p] : j;
+            *reinterpret_cast<i32x4 *>(dst + d_row * HD + ch * 8) = buf[p];
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void gather_scalar_kernel(const float *src, const int32_t *perm,

@@ -33,6 +33,7 @@ def _router_case(n, d, m, seed, x_dtype="bf16", dirichlet=None):
     (3001, 1536, 5, "bf16", 3),
     (2500, 512, 20, "bf16", 4),
     (700, 512, 64, "bf16", 5),       # W larger than the LDS budget: chunked over d
+    (1234, 200, 37, "bf16", 8),      # d not a multiple of 32: a partial last k-step
     (1, 64, 3, "bf16", 6),           # a single token
     (333, 128, 1, "f32", 7),         # one group: p == 1
 ])
