@@ -447,6 +447,21 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// max(v, value of the lane 32 apart): v_permlane32_swap exchanges the upper half of one
+// operand with the lower half of the other, so with both operands v each lane sees both
+__device__ __forceinline__ float max_across_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// acc + lo + hi of a packed pair of bf16 values (v_dot2 against (1, 1))
+__device__ __forceinline__ float sum_bf16x2(uint32_t packed, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+}
+
 // IDX: rows are read through the index maps (STGA groups, or the permutation itself for
 // the permute-free MoGA variant); each lane then fetches its chunk's row index first.
 template <int WAVES, bool IDX>
@@ -582,12 +597,20 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                         if (key >= klen) sacc[sb][v] = -INFINITY;
                     }
             }
-            float tmax = -INFINITY;
+            // row maximum: four max3 chains over 8 scores each, then across the two lane halves
+            // that hold the same query (a VALU lane swap, no LDS round trip)
+            float pm[4];
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int v = 0; v < 16; v += 2) tmax = fmaxf(tmax, fmaxf(sacc[sb][v], sacc[sb][v + 1]));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            for (int qd = 0; qd < 4; ++qd) {
+                const f32x16 &sv = sacc[qd >> 1];
+                const int v0 = 8 * (qd & 1);
+                float m = fmaxf(fmaxf(sv[v0], sv[v0 + 1]), sv[v0 + 2]);
+                m = fmaxf(fmaxf(m, sv[v0 + 3]), sv[v0 + 4]);
+                m = fmaxf(fmaxf(m, sv[v0 + 5]), sv[v0 + 6]);
+                pm[qd] = fmaxf(m, sv[v0 + 7]);
+            }
+            float tmax = fmaxf(fmaxf(fmaxf(pm[0], pm[1]), pm[2]), pm[3]);
+            tmax = max_across_halves(tmax);
             const bool up = tmax > m_run + thr;
             if (__ballot(up)) {
                 const float m_new = up ? tmax : m_run;
@@ -607,12 +630,16 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                 for (int half = 0; half < 2; ++half) {
                     float pv[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
+                    for (int e = 0; e < 8; ++e)
                         pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][half * 8 + e], c, -mc));
-                        l_run += pv[e];
-                    }
                     const uint4 packed = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                                                     pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+                    // the row sum adds the bf16 probabilities the MFMA multiplies V with,
+                    // two per dot2 instruction
+                    l_run = sum_bf16x2(packed.x, l_run);
+                    l_run = sum_bf16x2(packed.y, l_run);
+                    l_run = sum_bf16x2(packed.z, l_run);
+                    l_run = sum_bf16x2(packed.w, l_run);
                     pf[sb * 2 + half] = __builtin_bit_cast(bf16x8, packed);
                 }
 #pragma unroll
