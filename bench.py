@@ -27,9 +27,20 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 DEFAULT_WORKLOAD = "wan1.3b_30s_skewed_N282360_M5"
 METRIC = "MoGA fwd tokens/s + group-attn TFLOP/s (% bf16 MFMA peak) at N=282k, M=5"
 
-# HBM traffic calibration: bytes the FETCH_SIZE / WRITE_SIZE counters report per byte
-# actually moved, measured on a plain copy kernel (see profiles/).  None until measured.
-ATTN_TRAFFIC_BYTES = None
+# HBM bytes per launch of the attention kernel on the default workload: rocprofv3 FETCH_SIZE
+# and WRITE_SIZE (KiB per dispatch, one pass each), scaled by what the same counters read for a
+# plain 1 GiB device copy (FETCH 2.0x, WRITE 1.0x); the summary with the commands is under
+# profiles/.  The figure belongs to one version of the kernel source: any other attn.hip
+# reports null until the counters are taken again.
+ATTN_TRAFFIC = {"bytes": 10_363_380 * 1024 * 2 + 848_052 * 1024, "attn_hip_sha256_16": "262f963972321607"}
+
+
+def attn_traffic_bytes():
+    import hashlib
+    src = os.path.join(ROOT, "sparse_attention_long_moga_amd", "csrc", "attn.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    return ATTN_TRAFFIC["bytes"] if digest == ATTN_TRAFFIC["attn_hip_sha256_16"] else None
 
 
 def parse():
@@ -203,7 +214,7 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
     stages["roofline"] = {
         "bound": "mfma", "kernel": "attn_kernel_direct<8> (group_attn stage)",
         "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-        "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": ATTN_TRAFFIC_BYTES,
+        "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": attn_traffic_bytes(),
         "algorithmic_flops_per_launch": attn_flops,
         "launch_ms": ms["group_attn"],
     }
