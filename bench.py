@@ -53,6 +53,9 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-stages", action="store_true")
+    p.add_argument("--msweep", action="store_true",
+                   help="only run the group-count sweep (M = 1, 2, 4, 8, 16 at the 10 s shape) "
+                        "and print one JSON line per M")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates the HBM byte "
                         "counters against a known size) and exit")
@@ -90,6 +93,10 @@ def main():
     if not os.path.exists(os.path.join(ROOT, "sparse_attention_long_moga_amd", "libmoga.so")):
         from sparse_attention_long_moga_amd import build
         build.build()
+
+    if args.msweep:
+        msweep(args)
+        return
 
     wl = workloads.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
@@ -226,6 +233,85 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
         stages["stga_tflops"] = metrics.attention_flops(pt, h, hd) / (ms["stga"] / 1e3) / 1e12
     log(f"stages (ms): {ms}  attn {attn_tflops:.1f} TFLOP/s")
     return stages
+
+
+# The pages' group-count ablation for Wan2.1-1.3B at 10 s (papernotes.org MoGA note,
+# 消融实验表格): sparsity and whole-model forward PFLOPs per M.
+PAGES_MSWEEP = {1: (0.0, 0.88), 2: (0.4125, 0.59), 4: (0.6625, 0.42), 8: (0.7875, 0.36),
+                16: (0.8125, 0.35)}
+# Whole-model FLOPs in the pages' convention (their full-attention figures are reproduced by
+# it): 30 attention layers at 4*hd*H FLOPs per (query, key) pair plus 2 * 1.3e9 parameters per
+# token (Wan2.1-1.3B public sizes; the layer count and parameter count are not on the pages).
+WAN13B_LAYERS, WAN13B_PARAMS = 30, 1.3e9
+
+
+def msweep(args):
+    """Group-count sweep at the 10 s shape: for each M one JSON line with the routing's
+    sparsity (1 - sum n_i^2 / N^2), attention FLOPs, forward and attention-stage times."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from sparse_attention_long_moga_amd import api, metrics
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    for wl in workloads.MSWEEP:
+        n, h, hd, m = wl.n_tokens, wl.n_heads, wl.head_dim, wl.n_groups
+        log(f"msweep {wl.name}")
+        x, w = workloads.make_x(wl, dev), workloads.make_w(wl, dev)
+        q, k, v = workloads.make_qkv(wl, dev)
+        dims = api.make_dims(n, wl.d_model, h, hd, m, alpha=wl.alpha)
+        ws = api.workspace(api.moga_workspace_bytes(dims, None), dev)
+        out = dict(out=torch.empty_like(q), loss=torch.empty(1, dtype=torch.float64, device=dev),
+                   counts=torch.empty(m, dtype=torch.int32, device=dev))
+
+        def fwd():
+            api.moga_forward(x, w, q, k, v, m, alpha=wl.alpha, ws=ws, out=out)
+
+        r = api.moga_route(x, w, m, ws=ws)
+        cu, perm, (qp, kp, vp), pp = api.moga_permute(r["group_id"], [q, k, v], m,
+                                                      p_sel=r["p_sel"], ws=ws)
+        op = torch.empty_like(qp)
+
+        def attn():
+            api.moga_group_attn(qp, kp, vp, cu, cu, row_scale=pp, out=op, ws=ws)
+
+        res = {}
+        for name, fn in (("forward", fwd), ("attn", attn)):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / args.steps
+        counts = out["counts"].cpu().numpy().astype(np.int64)
+        pairs = metrics.moga_pairs(counts)
+        flops = metrics.attention_flops(pairs, h, hd)
+        full = metrics.attention_flops(float(n) ** 2, h, hd)
+        sparsity = 1.0 - pairs / float(n) ** 2
+        model_pf = (WAN13B_LAYERS * flops + 2.0 * WAN13B_PARAMS * n) / 1e15
+        page_sp, page_pf = PAGES_MSWEEP[m]
+        line = {
+            "mode": "msweep", "workload": wl.name, "n_tokens": n, "n_groups": m,
+            "group_sizes": counts.tolist(), "sparsity": sparsity,
+            "attn_tflop_per_layer": flops / 1e12, "full_attn_tflop_per_layer": full / 1e12,
+            "model_pflops_estimate": model_pf,
+            "pages": {"sparsity": page_sp, "pflops": page_pf},
+            "steps": args.steps, "warmup": args.warmup,
+            "forward_ms": res["forward"], "tokens_per_s": n / (res["forward"] / 1e3),
+            "attn_ms": res["attn"], "attn_tflops": flops / (res["attn"] / 1e3) / 1e12,
+            "attn_frac_of_bf16_peak": flops / (res["attn"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "dtype": "bf16", "data": "synthetic",
+        }
+        print(json.dumps(line), flush=True)
+        del x, w, q, k, v, ws, out, r, cu, perm, qp, kp, vp, pp, op
+        torch.cuda.empty_cache()
 
 
 def stga_pairs_closed_form(g):

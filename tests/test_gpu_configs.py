@@ -1,5 +1,6 @@
-"""Parity at the full sizes of the five workloads, in the launch configuration the benchmark
-times (one moga_forward call through the C ABI).
+"""Parity at the full sizes of the five workloads and of the group-count sweep (M = 1..16 at the
+10 s shape), in the launch configuration the benchmark times (one moga_forward call through the
+C ABI).
 
 Routing, cu_seqlens, perm, counts (F_i), P_i and the loss are compared on every token.
 Attention outputs are compared on seeded samples of output rows, which the oracle computes
@@ -38,7 +39,10 @@ def _sample_rows(wl, group_id, heads, per_group, seed):
     return rows_h, rows_t
 
 
-@pytest.mark.parametrize("wl", workloads.CONFIGS, ids=[w.name for w in workloads.CONFIGS])
+ALL = workloads.CONFIGS + workloads.MSWEEP
+
+
+@pytest.mark.parametrize("wl", ALL, ids=[w.name for w in ALL])
 def test_full_size_forward(wl):
     print(f"[case] full-size forward {wl.name}", flush=True)
     x, w = workloads.make_x(wl, DEV), workloads.make_w(wl, DEV)

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import workloads
 from oracle import bruteforce as bf
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -320,3 +321,14 @@ def test_flop_convention_reproduces_printed_pflops():
         per_layer = attention_flops(n * n, heads, hd)
         total = model["layers"] * per_layer + 2 * n * model["params"]
         assert abs(total / 1e15 - case["pflops_printed"]) < 0.006 * case["pflops_printed"]
+
+
+def test_group_count_sweep_shapes():
+    """The sweep follows the pages' M ablation: Wan2.1-1.3B widths at 10 s (40 latent frames of
+    1560 tokens), M in {1, 2, 4, 8, 16} (papernotes.org MoGA note, 消融实验表格)."""
+    assert workloads.MSWEEP_M == (1, 2, 4, 8, 16)
+    for wl, m in zip(workloads.MSWEEP, workloads.MSWEEP_M):
+        assert (wl.n_tokens, wl.d_model, wl.n_heads, wl.head_dim, wl.n_groups) == (
+            40 * 1560, 1536, 12, 128, m)
+        assert not wl.hybrid and wl.dirichlet is None
+    assert len({wl.seed for wl in workloads.MSWEEP}) == len(workloads.MSWEEP)

@@ -96,7 +96,15 @@ MMDIT60S = Workload("mmdit_60s_N563160_M20_stga", 361 * TOKENS_PER_FRAME, 5120, 
                     win_h=15, win_w=13, t_group=4, aug_frames=2)
 
 CONFIGS: List[Workload] = [TINY, WAN5S, WAN30S_SKEW, WAN30S_HYBRID, MMDIT60S]
-BY_NAME = {w.name: w for w in CONFIGS}
+
+# Group-count sweep at the 10 s shape (40 latent frames, N = 62,400) of the pages' M ablation
+# (papernotes.org MoGA note, 消融实验表格): MoGA only, uniform mixture, one seed per M.
+MSWEEP_M = (1, 2, 4, 8, 16)
+MSWEEP: List[Workload] = [
+    Workload(f"wan1.3b_10s_N62400_M{m}", 40 * TOKENS_PER_FRAME, 1536, 12, 128, m, seed=100 + m)
+    for m in MSWEEP_M]
+
+BY_NAME = {w.name: w for w in CONFIGS + MSWEEP}
 
 
 def small(name: str, n_tokens: int, d_model: int, n_heads: int, head_dim: int, n_groups: int,
