@@ -75,6 +75,13 @@ def _load():
     lib.oracle_varlen_attn.argtypes = [_f32p, _f32p, _f32p, c_i64, c_i64, c_int, c_int, _i64p,
                                        _i64p, vp, c_dbl, c_i64, _i32p, _i64p, _f64p]
     lib.oracle_varlen_attn.restype = c_i64
+    lib.oracle_moga_backward.argtypes = [_f32p, _f32p, c_i64, c_int, c_int, c_int, c_int, _f32p,
+                                         _f32p, _f32p, _i32p, _f32p, c_dbl, c_dbl, c_dbl, _f64p,
+                                         _f64p, _f64p, _f64p, _f64p, _f64p, _f64p]
+    lib.oracle_moga_backward.restype = c_int
+    lib.oracle_moga_dq_rows.argtypes = [_f32p, _f32p, _f32p, _f32p, c_i64, c_int, _i32p, c_int,
+                                        _f64p, c_dbl, c_i64, _i32p, _i64p, _f64p, _f64p, _f64p]
+    lib.oracle_moga_dq_rows.restype = c_int
     _lib = lib
     return lib
 
@@ -174,6 +181,43 @@ def moga_attn(q, k, v, group_id, m: int, p_sel, scale: float, rows_h, rows_t):
     if pairs < 0:
         raise ValueError("oracle_moga_attn failed")
     return out, int(pairs)
+
+
+def moga_backward(x, w, q, k, v, group_id, d_out, d_loss: float, alpha: float,
+                  scale: float) -> dict:
+    """Gradients of the MoGA forward (papernotes.org MoGA note, 关键设计 1 and 3) with the
+    routing held fixed: given d_out for out = p(g|x) * SA(q, K_g, V_g) and d_loss for L_gb,
+    returns dq, dk, dv ([H][N][hd]), dx ([N][d]), dw ([d][M]), dp ([N], gradient with respect
+    to p(g_t|x_t) from the attention output) and lse ([H][N]) in fp64."""
+    x, w = _f32(x), _f32(w)
+    q, k, v, go = _f32(q), _f32(k), _f32(v), _f32(d_out)
+    h, n, hd = q.shape
+    d, m = w.shape
+    g = np.ascontiguousarray(group_id, dtype=np.int32)
+    out = dict(dq=np.empty((h, n, hd)), dk=np.empty((h, n, hd)), dv=np.empty((h, n, hd)),
+               dx=np.empty((n, d)), dw=np.empty((d, m)), dp=np.empty(n), lse=np.empty((h, n)))
+    rc = _load().oracle_moga_backward(x, w, n, d, m, h, hd, q, k, v, g, go, float(d_loss),
+                                      float(alpha), float(scale), out["dq"], out["dk"],
+                                      out["dv"], out["dx"], out["dw"], out["dp"], out["lse"])
+    if rc != 0:
+        raise ValueError(f"oracle_moga_backward failed ({rc})")
+    return out
+
+
+def moga_dq_rows(q, k, v, d_out, group_id, m: int, p_sel, scale: float, rows_h, rows_t):
+    """dq, D = <dO', O'> and lse of selected (head, token) rows, same definitions as
+    moga_backward.  Returns (dq [rows][hd], D [rows], lse [rows])."""
+    q, k, v, go = _f32(q), _f32(k), _f32(v), _f32(d_out)
+    _, n, hd = q.shape
+    g = np.ascontiguousarray(group_id, dtype=np.int32)
+    ps = np.ascontiguousarray(p_sel, dtype=np.float64)
+    rh, rt = _rows(rows_h, rows_t)
+    dq, D, lse = np.empty((rh.shape[0], hd)), np.empty(rh.shape[0]), np.empty(rh.shape[0])
+    rc = _load().oracle_moga_dq_rows(q, k, v, go, n, hd, g, m, ps, float(scale), rh.shape[0],
+                                     rh, rt, dq, D, lse)
+    if rc != 0:
+        raise ValueError(f"oracle_moga_dq_rows failed ({rc})")
+    return dq, D, lse
 
 
 def varlen_attn(q, k, v, cu_q, cu_k, scale: float, rows_h, rows_i, row_scale=None):

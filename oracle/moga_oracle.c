@@ -349,3 +349,213 @@ int64_t oracle_varlen_attn(const float *q, const float *k, const float *v, int64
     }
     return pairs;
 }
+
+/* ========================================================================= */
+/* Backward of the MoGA forward ([N] key design 1: the router is made          */
+/* differentiable through the p(g(x)|x) factor; key design 3: L_gb).           */
+/*                                                                             */
+/* With the routing g held fixed (the argmax and the counts n_i, hence F_i,    */
+/* are piecewise constant in x), for upstream gradients d_out of              */
+/* out_t = p_t * O'_t (p_t = p(g_t|x_t), O'_t = SA(q_t, K_G, V_G), per head)   */
+/* and d_loss of L_gb:                                                         */
+/*   dO'_t = p_t d_out_t;  P_tu = softmax_u(scale <q_t,k_u>) over u in G(t)    */
+/*   D_t = <dO'_t, O'_t>;  dP_tu = <dO'_t, v_u>;  dS_tu = P_tu (dP_tu - D_t)   */
+/*   dq_t = scale sum_u dS_tu k_u;  dk_u = scale sum_t dS_tu q_t;              */
+/*   dv_u = sum_t P_tu dO'_t                                                   */
+/*   dp_t = sum_heads <d_out_t, O'_t>                                          */
+/*   a_ti = [i = g_t] dp_t + d_loss * alpha * M * F_i / n                      */
+/*          (dL_gb / dp(i|x_t), since P_i = (1/n) sum_t p(i|x_t))              */
+/*   dr_ti = p_ti (a_ti - sum_j a_tj p_tj)   (softmax backward)                */
+/*   dW = x^T dr;  dx = dr W^T                                                 */
+/* lse_t = log sum_u exp(scale <q_t,k_u>) per head (the softmax normaliser).   */
+/* All of q, k, v, d_out hold n_heads heads of [n][hd].  Plain loops, fp64.    */
+/* ========================================================================= */
+static void group_members(const int32_t *group_id, int64_t n, int m, int64_t *cnt,
+                          int64_t *members)
+{
+    int64_t j = 0;
+    for (int i = 0; i < m; ++i) {
+        cnt[i] = j;
+        for (int64_t t = 0; t < n; ++t)
+            if (group_id[t] == i) members[j++] = t;
+    }
+    cnt[m] = j;
+}
+
+/* router probabilities p [n][m] in fp64 */
+static void router_probs(const float *x, const float *w, int64_t n, int d, int m, double *p)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double *pt = p + t * m;
+        double mx = -INFINITY;
+        for (int i = 0; i < m; ++i) {
+            double r = 0.0;
+            for (int c = 0; c < d; ++c) r += (double)x[t * d + c] * (double)w[(int64_t)c * m + i];
+            pt[i] = r;
+            if (r > mx) mx = r;
+        }
+        double z = 0.0;
+        for (int i = 0; i < m; ++i) { pt[i] = exp(pt[i] - mx); z += pt[i]; }
+        for (int i = 0; i < m; ++i) pt[i] /= z;
+    }
+}
+
+/* scores, probabilities and O' of one query row against a key list; returns lse */
+static double softmax_row(const float *qrow, const float *kh, const float *vh, int hd,
+                          const int64_t *keys, int64_t nk, double scale, double *P, double *o)
+{
+    double smax = -INFINITY;
+    for (int64_t a = 0; a < nk; ++a) {
+        const float *kr = kh + keys[a] * (int64_t)hd;
+        double acc = 0.0;
+        for (int c = 0; c < hd; ++c) acc += (double)qrow[c] * (double)kr[c];
+        P[a] = scale * acc;
+        if (P[a] > smax) smax = P[a];
+    }
+    double z = 0.0;
+    for (int64_t a = 0; a < nk; ++a) { P[a] = exp(P[a] - smax); z += P[a]; }
+    for (int c = 0; c < hd; ++c) o[c] = 0.0;
+    for (int64_t a = 0; a < nk; ++a) {
+        P[a] /= z;
+        const float *vr = vh + keys[a] * (int64_t)hd;
+        for (int c = 0; c < hd; ++c) o[c] += P[a] * (double)vr[c];
+    }
+    return smax + log(z);
+}
+
+int oracle_moga_backward(const float *x, const float *w, int64_t n, int d, int m, int n_heads,
+                         int hd, const float *q, const float *k, const float *v,
+                         const int32_t *group_id, const float *d_out, double d_loss,
+                         double alpha, double scale, double *dq, double *dk, double *dv,
+                         double *dx, double *dw, double *dp, double *lse)
+{
+    if (n < 1 || d < 1 || m < 1 || n_heads < 1 || hd < 1) return -1;
+    for (int64_t t = 0; t < n; ++t)
+        if (group_id[t] < 0 || group_id[t] >= m) return -3;
+    int64_t *cnt = (int64_t *)calloc((size_t)m + 1, sizeof(int64_t));
+    int64_t *members = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    double *p = (double *)malloc(sizeof(double) * (size_t)n * m);
+    double *dpart = (double *)calloc((size_t)n * n_heads, sizeof(double)); /* <d_out, O'> per head */
+    if (!cnt || !members || !p || !dpart) { free(cnt); free(members); free(p); free(dpart); return -2; }
+    group_members(group_id, n, m, cnt, members);
+    router_probs(x, w, n, d, m, p);
+    const size_t E = (size_t)n_heads * n * hd;
+    memset(dq, 0, sizeof(double) * E);
+    memset(dk, 0, sizeof(double) * E);
+    memset(dv, 0, sizeof(double) * E);
+
+    /* attention part: one (head, group) at a time; a group's rows only touch its own keys */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t hg = 0; hg < (int64_t)n_heads * m; ++hg) {
+        const int h = (int)(hg / m), g = (int)(hg % m);
+        const int64_t nk = cnt[g + 1] - cnt[g];
+        if (nk == 0) continue;
+        const int64_t *keys = members + cnt[g];
+        const int64_t hoff = (int64_t)h * n * hd;
+        const float *qh = q + hoff, *kh = k + hoff, *vh = v + hoff, *gh = d_out + hoff;
+        double *P = (double *)malloc(sizeof(double) * (size_t)nk);
+        double *o = (double *)malloc(sizeof(double) * (size_t)hd);
+        double *dO = (double *)malloc(sizeof(double) * (size_t)hd);
+        for (int64_t a = 0; a < nk; ++a) {
+            const int64_t t = keys[a];
+            double l = softmax_row(qh + t * hd, kh, vh, hd, keys, nk, scale, P, o);
+            if (lse) lse[(int64_t)h * n + t] = l;
+            const double pt = p[t * m + g];
+            double Dt = 0.0, part = 0.0;
+            for (int c = 0; c < hd; ++c) {
+                dO[c] = pt * (double)gh[t * hd + c];
+                Dt += dO[c] * o[c];
+                part += (double)gh[t * hd + c] * o[c];
+            }
+            dpart[t * n_heads + h] = part;
+            for (int64_t b = 0; b < nk; ++b) {
+                const int64_t u = keys[b];
+                double dP = 0.0;
+                for (int c = 0; c < hd; ++c) dP += dO[c] * (double)vh[u * hd + c];
+                const double dS = P[b] * (dP - Dt);
+                for (int c = 0; c < hd; ++c) {
+                    dq[hoff + t * hd + c] += scale * dS * (double)kh[u * hd + c];
+                    dk[hoff + u * hd + c] += scale * dS * (double)qh[t * hd + c];
+                    dv[hoff + u * hd + c] += P[b] * dO[c];
+                }
+            }
+        }
+        free(P); free(o); free(dO);
+    }
+
+    /* router part */
+    double *F = (double *)malloc(sizeof(double) * (size_t)m);
+    double *dr = (double *)malloc(sizeof(double) * (size_t)n * m);
+    for (int i = 0; i < m; ++i) F[i] = (double)(cnt[i + 1] - cnt[i]) / (double)n;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double dpt = 0.0;
+        for (int h = 0; h < n_heads; ++h) dpt += dpart[t * n_heads + h];
+        if (dp) dp[t] = dpt;
+        double a[256], dot = 0.0;
+        for (int i = 0; i < m; ++i) {
+            a[i] = (i == group_id[t] ? dpt : 0.0) + d_loss * alpha * (double)m * F[i] / (double)n;
+            dot += a[i] * p[t * m + i];
+        }
+        for (int i = 0; i < m; ++i) dr[t * m + i] = p[t * m + i] * (a[i] - dot);
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int i = 0; i < m; ++i) acc += dr[t * m + i] * (double)w[(int64_t)c * m + i];
+            dx[t * d + c] = acc;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < d; ++c)
+        for (int i = 0; i < m; ++i) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < n; ++t) acc += (double)x[t * d + c] * dr[t * m + i];
+            dw[(int64_t)c * m + i] = acc;
+        }
+    free(F); free(dr); free(cnt); free(members); free(p); free(dpart);
+    return 0;
+}
+
+/* dq (and D, lse) of selected rows only: row r is head rows_h[r] (an index into the heads of
+ * q/k/v/d_out), token rows_t[r].  p_sel[t] = p(g_t|x_t).  Same definitions as above. */
+int oracle_moga_dq_rows(const float *q, const float *k, const float *v, const float *d_out,
+                        int64_t n, int hd, const int32_t *group_id, int m, const double *p_sel,
+                        double scale, int64_t n_rows, const int32_t *rows_h,
+                        const int64_t *rows_t, double *dq, double *D, double *lse)
+{
+    if (n < 1 || hd < 1 || m < 1) return -1;
+    int64_t *cnt = (int64_t *)calloc((size_t)m + 1, sizeof(int64_t));
+    int64_t *members = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    if (!cnt || !members) { free(cnt); free(members); return -2; }
+    group_members(group_id, n, m, cnt, members);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t t = rows_t[r];
+        const int g = group_id[t];
+        const int64_t nk = cnt[g + 1] - cnt[g];
+        const int64_t *keys = members + cnt[g];
+        const int64_t hoff = (int64_t)rows_h[r] * n * hd;
+        double *P = (double *)malloc(sizeof(double) * (size_t)nk);
+        double *o = (double *)malloc(sizeof(double) * (size_t)hd);
+        double *dO = (double *)malloc(sizeof(double) * (size_t)hd);
+        double l = softmax_row(q + hoff + t * hd, k + hoff, v + hoff, hd, keys, nk, scale, P, o);
+        double Dt = 0.0;
+        for (int c = 0; c < hd; ++c) {
+            dO[c] = p_sel[t] * (double)d_out[hoff + t * hd + c];
+            Dt += dO[c] * o[c];
+        }
+        for (int c = 0; c < hd; ++c) dq[r * hd + c] = 0.0;
+        for (int64_t b = 0; b < nk; ++b) {
+            const int64_t u = keys[b];
+            double dP = 0.0;
+            for (int c = 0; c < hd; ++c) dP += dO[c] * (double)v[hoff + u * hd + c];
+            const double dS = P[b] * (dP - Dt);
+            for (int c = 0; c < hd; ++c) dq[r * hd + c] += scale * dS * (double)k[hoff + u * hd + c];
+        }
+        if (D) D[r] = Dt;
+        if (lse) lse[r] = l;
+        free(P); free(o); free(dO);
+    }
+    free(cnt); free(members);
+    return 0;
+}

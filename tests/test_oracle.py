@@ -332,3 +332,125 @@ def test_group_count_sweep_shapes():
             40 * 1560, 1536, 12, 128, m)
         assert not wl.hybrid and wl.dirichlet is None
     assert len({wl.seed for wl in workloads.MSWEEP}) == len(workloads.MSWEEP)
+
+
+# ------------------------------------------------------------------ backward (NEXT-2)
+# Gradients of out = p(g|x) * SA(q, K_g, V_g) and of L_gb with the routing held fixed
+# (papernotes.org MoGA note, 关键设计 1: the router is trained through the p factor; 关键设计 3).
+def _bwd_case(n=48, d=12, m=3, h=2, hd=8, seed=31):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    w = (rng.standard_normal((d, m)) / np.sqrt(d)).astype(np.float32)
+    q, k, v, go = (rng.standard_normal((h, n, hd)).astype(np.float32) for _ in range(4))
+    return x, w, q, k, v, go
+
+
+def _bwd_loss_bruteforce(x, w, q, k, v, go, g_fixed, d_loss, alpha, scale):
+    """Scalar <d_out, out> + d_loss * L_gb from the dense NumPy forward, routing fixed."""
+    _, p, _ = bf.router(x, w)
+    n, m = p.shape
+    p_sel = p[np.arange(n), g_fixed]
+    mm = bf.moga_mask(g_fixed)
+    out = np.stack([p_sel[:, None] * bf.masked_attention(q[i], k[i], v[i], mm, scale)
+                    for i in range(q.shape[0])])
+    F = np.bincount(g_fixed, minlength=m) / n
+    return float((np.asarray(go, np.float64) * out).sum() + d_loss * alpha * m * (F * p.mean(0)).sum())
+
+
+def test_backward_matches_autograd():
+    """The hand-written gradients equal torch autograd of a dense fp64 formulation."""
+    x, w, q, k, v, go = _bwd_case()
+    n, m = x.shape[0], w.shape[1]
+    scale, alpha, d_loss = 0.35, 0.1, 0.7
+    g = bf.router(x, w)[2]
+    leaf = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    X, W, Q, K, V = leaf(x), leaf(w), leaf(q), leaf(k), leaf(v)
+    p = torch.softmax(X @ W, dim=1)
+    gi = torch.from_numpy(g.astype(np.int64))
+    p_sel = p[torch.arange(n), gi]
+    mask = gi[:, None] == gi[None, :]
+    s = (scale * Q @ K.transpose(1, 2)).masked_fill(~mask, float("-inf"))
+    out = p_sel[None, :, None] * (torch.softmax(s, dim=-1) @ V)
+    F = torch.bincount(gi, minlength=m).double() / n
+    L = (torch.from_numpy(go.astype(np.float64)) * out).sum() + \
+        d_loss * alpha * m * (F * p.mean(0)).sum()
+    grads = torch.autograd.grad(L, [X, W, Q, K, V])
+    ref = oracle.moga_backward(x, w, q, k, v, g, go, d_loss, alpha, scale)
+    for name, gr in zip(["dx", "dw", "dq", "dk", "dv"], grads):
+        np.testing.assert_allclose(ref[name], gr.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_backward_finite_differences():
+    """Central differences of the brute-force forward at random coordinates."""
+    x, w, q, k, v, go = _bwd_case(n=30, seed=32)
+    scale, alpha, d_loss = 0.4, 0.1, 1.3
+    g = bf.router(x, w)[2]
+    ref = oracle.moga_backward(x, w, q, k, v, g, go, d_loss, alpha, scale)
+    base = {n: np.asarray(a, np.float64) for n, a in zip("xwqkv", (x, w, q, k, v))}
+    rng = np.random.Generator(np.random.PCG64(33))
+    eps = 1e-6
+    for name, gname in zip("xwqkv", ["dx", "dw", "dq", "dk", "dv"]):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, s)) for s in base[name].shape)
+            val = []
+            for sgn in (+1, -1):
+                a = dict(base)
+                a[name] = base[name].copy()
+                a[name][idx] += sgn * eps
+                assert np.array_equal(bf.router(a["x"], a["w"])[2], g)  # routing unchanged
+                val.append(_bwd_loss_bruteforce(a["x"], a["w"], a["q"], a["k"], a["v"], go, g,
+                                                d_loss, alpha, scale))
+            fd = (val[0] - val[1]) / (2 * eps)
+            assert abs(fd - ref[gname][idx]) < 1e-6 * max(1.0, abs(fd)), (gname, idx, fd)
+
+
+def test_backward_group_sums():
+    """sum over a group of dv = sum of p * d_out over it (softmax rows sum to one), and the
+    sum of dk over a group vanishes (each row of dS sums to zero)."""
+    x, w, q, k, v, go = _bwd_case(n=200, d=16, m=5, h=2, hd=16, seed=34)
+    g = bf.router(x, w)[2]
+    ref = oracle.moga_backward(x, w, q, k, v, g, go, 0.0, 0.1, 0.25)
+    _, p, _ = bf.router(x, w)
+    p_sel = p[np.arange(len(g)), g]
+    for h in range(2):
+        for grp in np.unique(g):
+            mem = g == grp
+            np.testing.assert_allclose(ref["dv"][h][mem].sum(0),
+                                       (p_sel[mem, None] * go[h][mem]).sum(0), atol=1e-11)
+            np.testing.assert_allclose(ref["dk"][h][mem].sum(0), 0.0, atol=1e-11)
+
+
+def test_backward_single_group_router_is_flat():
+    """M = 1: p is identically 1, so x and W get no gradient from either term."""
+    x, w, q, k, v, go = _bwd_case(m=1, seed=35)
+    ref = oracle.moga_backward(x, w, q, k, v, np.zeros(x.shape[0], np.int32), go, 2.0, 0.1, 0.3)
+    assert np.all(ref["dx"] == 0.0) and np.all(ref["dw"] == 0.0)
+
+
+def test_backward_balance_loss_only():
+    """d_out = 0: only L_gb acts; dL/dr_t = p_t * (c - <c, p_t>) with c_i = alpha M F_i / N."""
+    x, w, q, k, v, go = _bwd_case(n=60, m=4, seed=36)
+    g = bf.router(x, w)[2]
+    zero = np.zeros_like(go)
+    ref = oracle.moga_backward(x, w, q, k, v, g, zero, 1.0, 0.1, 0.3)
+    for name in ("dq", "dk", "dv"):
+        assert np.all(ref[name] == 0.0)
+    _, p, _ = bf.router(x, w)
+    n, m = p.shape
+    c = 0.1 * m * np.bincount(g, minlength=m) / n / n
+    dr = p * (c[None, :] - (p * c[None, :]).sum(1, keepdims=True))
+    np.testing.assert_allclose(ref["dw"], x.astype(np.float64).T @ dr, rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(ref["dx"], dr @ w.astype(np.float64).T, rtol=1e-10, atol=1e-14)
+
+
+def test_backward_dq_rows_match_full():
+    x, w, q, k, v, go = _bwd_case(n=80, m=3, seed=37)
+    g = bf.router(x, w)[2]
+    _, p, _ = bf.router(x, w)
+    p_sel = p[np.arange(len(g)), g]
+    ref = oracle.moga_backward(x, w, q, k, v, g, go, 0.5, 0.1, 0.3)
+    rows_h = np.array([0, 1, 1, 0], np.int32)
+    rows_t = np.array([0, 5, 79, 40], np.int64)
+    dq, D, lse = oracle.moga_dq_rows(q, k, v, go, g, 3, p_sel, 0.3, rows_h, rows_t)
+    np.testing.assert_allclose(dq, ref["dq"][rows_h, rows_t], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, ref["lse"][rows_h, rows_t], rtol=1e-12)
