@@ -104,6 +104,10 @@ typedef struct {
     int32_t *perm;        /* optional [N]: grouped row -> token */
     int32_t *counts;      /* optional [M] */
     double *prob_sum;     /* optional [M]: sum over tokens of p(i|x) */
+    float *lse;           /* optional [H][N] fp32, token order: natural log of the softmax
+                             normaliser of the token's MoGA attention row,
+                             log sum_u exp(scale q.k_u) over its group's keys; the state
+                             moga_backward needs besides out */
 } moga_outputs;
 
 const char *moga_last_error(void);
@@ -189,6 +193,49 @@ moga_status moga_forward(const moga_inputs *in, const moga_dims *dims, const stg
 moga_status moga_forward_fused(const moga_inputs *in, const moga_dims *dims,
                                const stga_layout *stga, const moga_outputs *out, void *ws,
                                size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ backward
+ * Gradients of the MoGA forward (design 1: the router learns through the factor
+ * p(g(x)|x) of the output; design 3: L_gb), with the routing held fixed: g(x), the
+ * counts and the permutation are piecewise constant in x and W, so only p(g|x), the
+ * attention and P_i carry gradient.  Given G = d objective / d out and d_loss =
+ * d objective / d L_gb:
+ *   D[h][t]  = <G[h][t], out[h][t]>,  dp_t = sum_h D[h][t] / p_t  (gradient w.r.t. p(g_t|x_t))
+ *   attention backward of each group with dO' = p_t G (dQ, dK, dV; softmax recomputed from lse)
+ *   a_ti = [i = g_t] dp_t + d_loss alpha M F_i / N,  dr_t = p_t (a_t - <a_t, p_t>)  (p_t: all M
+ *   probabilities, recomputed from x W in fp32),  dx = dr W^T,  dW = x^T dr.
+ * MoGA only: the STGA branches have no backward here. */
+
+/* What moga_backward reads from the forward; all DEVICE, as written by moga_forward or
+ * moga_forward_fused called with stga NULL on the same inputs. */
+typedef struct {
+    const int32_t *group_id;   /* [N] */
+    const float *p_sel;        /* [N] */
+    const int32_t *counts;     /* [M] */
+    const int32_t *cu_seqlens; /* [M+1] */
+    const int32_t *perm;       /* [N] */
+    const void *out;           /* bf16 [H][N][head_dim], token order */
+    const float *lse;          /* [H][N], token order */
+} moga_saved;
+
+typedef struct {
+    void *dq, *dk, *dv;  /* required, bf16 [H][N][head_dim], token order */
+    float *dx;           /* optional [N][d_model] fp32 (for bf16 x too) */
+    float *dw;           /* optional [d_model][M] fp32 */
+    float *dp;           /* optional [N] fp32: dp_t above */
+} moga_grads;
+
+/* Workspace bytes needed by moga_backward (0 if the sizes are invalid). */
+size_t moga_backward_workspace_bytes(const moga_dims *dims);
+
+/* The backward above.  in: the forward's x, x_dtype, w, q, k, v (pin is not read: the
+ * saved group_id already holds it).  d_out: bf16 [H][N][head_dim], token order.  Needs
+ * head_dim 128.  dq, dk, dv, dx, dw, dp are fully overwritten.  dQ and dK/dV are computed by
+ * two kernels so that every output row has one writer (no atomics), and all sums run in a
+ * fixed order.  ws: moga_backward_workspace_bytes(dims). */
+moga_status moga_backward(const moga_inputs *in, const moga_saved *saved, const void *d_out,
+                          double d_loss, const moga_dims *dims, const moga_grads *grads,
+                          void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

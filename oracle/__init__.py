@@ -82,6 +82,9 @@ def _load():
     lib.oracle_moga_dq_rows.argtypes = [_f32p, _f32p, _f32p, _f32p, c_i64, c_int, _i32p, c_int,
                                         _f64p, c_dbl, c_i64, _i32p, _i64p, _f64p, _f64p, _f64p]
     lib.oracle_moga_dq_rows.restype = c_int
+    lib.oracle_router_bwd_rows.argtypes = [_f32p, _f32p, c_i64, c_int, c_int, _i32p, _f64p,
+                                           _i64p, c_i64, c_dbl, c_dbl, _f64p, _f64p]
+    lib.oracle_router_bwd_rows.restype = c_int
     _lib = lib
     return lib
 
@@ -218,6 +221,24 @@ def moga_dq_rows(q, k, v, d_out, group_id, m: int, p_sel, scale: float, rows_h, 
     if rc != 0:
         raise ValueError(f"oracle_moga_dq_rows failed ({rc})")
     return dq, D, lse
+
+
+def router_backward_rows(x_rows, w, group_rows, dp_rows, counts, n: int, d_loss: float,
+                         alpha: float):
+    """Router part of moga_backward for selected tokens: given their x rows, groups and
+    dp_t, and the whole problem's counts and N, returns (dr [rows][M], dx [rows][d])."""
+    x, w = _f32(x_rows), _f32(w)
+    r, d = x.shape
+    m = w.shape[1]
+    g = np.ascontiguousarray(group_rows, dtype=np.int32)
+    dp = np.ascontiguousarray(dp_rows, dtype=np.float64)
+    c = np.ascontiguousarray(counts, dtype=np.int64)
+    dr, dx = np.empty((r, m)), np.empty((r, d))
+    rc = _load().oracle_router_bwd_rows(x, w, r, d, m, g, dp, c, int(n), float(d_loss),
+                                        float(alpha), dr, dx)
+    if rc != 0:
+        raise ValueError(f"oracle_router_bwd_rows failed ({rc})")
+    return dr, dx
 
 
 def varlen_attn(q, k, v, cu_q, cu_k, scale: float, rows_h, rows_i, row_scale=None):

@@ -401,6 +401,25 @@ static void router_probs(const float *x, const float *w, int64_t n, int d, int m
     }
 }
 
+/* router part for one token: a_ti, then dr_t (softmax backward) and dx_t = dr_t W^T, from its
+ * probabilities p_t [m] over all groups, its group g, dp_t and F [m] */
+static void router_bwd_token(const double *pt, int g, double dpt, const double *F, int m, int d,
+                             const float *w, int64_t n, double d_loss, double alpha,
+                             double *dr_t, double *dx_t)
+{
+    double a[256], dot = 0.0;
+    for (int i = 0; i < m; ++i) {
+        a[i] = (i == g ? dpt : 0.0) + d_loss * alpha * (double)m * F[i] / (double)n;
+        dot += a[i] * pt[i];
+    }
+    for (int i = 0; i < m; ++i) dr_t[i] = pt[i] * (a[i] - dot);
+    for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int i = 0; i < m; ++i) acc += dr_t[i] * (double)w[(int64_t)c * m + i];
+        dx_t[c] = acc;
+    }
+}
+
 /* scores, probabilities and O' of one query row against a key list; returns lse */
 static double softmax_row(const float *qrow, const float *kh, const float *vh, int hd,
                           const int64_t *keys, int64_t nk, double scale, double *P, double *o)
@@ -493,17 +512,8 @@ int oracle_moga_backward(const float *x, const float *w, int64_t n, int d, int m
         double dpt = 0.0;
         for (int h = 0; h < n_heads; ++h) dpt += dpart[t * n_heads + h];
         if (dp) dp[t] = dpt;
-        double a[256], dot = 0.0;
-        for (int i = 0; i < m; ++i) {
-            a[i] = (i == group_id[t] ? dpt : 0.0) + d_loss * alpha * (double)m * F[i] / (double)n;
-            dot += a[i] * p[t * m + i];
-        }
-        for (int i = 0; i < m; ++i) dr[t * m + i] = p[t * m + i] * (a[i] - dot);
-        for (int c = 0; c < d; ++c) {
-            double acc = 0.0;
-            for (int i = 0; i < m; ++i) acc += dr[t * m + i] * (double)w[(int64_t)c * m + i];
-            dx[t * d + c] = acc;
-        }
+        router_bwd_token(p + t * m, group_id[t], dpt, F, m, d, w, n, d_loss, alpha, dr + t * m,
+                         dx + t * d);
     }
 #pragma omp parallel for schedule(static)
     for (int c = 0; c < d; ++c)
@@ -557,5 +567,25 @@ int oracle_moga_dq_rows(const float *q, const float *k, const float *v, const fl
         free(P); free(o); free(dO);
     }
     free(cnt); free(members);
+    return 0;
+}
+
+/* The router part above for selected tokens only: x_rows [n_rows][d] are those tokens' router
+ * inputs, g_rows their groups, dp_rows their dp_t; counts [m] and n are the whole problem's
+ * (F_i = counts_i / n).  Writes dr [n_rows][m] and dx [n_rows][d]. */
+int oracle_router_bwd_rows(const float *x_rows, const float *w, int64_t n_rows, int d, int m,
+                           const int32_t *g_rows, const double *dp_rows, const int64_t *counts,
+                           int64_t n, double d_loss, double alpha, double *dr, double *dx)
+{
+    if (n_rows < 0 || d < 1 || m < 1 || m > 256 || n < 1) return -1;
+    double *p = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1) * m);
+    double *F = (double *)malloc(sizeof(double) * (size_t)m);
+    if (!p || !F) { free(p); free(F); return -2; }
+    router_probs(x_rows, w, n_rows, d, m, p);
+    for (int i = 0; i < m; ++i) F[i] = (double)counts[i] / (double)n;
+    for (int64_t r = 0; r < n_rows; ++r)
+        router_bwd_token(p + r * m, g_rows[r], dp_rows[r], F, m, d, w, n, d_loss, alpha,
+                         dr + r * m, dx + r * d);
+    free(p); free(F);
     return 0;
 }

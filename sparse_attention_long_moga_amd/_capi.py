@@ -14,7 +14,8 @@ STATUS_NAMES = {0: "MOGA_OK", 1: "MOGA_ERR_ARG", 2: "MOGA_ERR_UNSUPPORTED",
 
 EXPORTS = ["moga_last_error", "moga_workspace_bytes", "moga_group_attn_workspace_bytes",
            "moga_route", "moga_permute", "moga_group_attn", "stga_group_attn",
-           "moga_balance_loss", "moga_forward", "moga_forward_fused"]
+           "moga_balance_loss", "moga_forward", "moga_forward_fused",
+           "moga_backward_workspace_bytes", "moga_backward"]
 
 
 class MogaDims(ctypes.Structure):
@@ -42,7 +43,19 @@ class MogaOutputs(ctypes.Structure):
     _fields_ = [("out", ctypes.c_void_p), ("loss", ctypes.c_void_p),
                 ("group_id", ctypes.c_void_p), ("p_sel", ctypes.c_void_p),
                 ("cu_seqlens", ctypes.c_void_p), ("perm", ctypes.c_void_p),
-                ("counts", ctypes.c_void_p), ("prob_sum", ctypes.c_void_p)]
+                ("counts", ctypes.c_void_p), ("prob_sum", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p)]
+
+
+class MogaSaved(ctypes.Structure):
+    _fields_ = [("group_id", ctypes.c_void_p), ("p_sel", ctypes.c_void_p),
+                ("counts", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
+class MogaGrads(ctypes.Structure):
+    _fields_ = [("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("dx", ctypes.c_void_p), ("dw", ctypes.c_void_p), ("dp", ctypes.c_void_p)]
 
 
 _lib = None
@@ -85,6 +98,11 @@ def load(path: str = LIB_PATH):
     lib.moga_forward.restype = st
     lib.moga_forward_fused.argtypes = lib.moga_forward.argtypes
     lib.moga_forward_fused.restype = st
+    lib.moga_backward_workspace_bytes.argtypes = [pdims]
+    lib.moga_backward_workspace_bytes.restype = sz
+    lib.moga_backward.argtypes = [ctypes.POINTER(MogaInputs), ctypes.POINTER(MogaSaved), vp,
+                                  ctypes.c_double, pdims, ctypes.POINTER(MogaGrads), vp, sz, vp]
+    lib.moga_backward.restype = st
     _lib = lib
     return lib
 

@@ -13,11 +13,11 @@ from typing import Optional, Sequence
 import torch
 
 from . import _capi
-from ._capi import MogaDims, MogaInputs, MogaOutputs, StgaLayout, check
+from ._capi import MogaDims, MogaGrads, MogaInputs, MogaOutputs, MogaSaved, StgaLayout, check
 
 __all__ = ["make_dims", "make_stga_layout", "moga_workspace_bytes", "workspace", "moga_route",
            "moga_permute", "moga_unpermute", "moga_group_attn", "stga_group_attn",
-           "moga_balance_loss", "moga_forward", "moga_forward_fused"]
+           "moga_balance_loss", "moga_forward", "moga_forward_fused", "moga_backward"]
 
 
 def _lib():
@@ -239,12 +239,13 @@ def moga_forward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Ten
                  v: torch.Tensor, n_groups: int, alpha: float = 0.1,
                  pin: Optional[torch.Tensor] = None, stga: Optional[_Layout] = None,
                  softmax_scale: float = 0.0, ws: Optional[torch.Tensor] = None,
-                 out: Optional[dict] = None, fused: bool = False) -> dict:
+                 out: Optional[dict] = None, fused: bool = False, with_lse: bool = False) -> dict:
     """Whole forward.  Returns a dict with out, loss and the routing tensors
-    (group_id, p_sel, cu_seqlens, perm, counts, prob_sum).  Pass `out` (a dict of
-    preallocated tensors with those keys) and `ws` to run without allocating.
-    fused=True calls moga_forward_fused (rows read through perm inside the attention
-    kernel; bitwise identical results)."""
+    (group_id, p_sel, cu_seqlens, perm, counts, prob_sum), plus lse ([H, N] f32, what
+    moga_backward needs) when with_lse is set.  Pass `out` (a dict of preallocated
+    tensors with those keys) and `ws` to run without allocating.  fused=True calls
+    moga_forward_fused (rows read through perm inside the attention kernel; bitwise
+    identical results)."""
     _need(x, "x", ndim=2)
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("x must be float32 or bfloat16")
@@ -265,13 +266,15 @@ def moga_forward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Ten
                    perm=torch.empty(n, dtype=torch.int32, device=dev),
                    counts=torch.empty(n_groups, dtype=torch.int32, device=dev),
                    prob_sum=torch.empty(n_groups, dtype=torch.float64, device=dev))
+        if with_lse:
+            out["lse"] = torch.empty(h, n, dtype=torch.float32, device=dev)
     ws = _ws(ws, moga_workspace_bytes(dims, stga), dev)
     ins = MogaInputs(x.data_ptr(), _capi.MOGA_BF16 if x.dtype == torch.bfloat16 else _capi.MOGA_F32,
                      w.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                      pin.data_ptr() if pin is not None else None)
     g = lambda key: out[key].data_ptr() if out.get(key) is not None else None
     outs = MogaOutputs(g("out"), g("loss"), g("group_id"), g("p_sel"), g("cu_seqlens"), g("perm"),
-                       g("counts"), g("prob_sum"))
+                       g("counts"), g("prob_sum"), g("lse"))
     fn = _lib().moga_forward_fused if fused else _lib().moga_forward
     check(fn(ctypes.byref(ins), ctypes.byref(dims), stga.ref() if stga else None,
              ctypes.byref(outs), _ptr(ws), ws.numel(), _stream()))
@@ -281,3 +284,52 @@ def moga_forward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Ten
 def moga_forward_fused(*args, **kwargs) -> dict:
     """moga_forward with the permutation applied inside the attention kernel."""
     return moga_forward(*args, fused=True, **kwargs)
+
+
+def moga_backward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                  v: torch.Tensor, saved: dict, d_out: torch.Tensor, d_loss: float = 0.0,
+                  alpha: float = 0.1, softmax_scale: float = 0.0,
+                  ws: Optional[torch.Tensor] = None, grads: Optional[dict] = None) -> dict:
+    """Gradients of moga_forward (stga None, routing held fixed).  saved: the dict
+    moga_forward returned with with_lse=True; d_out: bf16 [H, N, head_dim], the gradient
+    with respect to out; d_loss: the gradient with respect to the balance loss.  Returns
+    dq, dk, dv (bf16, like q), dx ([N, d] f32), dw ([d, M] f32) and dp ([N] f32)."""
+    _need(x, "x", ndim=2)
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    n, d = x.shape
+    _need(w, "w", torch.float32, 2, x.device)
+    m = w.shape[1]
+    h, nn, hd = _heads_shape([q, k, v, d_out, saved["out"]])
+    if nn != n or w.shape[0] != d:
+        raise ValueError("shape mismatch between x, w and q/k/v")
+    for key, dt, shape in (("group_id", torch.int32, (n,)), ("p_sel", torch.float32, (n,)),
+                           ("counts", torch.int32, (m,)), ("cu_seqlens", torch.int32, (m + 1,)),
+                           ("perm", torch.int32, (n,)), ("lse", torch.float32, (h, n))):
+        if saved.get(key) is None:
+            raise ValueError(f"saved['{key}'] is missing (run moga_forward with with_lse=True)")
+        _need(saved[key], f"saved['{key}']", dt, len(shape), x.device)
+        if tuple(saved[key].shape) != shape:
+            raise ValueError(f"saved['{key}'] must be {shape}")
+    dims = make_dims(n, d, h, hd, m, alpha=alpha, softmax_scale=softmax_scale)
+    dev = x.device
+    if grads is None:
+        grads = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                     dx=torch.empty(n, d, dtype=torch.float32, device=dev),
+                     dw=torch.empty(d, m, dtype=torch.float32, device=dev),
+                     dp=torch.empty(n, dtype=torch.float32, device=dev))
+    nb = _lib().moga_backward_workspace_bytes(ctypes.byref(dims))
+    if nb == 0:
+        check(_capi.MOGA_ERR_ARG)
+    ws = _ws(ws, nb, dev)
+    ins = MogaInputs(x.data_ptr(), _capi.MOGA_BF16 if x.dtype == torch.bfloat16 else _capi.MOGA_F32,
+                     w.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), None)
+    sv = lambda key: saved[key].data_ptr()
+    sav = MogaSaved(sv("group_id"), sv("p_sel"), sv("counts"), sv("cu_seqlens"), sv("perm"),
+                    sv("out"), sv("lse"))
+    g = lambda key: grads[key].data_ptr() if grads.get(key) is not None else None
+    gr = MogaGrads(g("dq"), g("dk"), g("dv"), g("dx"), g("dw"), g("dp"))
+    check(_lib().moga_backward(ctypes.byref(ins), ctypes.byref(sav), _ptr(d_out), float(d_loss),
+                               ctypes.byref(dims), ctypes.byref(gr), _ptr(ws), ws.numel(),
+                               _stream()))
+    return grads

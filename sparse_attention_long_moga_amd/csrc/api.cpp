@@ -125,7 +125,7 @@ struct Carver {
 struct Layout {
     // MoGA
     size_t part_p, part_c, wsplit, gid, psel, counts, probsum, cu, perm, table, base_rel, totals, pperm;
-    size_t qp, kp, vp, op, plan;
+    size_t qp, kp, vp, op, lsep, plan;
     // STGA
     size_t shot_info, cu_tq, cu_tk, cu_f, q_idx, kv_idx, ot, of;
     int32_t plan_seg;
@@ -157,6 +157,7 @@ Layout make_layout(const moga_dims *d, const StgaGeom *g) {
     L.kp = c.take(tensor);
     L.vp = c.take(tensor);
     L.op = c.take(tensor);
+    L.lsep = c.take(sizeof(float) * d->n_heads * n);
     int32_t seg = m;
     int64_t items = attn_max_items(d->n_heads, n, m);
     if (g) {
@@ -179,6 +180,39 @@ Layout make_layout(const moga_dims *d, const StgaGeom *g) {
     L.plan = c.take(attn_plan_bytes(seg, items));
     L.total = c.off;
     return L;
+}
+
+// backward: token-order D and dp, group-order copies of everything the attention backward
+// reads and writes, the router's dr and dW partials, and the attention plan
+struct BwdLayout {
+    size_t D, dp, Dp, lse2p, qp, kp, vp, dov, dqp, dkp, dvp, dr, dw_part, plan;
+    int64_t plan_items;
+    size_t total;
+};
+
+BwdLayout make_bwd_layout(const moga_dims *d) {
+    BwdLayout B{};
+    Carver c;
+    const int64_t n = d->n_tokens;
+    const size_t rows = sizeof(float) * d->n_heads * n;
+    const size_t tensor = (size_t)d->n_heads * n * d->head_dim * sizeof(uint16_t);
+    B.D = c.take(rows);
+    B.dp = c.take(sizeof(float) * n);
+    B.Dp = c.take(rows);
+    B.lse2p = c.take(rows);
+    B.qp = c.take(tensor);
+    B.kp = c.take(tensor);
+    B.vp = c.take(tensor);
+    B.dov = c.take(tensor);
+    B.dqp = c.take(tensor);
+    B.dkp = c.take(tensor);
+    B.dvp = c.take(tensor);
+    B.dr = c.take(sizeof(float) * n * d->n_groups);
+    B.dw_part = c.take(sizeof(float) * bwd_dw_chunks(n) * d->d_model * d->n_groups);
+    B.plan_items = attn_max_items(d->n_heads, n, d->n_groups);
+    B.plan = c.take(attn_plan_bytes(d->n_groups, B.plan_items));
+    B.total = c.off;
+    return B;
 }
 
 template <typename T>
@@ -243,7 +277,7 @@ moga_status run_attn(const void *q, const void *k, const void *v, void *o, const
                      const int32_t *kv_idx, const float *row_scale, int64_t len_q, int64_t len_k,
                      int64_t q_rows, int64_t kv_rows, int64_t o_rows, const moga_dims *d,
                      void *plan_mem, int32_t plan_seg, int64_t plan_items, int waves,
-                     hipStream_t s) {
+                     hipStream_t s, float *lse = nullptr) {
     AttnLaunch a{};
     a.q = static_cast<const bf16 *>(q); a.k = static_cast<const bf16 *>(k);
     a.v = static_cast<const bf16 *>(v); a.o = static_cast<bf16 *>(o);
@@ -253,6 +287,7 @@ moga_status run_attn(const void *q, const void *k, const void *v, void *o, const
     a.n_heads = d->n_heads; a.head_dim = d->head_dim; a.scale = scale_of(d);
     a.max_items = attn_max_items(d->n_heads, len_q, n_seg);
     a.waves = waves;
+    a.lse = lse;
     if (a.max_items > plan_items || n_seg > plan_seg)
         return fail(MOGA_ERR_WORKSPACE, "attention plan larger than its workspace region");
     attn_plan_carve(a.plan, plan_mem, n_seg, a.max_items);
@@ -434,7 +469,8 @@ static moga_status forward_impl(const moga_inputs *in, const moga_dims *dims, co
     if (fused) {
         // 3-5 in one pass: rows are read through perm and written back in token order
         if ((st = run_attn(in->q, in->k, in->v, out->out, cu, cu, dims->n_groups, perm, perm, psel,
-                           n, n, n, n, n, dims, plan, L.plan_seg, L.plan_items, 8, s)) != MOGA_OK)
+                           n, n, n, n, n, dims, plan, L.plan_seg, L.plan_items, 8, s,
+                           out->lse)) != MOGA_OK)
             return st;
     } else {
         // 3 gather Q, K, V and p by perm  4 varlen group attention scaled by p(g|x)
@@ -445,13 +481,17 @@ static moga_status forward_impl(const moga_inputs *in, const moga_dims *dims, co
         const void *src[3] = {in->q, in->k, in->v};
         void *dst[3] = {qp, kp, vp};
         if ((st = run_gather(0, perm, dims, src, dst, 3, psel, pperm, s)) != MOGA_OK) return st;
+        float *lsep = out->lse ? at<float>(ws, L.lsep) : nullptr;
         if ((st = run_attn(qp, kp, vp, op, cu, cu, dims->n_groups, nullptr, nullptr, pperm, n, n, n,
-                           n, n, dims, plan, L.plan_seg, L.plan_items, 8, s)) != MOGA_OK)
+                           n, n, dims, plan, L.plan_seg, L.plan_items, 8, s, lsep)) != MOGA_OK)
             return st;
         const void *osrc[1] = {op};
         void *odst[1] = {out->out};
         if ((st = run_gather(1, perm, dims, osrc, odst, 1, nullptr, nullptr, s)) != MOGA_OK)
             return st;
+        if (lsep)
+            HIP_TRY(launch_bwd_gather_f32(lsep, perm, n, dims->n_heads, 1.0f, 1, out->lse, s),
+                    "lse scatter launch");
     }
     // 6 group-balancing loss
     HIP_TRY(launch_balance_loss(counts, probsum, n, dims->n_groups, dims->alpha, out->loss, nullptr,
@@ -477,6 +517,95 @@ moga_status moga_forward_fused(const moga_inputs *in, const moga_dims *dims,
                                const stga_layout *stga, const moga_outputs *out, void *ws,
                                size_t ws_bytes, void *stream) {
     return forward_impl(in, dims, stga, out, ws, ws_bytes, stream, true);
+}
+
+size_t moga_backward_workspace_bytes(const moga_dims *dims) {
+    if (check_dims(dims) != MOGA_OK) return 0;
+    return make_bwd_layout(dims).total;
+}
+
+moga_status moga_backward(const moga_inputs *in, const moga_saved *saved, const void *d_out,
+                          double d_loss, const moga_dims *dims, const moga_grads *grads,
+                          void *ws, size_t ws_bytes, void *stream) {
+    moga_status st = check_dims(dims);
+    if (st != MOGA_OK) return st;
+    if (dims->head_dim != 128)
+        return fail(MOGA_ERR_UNSUPPORTED, "backward needs head_dim 128, got %d", dims->head_dim);
+    if (!in || !saved || !grads) return fail(MOGA_ERR_ARG, "inputs, saved or grads is NULL");
+    if ((st = check_route_args(in->x, in->x_dtype, in->w, dims)) != MOGA_OK) return st;
+    if (!in->q || !in->k || !in->v || !d_out) return fail(MOGA_ERR_ARG, "q, k, v or d_out is NULL");
+    if (!saved->group_id || !saved->p_sel || !saved->counts || !saved->cu_seqlens ||
+        !saved->perm || !saved->out || !saved->lse)
+        return fail(MOGA_ERR_ARG, "a saved forward tensor is NULL");
+    if (!grads->dq || !grads->dk || !grads->dv) return fail(MOGA_ERR_ARG, "dq, dk or dv is NULL");
+    const void *vec[8] = {in->q, in->k, in->v, d_out, saved->out, grads->dq, grads->dk, grads->dv};
+    for (const void *p : vec)
+        if (!aligned16(p)) return fail(MOGA_ERR_ARG, "q, k, v, d_out, out, dq, dk, dv must be 16-byte aligned");
+    if (!std::isfinite(d_loss)) return fail(MOGA_ERR_ARG, "d_loss is not finite");
+    const BwdLayout B = make_bwd_layout(dims);
+    if ((st = check_ws(ws, ws_bytes, B.total)) != MOGA_OK) return st;
+    if ((st = check_device()) != MOGA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = dims->n_tokens;
+    const int nh = dims->n_heads, m = dims->n_groups;
+    const int32_t *perm = saved->perm;
+
+    // D = <G, out> per (head, token) row; dp = sum over heads of D / p
+    float *D = at<float>(ws, B.D);
+    float *dp = grads->dp ? grads->dp : at<float>(ws, B.dp);
+    HIP_TRY(launch_bwd_rowdot(static_cast<const bf16 *>(d_out), static_cast<const bf16 *>(saved->out),
+                              (int64_t)nh * n, D, s),
+            "row dot launch");
+    HIP_TRY(launch_bwd_dp(D, saved->p_sel, n, nh, dp, s), "dp launch");
+    // group order: Q, K, V; dO' = p * G; D; lse in base 2
+    void *qp = at<char>(ws, B.qp), *kp = at<char>(ws, B.kp), *vp = at<char>(ws, B.vp);
+    void *dov = at<char>(ws, B.dov);
+    const void *src[3] = {in->q, in->k, in->v};
+    void *dst[3] = {qp, kp, vp};
+    if ((st = run_gather(0, perm, dims, src, dst, 3, nullptr, nullptr, s)) != MOGA_OK) return st;
+    {
+        GatherLaunch g{};
+        g.src[0] = d_out; g.dst[0] = dov; g.n_tensors = 1; g.perm = perm; g.n = n;
+        g.n_heads = nh; g.head_dim = dims->head_dim; g.inverse = 0; g.src_scale = saved->p_sel;
+        HIP_TRY(launch_gather(g, s), "scaled gather launch");
+    }
+    float *Dp = at<float>(ws, B.Dp), *lse2p = at<float>(ws, B.lse2p);
+    HIP_TRY(launch_bwd_gather_f32(D, perm, n, nh, 1.0f, 0, Dp, s), "D gather launch");
+    HIP_TRY(launch_bwd_gather_f32(saved->lse, perm, n, nh, 1.4426950408889634f, 0, lse2p, s),
+            "lse gather launch");
+    // attention backward per group
+    void *dqp = at<char>(ws, B.dqp), *dkp = at<char>(ws, B.dkp), *dvp = at<char>(ws, B.dvp);
+    {
+        AttnBwdLaunch a{};
+        a.q = static_cast<const bf16 *>(qp); a.k = static_cast<const bf16 *>(kp);
+        a.v = static_cast<const bf16 *>(vp); a.dov = static_cast<const bf16 *>(dov);
+        a.lse2 = lse2p; a.D = Dp;
+        a.dq = static_cast<bf16 *>(dqp); a.dk = static_cast<bf16 *>(dkp);
+        a.dv = static_cast<bf16 *>(dvp);
+        a.cu = saved->cu_seqlens; a.n_seg = m; a.len = n; a.n_heads = nh; a.scale = scale_of(dims);
+        a.max_items = B.plan_items;
+        attn_plan_carve(a.plan, at<char>(ws, B.plan), m, B.plan_items);
+        HIP_TRY(launch_attention_bwd(a, s), "attention backward launch");
+    }
+    // back to token order
+    {
+        const void *gsrc[3] = {dqp, dkp, dvp};
+        void *gdst[3] = {grads->dq, grads->dk, grads->dv};
+        if ((st = run_gather(1, perm, dims, gsrc, gdst, 3, nullptr, nullptr, s)) != MOGA_OK)
+            return st;
+    }
+    // router: softmax backward, dx, dW
+    if (grads->dx || grads->dw) {
+        BwdRouterLaunch r{};
+        r.x = in->x; r.x_is_bf16 = in->x_dtype == MOGA_BF16; r.w = in->w; r.n = n;
+        r.d = dims->d_model; r.m = m; r.group_id = saved->group_id; r.counts = saved->counts;
+        r.dp = dp;
+        r.loss_coef = (float)(d_loss * dims->alpha * m / ((double)n * (double)n));
+        r.dr = at<float>(ws, B.dr); r.dx = grads->dx; r.dw = grads->dw;
+        r.dw_part = at<float>(ws, B.dw_part);
+        HIP_TRY(launch_router_bwd(r, s), "router backward launch");
+    }
+    return MOGA_OK;
 }
 
 }  // extern "C"

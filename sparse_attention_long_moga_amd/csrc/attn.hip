@@ -22,22 +22,10 @@
 
 #include <type_traits>
 
-#include "moga_internal.h"
+#include "attn_common.h"
 
 namespace moga {
 namespace {
-
-constexpr int KT = 64;  // keys per LDS tile
-
-__device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
-    return v < lo ? lo : (v > hi ? hi : v);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    bf16x2 r = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, r);
-}
 
 // ---------------------------------------------------------------------------- planning
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const int32_t *cu_k,
@@ -132,22 +120,12 @@ struct Tile {
     static constexpr int VUNITS = (VCOMBOS + 2 * WAVES - 1) / (2 * WAVES);
 };
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor over [base, base + bytes): loads past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
 // Rescale the running output only when the row maximum has grown by more than 2^8 in
 // exp2 units; until then probabilities are formed against the stale maximum (they stay
 // <= 256), which changes no result beyond rounding because numerator and denominator
 // use the same reference.
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kLn2 = 0.69314718055994531f;
 
 // WAVES waves per block, 32 query rows each; every K/V tile brought into LDS serves all of
 // them, so 8 waves (256 rows, one block per CU, two waves per SIMD) halve the K/V traffic
@@ -399,6 +377,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel(AttnLaunch 
 
         // ---- epilogue: 1/l, optional per-row scale, bf16, 8-byte stores of 4 head channels
         const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+        if (a.lse && qvalid && hh == 0)  // log(sum exp(scale q.k)) = scale*m + ln(l)
+            a.lse[(int64_t)h * a.o_rows + qphys] =
+                l_tot > 0.0f ? (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
         if (qvalid) {
             float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
             if (a.row_scale) inv *= a.row_scale[qphys];
@@ -417,50 +398,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel(AttnLaunch 
 }
 
 // ---------------------------------------------------------------------------- attention,
-// head_dim 128, contiguous segments: K and V tiles go from HBM straight into LDS
-//
-// The permuted MoGA groups are contiguous rows, so each 16-byte chunk of a tile can be
-// fetched with a buffer load that writes LDS directly (no register staging, no LDS store
-// instructions).  Such a load places lane l's 16 bytes at base + 16*l, so the row layout
-// is chosen on the global side: LDS chunk c of row r holds global chunk c ^ sw(r).
-//   K: sw(r) = r & 15.  The A operand of S^T = K Q^T reads row j, chunk (2s + hh); 16
-//      consecutive rows then hit 16 different chunk positions, so each ds_read_b128 is
-//      bank-conflict free.
-//   V: natural [key][d] layout, sw(r) = 4 * (r & 3).  The A operand of O^T += V^T P^T is
-//      read with two ds_read_b64_tr_b16: within a group of 16 lanes, output lane 4a+b
-//      receives element b of the 8-byte pieces addressed by lanes a, a+4, a+8, a+12.  Lane
-//      s of group g points at row kc + 4*(g/2) + s/4 (+8 for the second read), columns
-//      32*ti + 16*(g%2) + 4*(s%4); lane d of the MFMA layout then holds V[4 keys][d], in
-//      the same key order as the probabilities.  The four rows a half-wave reads fall on
-//      four different 64-byte column ranges, so these reads are conflict free too.
-// LDS-side helpers of the direct-load kernel (kept out of lambdas: the host compilation
-// pass must not see the address-space-3 builtins)
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char *lds_base,
-                                           int voffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset, 0, 0, 0);
-}
-__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(p));
-    return __builtin_bit_cast(uint2, v);
-}
-
-// max(v, value of the lane 32 apart): v_permlane32_swap exchanges the upper half of one
-// operand with the lower half of the other, so with both operands v each lane sees both
-__device__ __forceinline__ float max_across_halves(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                    false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// acc + lo + hi of a packed pair of bf16 values (v_dot2 against (1, 1))
-__device__ __forceinline__ float sum_bf16x2(uint32_t packed, float acc) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
-}
+// head_dim 128: K and V tiles go from HBM straight into LDS, K in the A layout (S^T = K Q^T
+// reads it as the A operand) and V in the T layout (O^T += V^T P^T reads it transposed);
+// see attn_common.h.
 
 // IDX: rows are read through the index maps (STGA groups, or the permutation itself for
 // the permute-free MoGA variant); each lane then fetches its chunk's row index first.
@@ -484,23 +424,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
     const float thr = kRescaleLog2 / c;
 
     // per-lane LDS byte offsets of the MFMA operands within a tile
+    static_assert(ROWB == ROWB128, "direct-load layouts are for head_dim 128");
     int koff[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) koff[s] = j * ROWB + (((2 * s + hh) ^ (j & 15)) << 4);
-    const int s16 = lane & 15, g = lane >> 4;
+    for (int s = 0; s < NS; ++s) koff[s] = a_frag_off(j, hh, s);
+    const int s16 = lane & 15;
     int voff[NT];
 #pragma unroll
-    for (int ti = 0; ti < NT; ++ti)
-        voff[ti] = (4 * (g >> 1) + (s16 >> 2)) * ROWB +
-                   ((((ti ^ (s16 >> 2)) << 2) + 2 * (g & 1) + ((s16 & 3) >> 1)) << 4) + (s16 & 1) * 8;
+    for (int ti = 0; ti < NT; ++ti) voff[ti] = t_read_off(lane, ti);
     // per-lane global byte offsets of the direct loads within a tile
     int kgo[LOADS], vgo[LOADS], lrow[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
         const int r = (i * WAVES + wave) * 4 + (lane >> 4);
         lrow[i] = r;
-        kgo[i] = ((s16 ^ (r & 15)) << 4) + (IDX ? 0 : r * ROWB);
-        vgo[i] = ((s16 ^ (4 * (r & 3))) << 4) + (IDX ? 0 : r * ROWB);
+        kgo[i] = a_dma_chunk(r, s16) + (IDX ? 0 : r * ROWB);
+        vgo[i] = t_dma_chunk(r, s16) + (IDX ? 0 : r * ROWB);
     }
 
     for (;;) {
@@ -681,6 +620,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         }
 
         const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+        if (a.lse && qvalid && hh == 0)  // log(sum exp(scale q.k)) = scale*m + ln(l)
+            a.lse[(int64_t)h * a.o_rows + qphys] =
+                l_tot > 0.0f ? (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
         if (qvalid) {
             float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
             if (a.row_scale) inv *= a.row_scale[qphys];
@@ -739,6 +681,18 @@ void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items) 
     p.item_base = reinterpret_cast<int32_t *>(b); b += seg;
     p.items = reinterpret_cast<int4 *>(b); b += align256(sizeof(int4) * (size_t)max_items);
     p.counter = reinterpret_cast<int32_t *>(b);
+}
+
+hipError_t launch_attn_plan(const int32_t *cu_q, const int32_t *cu_k, int32_t n_seg,
+                            int64_t len_q, int64_t len_k, int n_heads, int bq, int64_t max_items,
+                            const AttnPlan &plan, hipStream_t s) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, cu_q, cu_k, n_seg, len_q, len_k,
+                       n_heads, bq, max_items, plan);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)((max_items + 255) / 256)), dim3(256), 0,
+                       s, plan, n_seg);
+    return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {

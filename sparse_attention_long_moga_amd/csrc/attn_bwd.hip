@@ -1,0 +1,409 @@
+// Backward of the group attention (head_dim 128, groups as contiguous row ranges), given the
+// forward's softmax normaliser per row (lse, natural log) and D = <dO', O'> per row:
+//   P = exp(scale Q K^T - lse),  dP = dO' V^T,  dS = P * (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO'
+// (dO' = p(g|x) * d_out: the factor of the MoGA output, papernotes.org MoGA note 关键设计 1).
+// Two kernels, so that each output row is written by one wave and no floating-point atomics
+// are needed (outputs are reproducible): one walks the keys of each query tile (dQ), the other
+// the queries of each key tile (dK, dV); both recompute P and dP from lse.
+// Tiles come from HBM straight into LDS in the two layouts described in attn_common.h.
+#include "attn_common.h"
+
+namespace moga {
+namespace {
+
+constexpr float kLog2eB = 1.4426950408889634f;
+
+// ------------------------------------------------------------------------------------- dQ
+// Item = (group, head, 128 query rows); wave w owns query rows 32w .. 32w+31 of the item.
+// Per 64-key tile: K in the A layout (S^T = K Q^T), K in the T layout (dQ^T += K^T dS^T) and
+// V in the A layout (dP^T = V dO'^T).  Q^T and dO'^T stay in registers as B operands; each
+// lane holds one query (a column of the 32x32 accumulators), so lse and D are one value per
+// lane, and the scores of a lane are 16 keys in runs of 4, the order dS^T is fed back in.
+// One wave per SIMD, like the dK/dV kernel: Q^T, dO'^T, dQ^T and two score accumulators do not
+// fit the 256 registers a wave gets when two share a SIMD.
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnBwdLaunch a) {
+    constexpr int HD = 128, NS = HD / 16, NT = HD / 32, WAVES = 4, THREADS = 64 * WAVES;
+    constexpr int BQ = 32 * WAVES;
+    constexpr int ROWB = ROWB128, TILEB = KT * ROWB;
+    constexpr int LOADS = TILEB / 16 / THREADS;
+    static_assert(LOADS * THREADS * 16 == TILEB, "tile must split into whole wave loads");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2][3][TILEB];  // K_A, K_T, V_A
+    __shared__ int s_item;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 31, hh = lane >> 5, s16 = lane & 15;
+    const int total = uniform(a.plan.counter[1]);
+    const float c = a.scale * kLog2eB;
+    int koff[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) koff[s] = a_frag_off(j, hh, s);
+    int voff[NT];
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) voff[ti] = t_read_off(lane, ti);
+    int ago[LOADS], tgo[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int r = (i * WAVES + wave) * 4 + (lane >> 4);
+        ago[i] = a_dma_chunk(r, s16) + r * ROWB;
+        tgo[i] = t_dma_chunk(r, s16) + r * ROWB;
+    }
+
+    for (;;) {
+        if (tid == 0) s_item = atomicAdd(a.plan.counter, 1);
+        __syncthreads();
+        const int item = uniform(s_item);
+        __syncthreads();
+        if (item >= total) break;
+        const int4 itm = a.plan.items[item];
+        const int seg = uniform(itm.x), h = uniform(itm.y), qt = uniform(itm.z);
+        const int rb = uniform((int)clamp64(a.cu[seg], 0, a.len));
+        const int re = uniform((int)clamp64(a.cu[seg + 1], rb, a.len));
+        const int klen = re - rb;
+        const int qrow = rb + qt * BQ + wave * 32 + j;
+        const bool qvalid = qrow < re;
+        const int qrow_c = qvalid ? qrow : re - 1;  // re > rb for every item
+        const int64_t hrow = (int64_t)h * a.len;
+        bf16x8 qf[NS], gf[NS];
+        {
+            const bf16 *qp = a.q + (hrow + qrow_c) * HD + 8 * hh;
+            const bf16 *gp = a.dov + (hrow + qrow_c) * HD + 8 * hh;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
+                gf[s] = *reinterpret_cast<const bf16x8 *>(gp + 16 * s);
+            }
+        }
+        const float lse2 = a.lse2[hrow + qrow_c], dd = a.D[hrow + qrow_c];
+        const bf16 *kbase = a.k + hrow * HD, *vbase = a.v + hrow * HD;
+        const int ntiles = (klen + KT - 1) / KT;
+
+        // key tile t -> buffer BUF; rows past the group read as zeros
+        auto issue = [&](auto bufc, int t) {
+            constexpr int buf = decltype(bufc)::value;
+            const int key0 = t * KT;
+            const uint32_t bytes = (uint32_t)max(klen - key0, 0) * ROWB;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)(rb + key0) * HD, bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)(rb + key0) * HD, bytes);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int slot = (i * WAVES + wave) * 1024;
+                load_lds16(rk, &lds[buf][0][slot], ago[i]);
+                load_lds16(rk, &lds[buf][1][slot], tgo[i]);
+                load_lds16(rv, &lds[buf][2][slot], ago[i]);
+            }
+        };
+
+        f32x16 dq[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) dq[ti] = f32x16{};
+
+        auto tile = [&](auto bufc, auto maskc, int t) {
+            constexpr int buf = decltype(bufc)::value;
+            constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
+            if (t + 1 < ntiles) issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
+            const unsigned char *ka = lds[buf][0], *kt_ = lds[buf][1], *va = lds[buf][2];
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {  // one 32-key block at a time
+                f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ka + sb * 32 * ROWB + koff[s]);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
+                    const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(va + sb * 32 * ROWB + koff[s]);
+                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[s], pacc, 0, 0, 0);
+                }
+                bf16x8 dsf[2];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    float ds[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int v = half * 8 + e;
+                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c, -lse2));
+                        if constexpr (MASK) {
+                            const int key = t * KT + sb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+                            if (key >= klen) p = 0.0f;
+                        }
+                        ds[e] = p * (pacc[v] - dd);
+                    }
+                    const uint4 packed = make_uint4(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
+                                                    pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7]));
+                    dsf[half] = __builtin_bit_cast(bf16x8, packed);
+                }
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int ti = 0; ti < NT; ++ti) {
+                        const unsigned char *kp = kt_ + (sb * 2 + half) * 16 * ROWB + voff[ti];
+                        const uint2 ulo = lds_read_tr16(kp), uhi = lds_read_tr16(kp + 8 * ROWB);
+                        const bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+                        dq[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dsf[half], dq[ti], 0, 0, 0);
+                    }
+            }
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed
+            __syncthreads();
+        };
+
+        if (ntiles > 0) {
+            issue(std::integral_constant<int, 0>{}, 0);
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+            __syncthreads();
+        }
+        const int nfull = klen / KT;
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        using NoMask = std::integral_constant<bool, false>;
+        using Mask = std::integral_constant<bool, true>;
+        int t = 0;
+        for (; t + 1 < nfull; t += 2) {
+            tile(B0{}, NoMask{}, t);
+            tile(B1{}, NoMask{}, t + 1);
+        }
+        if (t < nfull) {
+            tile(B0{}, NoMask{}, t);
+            ++t;
+        }
+        if (t < ntiles) {
+            if (t & 1) tile(B1{}, Mask{}, t);
+            else tile(B0{}, Mask{}, t);
+        }
+        if (qvalid) {
+            bf16 *op = a.dq + (hrow + qrow) * HD + 4 * hh;
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) {
+                    const uint2 w = make_uint2(
+                        pack_bf16x2(dq[ti][kq * 4 + 0] * a.scale, dq[ti][kq * 4 + 1] * a.scale),
+                        pack_bf16x2(dq[ti][kq * 4 + 2] * a.scale, dq[ti][kq * 4 + 3] * a.scale));
+                    *reinterpret_cast<uint2 *>(op + 32 * ti + 8 * kq) = w;
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------- dK, dV
+// Item = (group, head, 128 key rows); wave w owns key rows 32w .. 32w+31.  Per 64-query tile:
+// Q and dO' each in the A layout (S = Q K^T, dP = dO' V^T read them as A operands) and in the
+// T layout (dK^T += Q^T dS, dV^T += dO'^T P read them transposed), plus lse2 and D of the
+// tile's queries.  K^T and V^T stay in registers as B operands; each lane holds one key (a
+// column of the 32x32 accumulators) and 16 query rows in runs of 4, so P and dS are fed back
+// as B operands directly.  One wave per SIMD: the two accumulators take 128 registers, so the
+// kernel uses the accumulation registers as well.
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) {
+    constexpr int HD = 128, NS = HD / 16, NT = HD / 32, WAVES = 4, THREADS = 64 * WAVES;
+    constexpr int BK = 32 * WAVES;
+    constexpr int ROWB = ROWB128, TILEB = KT * ROWB;
+    constexpr int LOADS = TILEB / 16 / THREADS;
+    static_assert(LOADS * THREADS * 16 == TILEB, "tile must split into whole wave loads");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2][4][TILEB];  // Q_A Q_T G_A G_T
+    __shared__ __attribute__((aligned(16))) float rowv[2][2][256];              // lse2, D
+    __shared__ int s_item;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 31, hh = lane >> 5, s16 = lane & 15;
+    const int total = uniform(a.plan.counter[1]);
+    const float c = a.scale * kLog2eB;
+    int koff[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) koff[s] = a_frag_off(j, hh, s);
+    int voff[NT];
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) voff[ti] = t_read_off(lane, ti);
+    int ago[LOADS], tgo[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int r = (i * WAVES + wave) * 4 + (lane >> 4);
+        ago[i] = a_dma_chunk(r, s16) + r * ROWB;
+        tgo[i] = t_dma_chunk(r, s16) + r * ROWB;
+    }
+
+    for (;;) {
+        if (tid == 0) s_item = atomicAdd(a.plan.counter, 1);
+        __syncthreads();
+        const int item = uniform(s_item);
+        __syncthreads();
+        if (item >= total) break;
+        const int4 itm = a.plan.items[item];
+        const int seg = uniform(itm.x), h = uniform(itm.y), kt = uniform(itm.z);
+        const int rb = uniform((int)clamp64(a.cu[seg], 0, a.len));
+        const int re = uniform((int)clamp64(a.cu[seg + 1], rb, a.len));
+        const int qlen = re - rb;
+        const int krow = rb + kt * BK + wave * 32 + j;
+        const bool kvalid = krow < re;
+        const int krow_c = kvalid ? krow : re - 1;
+        const int64_t hrow = (int64_t)h * a.len;
+        bf16x8 kf[NS], vf[NS];
+        {
+            const bf16 *kp = a.k + (hrow + krow_c) * HD + 8 * hh;
+            const bf16 *vp = a.v + (hrow + krow_c) * HD + 8 * hh;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                kf[s] = *reinterpret_cast<const bf16x8 *>(kp + 16 * s);
+                vf[s] = *reinterpret_cast<const bf16x8 *>(vp + 16 * s);
+            }
+        }
+        const bf16 *qbase = a.q + hrow * HD, *gbase = a.dov + hrow * HD;
+        const int ntiles = (qlen + KT - 1) / KT;
+
+        // query tile t -> buffer BUF; rows past the group read as zeros
+        auto issue = [&](auto bufc, int t) {
+            constexpr int buf = decltype(bufc)::value;
+            const int q0 = t * KT;
+            const uint32_t bytes = (uint32_t)max(qlen - q0, 0) * ROWB;
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (int64_t)(rb + q0) * HD, bytes);
+            const __amdgpu_buffer_rsrc_t rg = make_rsrc(gbase + (int64_t)(rb + q0) * HD, bytes);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int slot = (i * WAVES + wave) * 1024;
+                load_lds16(rq, &lds[buf][0][slot], ago[i]);
+                load_lds16(rq, &lds[buf][1][slot], tgo[i]);
+                load_lds16(rg, &lds[buf][2][slot], ago[i]);
+                load_lds16(rg, &lds[buf][3][slot], tgo[i]);
+            }
+            if (wave == 0) {  // lse2 and D of the tile's queries (256 entries; 64 are used)
+                const uint32_t rbytes = (uint32_t)max(qlen - q0, 0) * 4;
+                const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse2 + hrow + rb + q0, rbytes);
+                const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.D + hrow + rb + q0, rbytes);
+                load_lds16(rl, reinterpret_cast<unsigned char *>(&rowv[buf][0][0]), 16 * lane);
+                load_lds16(rd, reinterpret_cast<unsigned char *>(&rowv[buf][1][0]), 16 * lane);
+            }
+        };
+
+        f32x16 dk[NT], dv[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) { dk[ti] = f32x16{}; dv[ti] = f32x16{}; }
+
+        auto tile = [&](auto bufc, auto maskc, int t) {
+            constexpr int buf = decltype(bufc)::value;
+            constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
+            if (t + 1 < ntiles) issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
+            const unsigned char *qa = lds[buf][0], *qt_ = lds[buf][1];
+            const unsigned char *ga = lds[buf][2], *gt_ = lds[buf][3];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(qa + qb * 32 * ROWB + koff[s]);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[s], sacc, 0, 0, 0);
+                    const bf16x8 gf = *reinterpret_cast<const bf16x8 *>(ga + qb * 32 * ROWB + koff[s]);
+                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, vf[s], pacc, 0, 0, 0);
+                }
+                // the 16 query rows of this lane: qb*32 + 8*kq + 4*hh + e, kq < 4, e < 4
+                bf16x8 pf[2], dsf[2];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    float pv[8], ds[8];
+                    float4 l4[2], d4[2];
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2) {
+                        const int row = qb * 32 + 8 * (2 * half + k2) + 4 * hh;
+                        l4[k2] = *reinterpret_cast<const float4 *>(&rowv[buf][0][row]);
+                        d4[k2] = *reinterpret_cast<const float4 *>(&rowv[buf][1][row]);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int v = half * 8 + e, kq = v >> 2;
+                        const float ls = (&l4[e >> 2].x)[v & 3], dd = (&d4[e >> 2].x)[v & 3];
+                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c, -ls));
+                        if constexpr (MASK) {
+                            const int q = t * KT + qb * 32 + 8 * kq + 4 * hh + (v & 3);
+                            if (q >= qlen) p = 0.0f;
+                        }
+                        pv[e] = p;
+                        ds[e] = p * (pacc[v] - dd);
+                    }
+                    pf[half] = __builtin_bit_cast(
+                        bf16x8, make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
+                    dsf[half] = __builtin_bit_cast(
+                        bf16x8, make_uint4(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
+                                           pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7])));
+                }
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int ch = qb * 2 + half;
+#pragma unroll
+                    for (int ti = 0; ti < NT; ++ti) {
+                        const unsigned char *gp = gt_ + ch * 16 * ROWB + voff[ti];
+                        const uint2 glo = lds_read_tr16(gp), ghi = lds_read_tr16(gp + 8 * ROWB);
+                        const bf16x8 gT = __builtin_bit_cast(bf16x8, make_uint4(glo.x, glo.y, ghi.x, ghi.y));
+                        dv[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gT, pf[half], dv[ti], 0, 0, 0);
+                        const unsigned char *qp = qt_ + ch * 16 * ROWB + voff[ti];
+                        const uint2 qlo = lds_read_tr16(qp), qhi = lds_read_tr16(qp + 8 * ROWB);
+                        const bf16x8 qT = __builtin_bit_cast(bf16x8, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
+                        dk[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf[half], dk[ti], 0, 0, 0);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed
+            __syncthreads();
+        };
+
+        if (ntiles > 0) {
+            issue(std::integral_constant<int, 0>{}, 0);
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+            __syncthreads();
+        }
+        const int nfull = qlen / KT;
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        using NoMask = std::integral_constant<bool, false>;
+        using Mask = std::integral_constant<bool, true>;
+        int t = 0;
+        for (; t + 1 < nfull; t += 2) {
+            tile(B0{}, NoMask{}, t);
+            tile(B1{}, NoMask{}, t + 1);
+        }
+        if (t < nfull) {
+            tile(B0{}, NoMask{}, t);
+            ++t;
+        }
+        if (t < ntiles) {
+            if (t & 1) tile(B1{}, Mask{}, t);
+            else tile(B0{}, Mask{}, t);
+        }
+        if (kvalid) {
+            bf16 *kp = a.dk + (hrow + krow) * HD + 4 * hh;
+            bf16 *vp = a.dv + (hrow + krow) * HD + 4 * hh;
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) {
+                    const uint2 wk = make_uint2(
+                        pack_bf16x2(dk[ti][kq * 4 + 0] * a.scale, dk[ti][kq * 4 + 1] * a.scale),
+                        pack_bf16x2(dk[ti][kq * 4 + 2] * a.scale, dk[ti][kq * 4 + 3] * a.scale));
+                    *reinterpret_cast<uint2 *>(kp + 32 * ti + 8 * kq) = wk;
+                    const uint2 wv = make_uint2(pack_bf16x2(dv[ti][kq * 4 + 0], dv[ti][kq * 4 + 1]),
+                                                pack_bf16x2(dv[ti][kq * 4 + 2], dv[ti][kq * 4 + 3]));
+                    *reinterpret_cast<uint2 *>(vp + 32 * ti + 8 * kq) = wv;
+                }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attention_bwd(const AttnBwdLaunch &a, hipStream_t s) {
+    if (a.n_seg <= 0) return hipSuccess;
+    int cus = 0;
+    hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    // dQ: items of 128 query rows, inner loop over the group's keys
+    if ((e = launch_attn_plan(a.cu, a.cu, a.n_seg, a.len, a.len, a.n_heads, 128, a.max_items,
+                              a.plan, s)) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)cus), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // dK, dV: items of 128 key rows, inner loop over the group's queries (the plan is rebuilt
+    // in place once the dQ kernel, earlier on the stream, is done with it)
+    if ((e = launch_attn_plan(a.cu, a.cu, a.n_seg, a.len, a.len, a.n_heads, 128, a.max_items,
+                              a.plan, s)) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)cus), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moga

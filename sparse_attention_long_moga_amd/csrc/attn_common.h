@@ -1,0 +1,95 @@
+// Device helpers shared by the forward and backward attention kernels of libmoga.so
+// (internal; not part of the public ABI).
+//
+// Direct-to-LDS tiles (head_dim 128): a buffer load that writes LDS places lane l's 16 bytes
+// at base + 16*l, so the row layout is chosen on the global side: LDS chunk c of row r holds
+// global chunk c ^ sw(r).  Two layouts:
+//   "A" layout, sw(r) = r & 15: an MFMA A operand (32 rows x 16 columns) is read with one
+//      ds_read_b128 per lane (row j, 16-byte chunk 2s + hh); 16 consecutive rows hit 16
+//      different chunk positions, so the read is bank-conflict free.
+//   "T" layout, natural [row][d] order, sw(r) = 4 * (r & 3): the transposed A operand
+//      (32 columns of d x 16 rows) is read with two ds_read_b64_tr_b16; within a group of 16
+//      lanes, output lane 4a+b receives element b of the 8-byte pieces addressed by lanes a,
+//      a+4, a+8, a+12.  Lane s of group g points at row kc + 4*(g/2) + s/4 (+8 for the second
+//      read), columns 32*ti + 16*(g%2) + 4*(s%4); lane d of the MFMA layout then holds
+//      X[4 rows][d] in the same row order as a 32x32 accumulator's rows (runs of 4), which is
+//      the order a B operand built from such an accumulator uses.  The four rows a half-wave
+//      reads fall on four different 64-byte column ranges, so these reads are conflict free.
+#pragma once
+
+#include "moga_internal.h"
+
+namespace moga {
+namespace {
+
+constexpr int KT = 64;       // rows per LDS tile
+constexpr int ROWB128 = 256; // bytes per bf16 row at head_dim 128
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Buffer descriptor over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// LDS-side helpers (kept out of lambdas: the host compilation pass must not see the
+// address-space-3 builtins)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char *lds_base,
+                                           int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset, 0, 0, 0);
+}
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// max(v, value of the lane 32 apart): v_permlane32_swap exchanges the upper half of one
+// operand with the lower half of the other, so with both operands v each lane sees both
+__device__ __forceinline__ float max_across_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// acc + lo + hi of a packed pair of bf16 values (v_dot2 against (1, 1))
+__device__ __forceinline__ float sum_bf16x2(uint32_t packed, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+}
+
+// LDS byte offset, within a tile in the A layout, of the 16 bytes lane (row j, half hh) reads
+// for MFMA k-step s (columns 16s .. 16s+15 of head_dim 128)
+__device__ __forceinline__ int a_frag_off(int j, int hh, int s) {
+    return j * ROWB128 + (((2 * s + hh) ^ (j & 15)) << 4);
+}
+// LDS byte offset, within a tile in the T layout, of lane's first transposed 8-byte read for
+// d block ti (the second read is 8 rows further); add 16 * ROWB128 per 16-row chunk
+__device__ __forceinline__ int t_read_off(int lane, int ti) {
+    const int s16 = lane & 15, g = lane >> 4;
+    return (4 * (g >> 1) + (s16 >> 2)) * ROWB128 +
+           ((((ti ^ (s16 >> 2)) << 2) + 2 * (g & 1) + ((s16 & 3) >> 1)) << 4) + (s16 & 1) * 8;
+}
+// byte offset within a global row of the 16-byte chunk that lands in LDS chunk s16 of row r
+__device__ __forceinline__ int a_dma_chunk(int r, int s16) { return (s16 ^ (r & 15)) << 4; }
+__device__ __forceinline__ int t_dma_chunk(int r, int s16) { return (s16 ^ (4 * (r & 3))) << 4; }
+
+}  // namespace
+}  // namespace moga

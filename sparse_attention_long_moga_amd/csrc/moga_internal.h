@@ -71,6 +71,7 @@ struct GatherLaunch {
     int inverse;
     const float *p_sel;  // optional gather of one fp32 value per row (inverse == 0 only)
     float *p_perm;
+    const float *src_scale;  // NULL, or (inverse == 0, one tensor) dst row j = src_scale[perm[j]] * src row
 };
 hipError_t launch_gather(const GatherLaunch &a, hipStream_t s);
 
@@ -102,8 +103,56 @@ struct AttnLaunch {
     AttnPlan plan;
     int64_t max_items;
     int waves;               // 8: long segments (MoGA groups), 4: short ones (STGA)
+    float *lse;              // NULL or [H][o_rows]: natural-log softmax normaliser per row
 };
 hipError_t launch_attention(const AttnLaunch &a, hipStream_t s);
+// Builds the item list of a launch: items (segment, head, tile of bq rows of cu_q), segments
+// ordered by decreasing cu_k length.
+hipError_t launch_attn_plan(const int32_t *cu_q, const int32_t *cu_k, int32_t n_seg,
+                            int64_t len_q, int64_t len_k, int n_heads, int bq, int64_t max_items,
+                            const AttnPlan &plan, hipStream_t s);
+
+// ---------------------------------------------------------------- attention backward
+struct AttnBwdLaunch {
+    const bf16 *q, *k, *v;   // group order [H][len][hd]
+    const bf16 *dov;         // dO' = p(g|x) * d_out, group order [H][len][hd]
+    const float *lse2;       // [H][len]: log2(sum_u exp2(c q.k_u)), c = scale * log2(e)
+    const float *D;          // [H][len]: <dO', O'>
+    bf16 *dq, *dk, *dv;      // group order [H][len][hd]
+    const int32_t *cu;       // [n_seg + 1]: group u's rows are [cu[u], cu[u+1]) for q and k
+    int32_t n_seg;
+    int64_t len;             // rows per head
+    int n_heads;
+    float scale;
+    AttnPlan plan;           // rebuilt for each of the two kernels
+    int64_t max_items;
+};
+hipError_t launch_attention_bwd(const AttnBwdLaunch &a, hipStream_t s);
+
+// ---------------------------------------------------------------- backward support
+struct BwdRouterLaunch {
+    const void *x;
+    int x_is_bf16;
+    const float *w;          // [d][m]
+    int64_t n;
+    int d, m;
+    const int32_t *group_id; // [n]
+    const int32_t *counts;   // [m]
+    const float *dp;         // [n]
+    float loss_coef;         // d_loss * alpha * m / n^2  (times counts_i = the L_gb term)
+    float *dr;               // [n][m]
+    float *dx;               // NULL or [n][d]
+    float *dw;               // NULL or [d][m]
+    float *dw_part;          // [bwd_dw_chunks(n)][d][m]
+};
+int64_t bwd_dw_chunks(int64_t n);
+hipError_t launch_bwd_rowdot(const bf16 *d_out, const bf16 *out, int64_t rows, float *D,
+                             hipStream_t s);
+hipError_t launch_bwd_dp(const float *D, const float *p_sel, int64_t n, int n_heads, float *dp,
+                         hipStream_t s);
+hipError_t launch_bwd_gather_f32(const float *src, const int32_t *perm, int64_t n, int n_heads,
+                                 float mult, int inverse, float *dst, hipStream_t s);
+hipError_t launch_router_bwd(const BwdRouterLaunch &a, hipStream_t s);
 
 // ---------------------------------------------------------------- STGA
 struct StgaGeom {

@@ -106,7 +106,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *gid, int64_
 }
 
 // Row gather/scatter.  grid = (row blocks, heads, tensors); each thread moves 16 bytes.
-template <int HD>
+// SCALED: dst row j = bf16(src_scale[perm[j]] * src row perm[j]) (forward direction only)
+template <int HD, bool SCALED>
 __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch a) {
     typedef int i32x4 __attribute__((ext_vector_type(4)));
     constexpr int CH = HD * 2 / 16;         // 16-byte chunks per row
@@ -139,6 +140,22 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch a) {
         const bool ok = j < n && pj[p] >= 0 && pj[p] < n;
         const int64_t s_row = ok ? (a.inverse ? j : (int64_t)pj[p]) : 0;
         buf[p] = *reinterpret_cast<const i32x4 *>(src + s_row * HD + ch * 8);
+    }
+    if constexpr (SCALED) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int64_t j = j0 + p * ROWS;
+            const bool ok = j < n && pj[p] >= 0 && pj[p] < n;
+            const float f = a.src_scale[ok ? pj[p] : 0];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w = (uint32_t)buf[p][q];
+                const float lo = __uint_as_float(w << 16) * f, hi = __uint_as_float(w & 0xffff0000u) * f;
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                const bf16x2 r = {(__bf16)lo, (__bf16)hi};
+                buf[p][q] = (int)__builtin_bit_cast(uint32_t, r);
+            }
+        }
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
@@ -184,10 +201,14 @@ hipError_t launch_gather(const GatherLaunch &a, hipStream_t s) {
         const int ch = a.head_dim * 2 / 16;
         const int64_t rows_per_block = (256 / ch) * 8;
         dim3 grid((unsigned)((a.n + rows_per_block - 1) / rows_per_block), a.n_heads, a.n_tensors);
-        if (a.head_dim == 128)
-            hipLaunchKernelGGL(gather_kernel<128>, grid, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL(gather_kernel<64>, grid, dim3(256), 0, s, a);
+        const bool scaled = a.src_scale && !a.inverse;
+        if (a.head_dim == 128) {
+            if (scaled) hipLaunchKernelGGL((gather_kernel<128, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((gather_kernel<128, false>), grid, dim3(256), 0, s, a);
+        } else {
+            if (scaled) hipLaunchKernelGGL((gather_kernel<64, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((gather_kernel<64, false>), grid, dim3(256), 0, s, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -404,6 +404,29 @@ def test_backward_finite_differences():
             assert abs(fd - ref[gname][idx]) < 1e-6 * max(1.0, abs(fd)), (gname, idx, fd)
 
 
+def test_router_backward_rows_matches_autograd():
+    """The router part on a subset of tokens equals torch autograd, in x, of
+    sum_t dp_t p(g_t|x_t) + d_loss alpha M sum_i F_i mean_t p(i|x_t), where F and the mean
+    are over the whole problem's n tokens and only the selected rows vary."""
+    rng = np.random.Generator(np.random.PCG64(35))
+    n, r, d, m = 50, 7, 12, 6
+    x = rng.standard_normal((r, d)).astype(np.float32)
+    w = (rng.standard_normal((d, m)) / 3).astype(np.float32)
+    g = rng.integers(0, m, r).astype(np.int32)
+    dp = rng.standard_normal(r)
+    counts = np.array([12, 0, 9, 20, 4, 5], np.int64)
+    d_loss, alpha = 0.9, 0.1
+    X = torch.tensor(x.astype(np.float64), requires_grad=True)
+    p = torch.softmax(X @ torch.from_numpy(w.astype(np.float64)), dim=1)
+    F = torch.from_numpy(counts.astype(np.float64)) / n
+    J = (torch.from_numpy(dp) * p[torch.arange(r), torch.from_numpy(g.astype(np.int64))]).sum() + \
+        d_loss * alpha * m * (F * p.sum(0) / n).sum()
+    (gx,) = torch.autograd.grad(J, [X])
+    dr, dx = oracle.router_backward_rows(x, w, g, dp, counts, n, d_loss, alpha)
+    np.testing.assert_allclose(dx, gx.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dr.sum(1), 0.0, atol=1e-13)  # softmax backward rows sum to zero
+
+
 def test_backward_group_sums():
     """sum over a group of dv = sum of p * d_out over it (softmax rows sum to one), and the
     sum of dk over a group vanishes (each row of dS sums to zero)."""

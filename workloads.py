@@ -162,6 +162,15 @@ def make_qkv(wl: Workload, device="cpu", n_heads: Optional[int] = None):
                  for _ in range(3))
 
 
+def make_dout(wl: Workload, device="cpu", n_heads: Optional[int] = None) -> torch.Tensor:
+    """Gradient arriving at the attention output: N(0,1) as bf16 [H][N][hd] on `device`."""
+    h = wl.n_heads if n_heads is None else n_heads
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed * 1000 + 37)
+    return torch.randn((h, wl.n_tokens, wl.head_dim), generator=g, device=device,
+                       dtype=torch.bfloat16)
+
+
 def random_rows(n: int, k: int, seed: int) -> np.ndarray:
     """k distinct sorted indices in [0, n), seeded (for sampled parity checks)."""
     rng = np.random.Generator(np.random.PCG64(seed))
