@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--msweep", action="store_true",
                    help="only run the group-count sweep (M = 1, 2, 4, 8, 16 at the 10 s shape) "
                         "and print one JSON line per M")
+    p.add_argument("--backward", action="store_true",
+                   help="only time moga_backward (after one forward that saves lse) on the "
+                        "workload and print one JSON line")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates the HBM byte "
                         "counters against a known size) and exit")
@@ -96,6 +99,9 @@ def main():
 
     if args.msweep:
         msweep(args)
+        return
+    if args.backward:
+        backward(args)
         return
 
     wl = workloads.BY_NAME[args.workload]
@@ -243,6 +249,71 @@ PAGES_MSWEEP = {1: (0.0, 0.88), 2: (0.4125, 0.59), 4: (0.6625, 0.42), 8: (0.7875
 # it): 30 attention layers at 4*hd*H FLOPs per (query, key) pair plus 2 * 1.3e9 parameters per
 # token (Wan2.1-1.3B public sizes; the layer count and parameter count are not on the pages).
 WAN13B_LAYERS, WAN13B_PARAMS = 30, 1.3e9
+
+
+def backward(args):
+    """Time moga_backward: D and dp, the row gathers, the dQ and dK/dV attention kernels, the
+    inverse gathers and the router backward, with inputs and the forward's saved state
+    resident in HBM.  Attention FLOPs are counted two ways: the five products of the
+    standard attention backward (S recomputed, dP, dV, dQ, dK: 10 hd per query-key pair and
+    head) and what the two kernels execute (both compute S and dP: 14 hd)."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from sparse_attention_long_moga_amd import api, metrics
+
+    wl = workloads.BY_NAME[args.workload]
+    if wl.hybrid:
+        raise SystemExit("the backward covers MoGA only; pick a workload without STGA")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n, h, hd, m = wl.n_tokens, wl.n_heads, wl.head_dim, wl.n_groups
+    log(f"backward {wl.name}: generating inputs")
+    x, w = workloads.make_x(wl, dev), workloads.make_w(wl, dev)
+    q, k, v = workloads.make_qkv(wl, dev)
+    dout = workloads.make_dout(wl, dev)
+    saved = api.moga_forward(x, w, q, k, v, m, alpha=wl.alpha, fused=True, with_lse=True)
+    dims = api.make_dims(n, wl.d_model, h, hd, m, alpha=wl.alpha)
+    import ctypes
+    from sparse_attention_long_moga_amd import _capi
+    ws = api.workspace(_capi.load().moga_backward_workspace_bytes(ctypes.byref(dims)), dev)
+    grads = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                 dx=torch.empty(n, wl.d_model, dtype=torch.float32, device=dev),
+                 dw=torch.empty(wl.d_model, m, dtype=torch.float32, device=dev),
+                 dp=torch.empty(n, dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+
+    def step():
+        api.moga_backward(x, w, q, k, v, saved, dout, d_loss=1.0, alpha=wl.alpha, ws=ws,
+                          grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} backward steps")
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    counts = saved["counts"].cpu().numpy().astype(np.int64)
+    pairs = metrics.moga_pairs(counts)
+    fwd_flops = metrics.attention_flops(pairs, h, hd)  # 4 hd per pair and head
+    algo, executed = 2.5 * fwd_flops, 3.5 * fwd_flops
+    line = {
+        "mode": "backward", "workload": wl.name, "n_tokens": n, "n_groups": m,
+        "group_sizes": counts.tolist(), "steps": args.steps, "warmup": args.warmup,
+        "backward_ms": ms, "tokens_per_s": n / (ms / 1e3),
+        "attn_bwd_tflop_algorithmic": algo / 1e12, "attn_bwd_tflop_executed": executed / 1e12,
+        "whole_backward_tflops_algorithmic": algo / (ms / 1e3) / 1e12,
+        "whole_backward_tflops_executed": executed / (ms / 1e3) / 1e12,
+        "dtype": "bf16", "data": "synthetic",
+    }
+    print(json.dumps(line), flush=True)
 
 
 def msweep(args):

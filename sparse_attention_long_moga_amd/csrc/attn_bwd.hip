@@ -14,16 +14,38 @@ namespace {
 
 constexpr float kLog2eB = 1.4426950408889634f;
 
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kValu = 0x0002 | 0x0400;  // vector ALU, transcendental included
+constexpr int kMfma = 0x0008;
+constexpr int kDsRead = 0x0100;
+#define SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
+// Copies of the per-lane LDS offsets that the compiler cannot see through.  Taken once per
+// tile, they keep each LDS address a register plus a constant that fits the instruction's
+// offset field; otherwise every (buffer, block, operand) address is hoisted out of the key
+// loop into a register of its own, which leaves too few registers to read operands ahead.
+template <int N>
+__device__ __forceinline__ void opaque_copy(const int (&src)[N], int (&dst)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        dst[i] = src[i];
+        asm volatile("" : "+v"(dst[i]));
+    }
+}
+
 // ------------------------------------------------------------------------------------- dQ
 // Item = (group, head, 128 query rows); wave w owns query rows 32w .. 32w+31 of the item.
 // Per 64-key tile: K in the A layout (S^T = K Q^T), K in the T layout (dQ^T += K^T dS^T) and
 // V in the A layout (dP^T = V dO'^T).  Q^T and dO'^T stay in registers as B operands; each
 // lane holds one query (a column of the 32x32 accumulators), so lse and D are one value per
 // lane, and the scores of a lane are 16 keys in runs of 4, the order dS^T is fed back in.
-// One wave per SIMD, like the dK/dV kernel: Q^T, dO'^T, dQ^T and two score accumulators do not
-// fit the 256 registers a wave gets when two share a SIMD.
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnBwdLaunch a) {
-    constexpr int HD = 128, NS = HD / 16, NT = HD / 32, WAVES = 4, THREADS = 64 * WAVES;
+// Eight waves (two per SIMD) share each K/V tile: a wave's Q^T, dO'^T, dQ^T and one block's
+// score accumulators fit the 256 registers it gets, so the products accumulate in ordinary
+// vector registers that the softmax reads directly, and one wave computes while the other
+// waits on LDS.
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunch a) {
+    constexpr int HD = 128, NS = HD / 16, NT = HD / 32, THREADS = 64 * WAVES;
     constexpr int BQ = 32 * WAVES;
     constexpr int ROWB = ROWB128, TILEB = KT * ROWB;
     constexpr int LOADS = TILEB / 16 / THREADS;
@@ -35,12 +57,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnBwdLaunch a) {
     const int j = lane & 31, hh = lane >> 5, s16 = lane & 15;
     const int total = uniform(a.plan.counter[1]);
     const float c = a.scale * kLog2eB;
-    int koff[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) koff[s] = a_frag_off(j, hh, s);
-    int voff[NT];
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti) voff[ti] = t_read_off(lane, ti);
+    const int kbase0 = a_frag_off(j, hh, 0), vbase0 = t_read_off(lane, 0);
     int ago[LOADS], tgo[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -103,17 +120,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnBwdLaunch a) {
             constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
             if (t + 1 < ntiles) issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
             const unsigned char *ka = lds[buf][0], *kt_ = lds[buf][1], *va = lds[buf][2];
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {  // one 32-key block at a time
-                f32x16 sacc = f32x16{}, pacc = f32x16{};
+            int k0 = kbase0, v0 = vbase0;
+            asm volatile("" : "+v"(k0), "+v"(v0));
+            // S^T and dP^T of 32-key block sb (16 products; operands read from LDS)
+            auto sdp = [&](int sb, f32x16 &sacc, f32x16 &pacc) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ka + sb * 32 * ROWB + koff[s]);
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
-                    const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(va + sb * 32 * ROWB + koff[s]);
-                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[s], pacc, 0, 0, 0);
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ka + sb * 32 * ROWB + a_frag_step(k0, s));
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s ? sacc : f32x16{}, 0, 0, 0);
+                    const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(va + sb * 32 * ROWB + a_frag_step(k0, s));
+                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[s], s ? pacc : f32x16{}, 0, 0, 0);
                 }
-                bf16x8 dsf[2];
+            };
+            // dS^T = P^T * (dP^T - D), packed to bf16 as the B operand of dQ^T += K^T dS^T
+            auto softmax = [&](int sb, const f32x16 &sacc, const f32x16 &pacc, bf16x8 (&dsf)[2]) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     float ds[8];
@@ -131,15 +151,26 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnBwdLaunch a) {
                                                     pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7]));
                     dsf[half] = __builtin_bit_cast(bf16x8, packed);
                 }
+            };
+            auto dqmm = [&](int sb, const bf16x8 (&dsf)[2]) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half)
 #pragma unroll
                     for (int ti = 0; ti < NT; ++ti) {
-                        const unsigned char *kp = kt_ + (sb * 2 + half) * 16 * ROWB + voff[ti];
+                        const unsigned char *kp = kt_ + (sb * 2 + half) * 16 * ROWB + t_read_step(v0, ti);
                         const uint2 ulo = lds_read_tr16(kp), uhi = lds_read_tr16(kp + 8 * ROWB);
                         const bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
                         dq[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dsf[half], dq[ti], 0, 0, 0);
                     }
+            };
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                f32x16 sacc, pacc;
+                bf16x8 dsf[2];
+                sdp(sb, sacc, pacc);
+                softmax(sb, sacc, pacc, dsf);
+                dqmm(sb, dsf);
+                __builtin_amdgcn_sched_barrier(0);  // no reads of the next block hoisted here
             }
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed
             __syncthreads();
@@ -151,6 +182,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnBwdLaunch a) {
             __syncthreads();
         }
         const int nfull = klen / KT;
+        // buffer indices are compile-time constants so that the compiler can tell the LDS reads
+        // of one buffer from the direct loads into the other and adds no waits between them
         using B0 = std::integral_constant<int, 0>;
         using B1 = std::integral_constant<int, 1>;
         using NoMask = std::integral_constant<bool, false>;
@@ -184,16 +217,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnBwdLaunch a) {
 }
 
 // ---------------------------------------------------------------------------------- dK, dV
-// Item = (group, head, 128 key rows); wave w owns key rows 32w .. 32w+31.  Per 64-query tile:
-// Q and dO' each in the A layout (S = Q K^T, dP = dO' V^T read them as A operands) and in the
-// T layout (dK^T += Q^T dS, dV^T += dO'^T P read them transposed), plus lse2 and D of the
-// tile's queries.  K^T and V^T stay in registers as B operands; each lane holds one key (a
-// column of the 32x32 accumulators) and 16 query rows in runs of 4, so P and dS are fed back
-// as B operands directly.  One wave per SIMD: the two accumulators take 128 registers, so the
-// kernel uses the accumulation registers as well.
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) {
-    constexpr int HD = 128, NS = HD / 16, NT = HD / 32, WAVES = 4, THREADS = 64 * WAVES;
-    constexpr int BK = 32 * WAVES;
+// Item = (group, head, 128 key rows).  Eight waves; waves w and w + 4 share a SIMD and own the
+// same 32 key rows (32 (w & 3) .. + 31): wave w computes their dV, wave w + 4 their dK.  Per
+// 64-query tile: Q and dO' each in the A layout (S = Q K^T, dP = dO' V^T read them as A
+// operands) and in the T layout (dK^T += Q^T dS, dV^T += dO'^T P read them transposed), plus
+// lse2 and D of the tile's queries.  K^T (and, in dK waves, V^T) stay in registers as B
+// operands; each lane holds one key (a column of the 32x32 accumulators) and 16 query rows in
+// runs of 4, so P and dS are fed back as B operands directly.  Both roles compute S: that is
+// a quarter more matrix work than one wave doing both, but each role fits the 256 registers
+// of a wave that shares its SIMD with another, which the fused form (two 64-register
+// accumulators and both operand sets) does not.
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) {
+    constexpr int HD = 128, NS = HD / 16, NT = HD / 32, WAVES = 8, THREADS = 64 * WAVES;
+    constexpr int BK = 128;
     constexpr int ROWB = ROWB128, TILEB = KT * ROWB;
     constexpr int LOADS = TILEB / 16 / THREADS;
     static_assert(LOADS * THREADS * 16 == TILEB, "tile must split into whole wave loads");
@@ -202,15 +238,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
     __shared__ int s_item;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool dk_role = wave >= 4;  // uniform per wave
+    const int kw = wave & 3;
     const int j = lane & 31, hh = lane >> 5, s16 = lane & 15;
     const int total = uniform(a.plan.counter[1]);
     const float c = a.scale * kLog2eB;
-    int koff[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) koff[s] = a_frag_off(j, hh, s);
-    int voff[NT];
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti) voff[ti] = t_read_off(lane, ti);
+    const int kbase0 = a_frag_off(j, hh, 0), vbase0 = t_read_off(lane, 0);
     int ago[LOADS], tgo[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -230,18 +263,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
         const int rb = uniform((int)clamp64(a.cu[seg], 0, a.len));
         const int re = uniform((int)clamp64(a.cu[seg + 1], rb, a.len));
         const int qlen = re - rb;
-        const int krow = rb + kt * BK + wave * 32 + j;
+        const int krow = rb + kt * BK + kw * 32 + j;
         const bool kvalid = krow < re;
         const int krow_c = kvalid ? krow : re - 1;
         const int64_t hrow = (int64_t)h * a.len;
+        // B operands: K^T for both roles, V^T for dK waves
         bf16x8 kf[NS], vf[NS];
         {
             const bf16 *kp = a.k + (hrow + krow_c) * HD + 8 * hh;
             const bf16 *vp = a.v + (hrow + krow_c) * HD + 8 * hh;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                kf[s] = *reinterpret_cast<const bf16x8 *>(kp + 16 * s);
-                vf[s] = *reinterpret_cast<const bf16x8 *>(vp + 16 * s);
+            for (int s = 0; s < NS; ++s) kf[s] = *reinterpret_cast<const bf16x8 *>(kp + 16 * s);
+            if (dk_role) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) vf[s] = *reinterpret_cast<const bf16x8 *>(vp + 16 * s);
             }
         }
         const bf16 *qbase = a.q + hrow * HD, *gbase = a.dov + hrow * HD;
@@ -271,9 +306,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
             }
         };
 
-        f32x16 dk[NT], dv[NT];
+        f32x16 acc[NT];  // dV^T or dK^T of the wave's 32 keys
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti) { dk[ti] = f32x16{}; dv[ti] = f32x16{}; }
+        for (int ti = 0; ti < NT; ++ti) acc[ti] = f32x16{};
 
         auto tile = [&](auto bufc, auto maskc, int t) {
             constexpr int buf = decltype(bufc)::value;
@@ -281,61 +316,88 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
             if (t + 1 < ntiles) issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
             const unsigned char *qa = lds[buf][0], *qt_ = lds[buf][1];
             const unsigned char *ga = lds[buf][2], *gt_ = lds[buf][3];
+            int k0 = kbase0, v0 = vbase0;
+            asm volatile("" : "+v"(k0), "+v"(v0));
+            // P (and dS) of the 16 query rows of this lane in block qb: rows qb*32 + 8*kq +
+            // 4*hh + e, kq < 4, e < 4; the 8 values of half `half` are kq = 2*half, 2*half + 1
+            auto probs = [&](int qb, int half, const f32x16 &sacc, float (&pv)[8]) {
+                float4 l4[2];
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                f32x16 sacc = f32x16{}, pacc = f32x16{};
+                for (int k2 = 0; k2 < 2; ++k2)
+                    l4[k2] = *reinterpret_cast<const float4 *>(
+                        &rowv[buf][0][qb * 32 + 8 * (2 * half + k2) + 4 * hh]);
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(qa + qb * 32 * ROWB + koff[s]);
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[s], sacc, 0, 0, 0);
-                    const bf16x8 gf = *reinterpret_cast<const bf16x8 *>(ga + qb * 32 * ROWB + koff[s]);
-                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, vf[s], pacc, 0, 0, 0);
+                for (int e = 0; e < 8; ++e) {
+                    const int v = half * 8 + e;
+                    float p = __builtin_amdgcn_exp2f(
+                        __builtin_fmaf(sacc[v], c, -(&l4[e >> 2].x)[v & 3]));
+                    if constexpr (MASK) {
+                        const int q = t * KT + qb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+                        if (q >= qlen) p = 0.0f;
+                    }
+                    pv[e] = p;
                 }
-                // the 16 query rows of this lane: qb*32 + 8*kq + 4*hh + e, kq < 4, e < 4
-                bf16x8 pf[2], dsf[2];
+            };
+            auto pack8 = [](const float (&x)[8]) {
+                return __builtin_bit_cast(
+                    bf16x8, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
+            };
+            // acc^T += X^T B for the 16-query chunk ch of the tile, X in the T layout at xt
+            auto accumulate = [&](const unsigned char *xt, int ch, const bf16x8 &bop) {
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    float pv[8], ds[8];
-                    float4 l4[2], d4[2];
-#pragma unroll
-                    for (int k2 = 0; k2 < 2; ++k2) {
-                        const int row = qb * 32 + 8 * (2 * half + k2) + 4 * hh;
-                        l4[k2] = *reinterpret_cast<const float4 *>(&rowv[buf][0][row]);
-                        d4[k2] = *reinterpret_cast<const float4 *>(&rowv[buf][1][row]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int v = half * 8 + e, kq = v >> 2;
-                        const float ls = (&l4[e >> 2].x)[v & 3], dd = (&d4[e >> 2].x)[v & 3];
-                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c, -ls));
-                        if constexpr (MASK) {
-                            const int q = t * KT + qb * 32 + 8 * kq + 4 * hh + (v & 3);
-                            if (q >= qlen) p = 0.0f;
-                        }
-                        pv[e] = p;
-                        ds[e] = p * (pacc[v] - dd);
-                    }
-                    pf[half] = __builtin_bit_cast(
-                        bf16x8, make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
-                    dsf[half] = __builtin_bit_cast(
-                        bf16x8, make_uint4(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
-                                           pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7])));
+                for (int ti = 0; ti < NT; ++ti) {
+                    const unsigned char *xp = xt + ch * 16 * ROWB + t_read_step(v0, ti);
+                    const uint2 lo = lds_read_tr16(xp), hi = lds_read_tr16(xp + 8 * ROWB);
+                    const bf16x8 xf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bop, acc[ti], 0, 0, 0);
                 }
+            };
+            if (!dk_role) {
+                // dV^T += dO'^T P
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int ch = qb * 2 + half;
+                for (int qb = 0; qb < 2; ++qb) {
+                    f32x16 sacc;
 #pragma unroll
-                    for (int ti = 0; ti < NT; ++ti) {
-                        const unsigned char *gp = gt_ + ch * 16 * ROWB + voff[ti];
-                        const uint2 glo = lds_read_tr16(gp), ghi = lds_read_tr16(gp + 8 * ROWB);
-                        const bf16x8 gT = __builtin_bit_cast(bf16x8, make_uint4(glo.x, glo.y, ghi.x, ghi.y));
-                        dv[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gT, pf[half], dv[ti], 0, 0, 0);
-                        const unsigned char *qp = qt_ + ch * 16 * ROWB + voff[ti];
-                        const uint2 qlo = lds_read_tr16(qp), qhi = lds_read_tr16(qp + 8 * ROWB);
-                        const bf16x8 qT = __builtin_bit_cast(bf16x8, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
-                        dk[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf[half], dk[ti], 0, 0, 0);
+                    for (int s = 0; s < NS; ++s) {
+                        const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(qa + qb * 32 * ROWB + a_frag_step(k0, s));
+                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[s], s ? sacc : f32x16{}, 0, 0, 0);
                     }
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        float pv[8];
+                        probs(qb, half, sacc, pv);
+                        accumulate(gt_, qb * 2 + half, pack8(pv));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                // dK^T += Q^T dS,  dS = P (dP - D)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    f32x16 sacc, pacc;
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) {
+                        const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(qa + qb * 32 * ROWB + a_frag_step(k0, s));
+                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[s], s ? sacc : f32x16{}, 0, 0, 0);
+                        const bf16x8 gf = *reinterpret_cast<const bf16x8 *>(ga + qb * 32 * ROWB + a_frag_step(k0, s));
+                        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, vf[s], s ? pacc : f32x16{}, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        float pv[8];
+                        probs(qb, half, sacc, pv);
+                        float4 d4[2];
+#pragma unroll
+                        for (int k2 = 0; k2 < 2; ++k2)
+                            d4[k2] = *reinterpret_cast<const float4 *>(
+                                &rowv[buf][1][qb * 32 + 8 * (2 * half + k2) + 4 * hh]);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            pv[e] *= pacc[half * 8 + e] - (&d4[e >> 2].x)[e & 3];
+                        accumulate(qt_, qb * 2 + half, pack8(pv));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed
@@ -348,6 +410,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
             __syncthreads();
         }
         const int nfull = qlen / KT;
+        // buffer indices are compile-time constants so that the compiler can tell the LDS reads
+        // of one buffer from the direct loads into the other and adds no waits between them
         using B0 = std::integral_constant<int, 0>;
         using B1 = std::integral_constant<int, 1>;
         using NoMask = std::integral_constant<bool, false>;
@@ -366,19 +430,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
             else tile(B0{}, Mask{}, t);
         }
         if (kvalid) {
-            bf16 *kp = a.dk + (hrow + krow) * HD + 4 * hh;
-            bf16 *vp = a.dv + (hrow + krow) * HD + 4 * hh;
+            bf16 *op = (dk_role ? a.dk : a.dv) + (hrow + krow) * HD + 4 * hh;
+            const float mul = dk_role ? a.scale : 1.0f;
 #pragma unroll
             for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
                 for (int kq = 0; kq < 4; ++kq) {
-                    const uint2 wk = make_uint2(
-                        pack_bf16x2(dk[ti][kq * 4 + 0] * a.scale, dk[ti][kq * 4 + 1] * a.scale),
-                        pack_bf16x2(dk[ti][kq * 4 + 2] * a.scale, dk[ti][kq * 4 + 3] * a.scale));
-                    *reinterpret_cast<uint2 *>(kp + 32 * ti + 8 * kq) = wk;
-                    const uint2 wv = make_uint2(pack_bf16x2(dv[ti][kq * 4 + 0], dv[ti][kq * 4 + 1]),
-                                                pack_bf16x2(dv[ti][kq * 4 + 2], dv[ti][kq * 4 + 3]));
-                    *reinterpret_cast<uint2 *>(vp + 32 * ti + 8 * kq) = wv;
+                    const uint2 w = make_uint2(
+                        pack_bf16x2(acc[ti][kq * 4 + 0] * mul, acc[ti][kq * 4 + 1] * mul),
+                        pack_bf16x2(acc[ti][kq * 4 + 2] * mul, acc[ti][kq * 4 + 3] * mul));
+                    *reinterpret_cast<uint2 *>(op + 32 * ti + 8 * kq) = w;
                 }
         }
     }
@@ -391,18 +452,20 @@ hipError_t launch_attention_bwd(const AttnBwdLaunch &a, hipStream_t s) {
     int cus = 0;
     hipError_t e = device_cus(&cus);
     if (e != hipSuccess) return e;
-    // dQ: items of 128 query rows, inner loop over the group's keys
-    if ((e = launch_attn_plan(a.cu, a.cu, a.n_seg, a.len, a.len, a.n_heads, 128, a.max_items,
-                              a.plan, s)) != hipSuccess)
+    // dQ: items of 256 query rows, inner loop over the group's keys
+    constexpr int kDqWaves = 8;
+    if ((e = launch_attn_plan(a.cu, a.cu, a.n_seg, a.len, a.len, a.n_heads, 32 * kDqWaves,
+                              a.max_items, a.plan, s)) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)cus), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<kDqWaves>, dim3((unsigned)cus), dim3(64 * kDqWaves), 0, s,
+                       a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // dK, dV: items of 128 key rows, inner loop over the group's queries (the plan is rebuilt
     // in place once the dQ kernel, earlier on the stream, is done with it)
     if ((e = launch_attn_plan(a.cu, a.cu, a.n_seg, a.len, a.len, a.n_heads, 128, a.max_items,
                               a.plan, s)) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)cus), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)cus), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
