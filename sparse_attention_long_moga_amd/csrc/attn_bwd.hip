@@ -20,18 +20,6 @@ constexpr int kMfma = 0x0008;
 constexpr int kDsRead = 0x0100;
 #define SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
-// Copies of the per-lane LDS offsets that the compiler cannot see through.  Taken once per
-// tile, they keep each LDS address a register plus a constant that fits the instruction's
-// offset field; otherwise every (buffer, block, operand) address is hoisted out of the key
-// loop into a register of its own, which leaves too few registers to read operands ahead.
-template <int N>
-__device__ __forceinline__ void opaque_copy(const int (&src)[N], int (&dst)[N]) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        dst[i] = src[i];
-        asm volatile("" : "+v"(dst[i]));
-    }
-}
 
 // ------------------------------------------------------------------------------------- dQ
 // Item = (group, head, 128 query rows); wave w owns query rows 32w .. 32w+31 of the item.
@@ -57,7 +45,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunc
     const int j = lane & 31, hh = lane >> 5, s16 = lane & 15;
     const int total = uniform(a.plan.counter[1]);
     const float c = a.scale * kLog2eB;
-    const int kbase0 = a_frag_off(j, hh, 0), vbase0 = t_read_off(lane, 0);
+    int koff[NS], voff[NT];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) koff[s] = a_frag_off(j, hh, s);
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) voff[ti] = t_read_off(lane, ti);
     int ago[LOADS], tgo[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -119,16 +111,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunc
             constexpr int buf = decltype(bufc)::value;
             constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
             if (t + 1 < ntiles) issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
-            const unsigned char *ka = lds[buf][0], *kt_ = lds[buf][1], *va = lds[buf][2];
-            int k0 = kbase0, v0 = vbase0;
-            asm volatile("" : "+v"(k0), "+v"(v0));
+            lds_cu8 *ka = lds_ptr(lds[buf][0]), *kt_ = lds_ptr(lds[buf][1]), *va = lds_ptr(lds[buf][2]);
             // S^T and dP^T of 32-key block sb (16 products; operands read from LDS)
             auto sdp = [&](int sb, f32x16 &sacc, f32x16 &pacc) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ka + sb * 32 * ROWB + a_frag_step(k0, s));
+                    const bf16x8 kf = lds_read_b128(ka + sb * 32 * ROWB + koff[s]);
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s ? sacc : f32x16{}, 0, 0, 0);
-                    const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(va + sb * 32 * ROWB + a_frag_step(k0, s));
+                    const bf16x8 vf = lds_read_b128(va + sb * 32 * ROWB + koff[s]);
                     pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[s], s ? pacc : f32x16{}, 0, 0, 0);
                 }
             };
@@ -157,7 +147,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunc
                 for (int half = 0; half < 2; ++half)
 #pragma unroll
                     for (int ti = 0; ti < NT; ++ti) {
-                        const unsigned char *kp = kt_ + (sb * 2 + half) * 16 * ROWB + t_read_step(v0, ti);
+                        lds_cu8 *kp = kt_ + (sb * 2 + half) * 16 * ROWB + voff[ti];
                         const uint2 ulo = lds_read_tr16(kp), uhi = lds_read_tr16(kp + 8 * ROWB);
                         const bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
                         dq[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dsf[half], dq[ti], 0, 0, 0);
@@ -170,7 +160,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunc
                 sdp(sb, sacc, pacc);
                 softmax(sb, sacc, pacc, dsf);
                 dqmm(sb, dsf);
-                __builtin_amdgcn_sched_barrier(0);  // no reads of the next block hoisted here
             }
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed
             __syncthreads();
@@ -218,15 +207,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunc
 
 // ---------------------------------------------------------------------------------- dK, dV
 // Item = (group, head, 128 key rows).  Eight waves; waves w and w + 4 share a SIMD and own the
-// same 32 key rows (32 (w & 3) .. + 31): wave w computes their dV, wave w + 4 their dK.  Per
-// 64-query tile: Q and dO' each in the A layout (S = Q K^T, dP = dO' V^T read them as A
-// operands) and in the T layout (dK^T += Q^T dS, dV^T += dO'^T P read them transposed), plus
-// lse2 and D of the tile's queries.  K^T (and, in dK waves, V^T) stay in registers as B
-// operands; each lane holds one key (a column of the 32x32 accumulators) and 16 query rows in
-// runs of 4, so P and dS are fed back as B operands directly.  Both roles compute S: that is
-// a quarter more matrix work than one wave doing both, but each role fits the 256 registers
-// of a wave that shares its SIMD with another, which the fused form (two 64-register
-// accumulators and both operand sets) does not.
+// same 32 key rows (32 (w & 3) .. + 31).  Per 32-query block, wave w computes S = Q K^T and
+// P, hands P (bf16, in the B-operand layout) to wave w + 4 through LDS and accumulates
+// dV^T += dO'^T P; wave w + 4 computes dP = dO' V^T, takes P after one workgroup barrier and
+// accumulates dK^T += Q^T dS with dS = P (dP - D).  Each wave issues 16 products per block
+// (the same total as one wave doing both) and holds one 64-register accumulator, so two fit
+// a SIMD.  Per 64-query tile: Q and dO' each in the A layout (read as A operands) and in the
+// T layout (read transposed), plus lse2 and D of the tile's queries.  K^T (dV waves) or V^T
+// (dK waves) stays in registers as the B operand; each lane holds one key (a column of the
+// 32x32 accumulators) and 16 query rows in runs of 4, the order P and dS are fed back in.
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) {
     constexpr int HD = 128, NS = HD / 16, NT = HD / 32, WAVES = 8, THREADS = 64 * WAVES;
     constexpr int BK = 128;
@@ -235,15 +224,22 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
     static_assert(LOADS * THREADS * 16 == TILEB, "tile must split into whole wave loads");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2][4][TILEB];  // Q_A Q_T G_A G_T
     __shared__ __attribute__((aligned(16))) float rowv[2][2][256];              // lse2, D
+    __shared__ __attribute__((aligned(16))) uint4 pbuf[2][4][2][64];            // P: [block][pair][half][lane]
     __shared__ int s_item;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool dk_role = wave >= 4;  // uniform per wave
+    // the role test reads a scalar copy (a scalar branch); addresses use `wave` itself, whose
+    // range the compiler knows, so it can tell this buffer's reads from the other's loads
+    const bool dk_role = uniform(wave) >= 4;
     const int kw = wave & 3;
     const int j = lane & 31, hh = lane >> 5, s16 = lane & 15;
     const int total = uniform(a.plan.counter[1]);
     const float c = a.scale * kLog2eB;
-    const int kbase0 = a_frag_off(j, hh, 0), vbase0 = t_read_off(lane, 0);
+    int koff[NS], voff[NT];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) koff[s] = a_frag_off(j, hh, s);
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) voff[ti] = t_read_off(lane, ti);
     int ago[LOADS], tgo[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -267,17 +263,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
         const bool kvalid = krow < re;
         const int krow_c = kvalid ? krow : re - 1;
         const int64_t hrow = (int64_t)h * a.len;
-        // B operands: K^T for both roles, V^T for dK waves
-        bf16x8 kf[NS], vf[NS];
+        // B operand: K^T in dV waves, V^T in dK waves
+        bf16x8 bf[NS];
         {
-            const bf16 *kp = a.k + (hrow + krow_c) * HD + 8 * hh;
-            const bf16 *vp = a.v + (hrow + krow_c) * HD + 8 * hh;
+            const bf16 *bp = (dk_role ? a.v : a.k) + (hrow + krow_c) * HD + 8 * hh;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) kf[s] = *reinterpret_cast<const bf16x8 *>(kp + 16 * s);
-            if (dk_role) {
-#pragma unroll
-                for (int s = 0; s < NS; ++s) vf[s] = *reinterpret_cast<const bf16x8 *>(vp + 16 * s);
-            }
+            for (int s = 0; s < NS; ++s) bf[s] = *reinterpret_cast<const bf16x8 *>(bp + 16 * s);
         }
         const bf16 *qbase = a.q + hrow * HD, *gbase = a.dov + hrow * HD;
         const int ntiles = (qlen + KT - 1) / KT;
@@ -314,10 +305,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
             constexpr int buf = decltype(bufc)::value;
             constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
             if (t + 1 < ntiles) issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
-            const unsigned char *qa = lds[buf][0], *qt_ = lds[buf][1];
-            const unsigned char *ga = lds[buf][2], *gt_ = lds[buf][3];
-            int k0 = kbase0, v0 = vbase0;
-            asm volatile("" : "+v"(k0), "+v"(v0));
+            lds_cu8 *qa = lds_ptr(lds[buf][0]), *qt_ = lds_ptr(lds[buf][1]);
+            lds_cu8 *ga = lds_ptr(lds[buf][2]), *gt_ = lds_ptr(lds[buf][3]);
             // P (and dS) of the 16 query rows of this lane in block qb: rows qb*32 + 8*kq +
             // 4*hh + e, kq < 4, e < 4; the 8 values of half `half` are kq = 2*half, 2*half + 1
             auto probs = [&](int qb, int half, const f32x16 &sacc, float (&pv)[8]) {
@@ -344,60 +333,65 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
                                        pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
             };
             // acc^T += X^T B for the 16-query chunk ch of the tile, X in the T layout at xt
-            auto accumulate = [&](const unsigned char *xt, int ch, const bf16x8 &bop) {
+            auto accumulate = [&](lds_cu8 *xt, int ch, const bf16x8 &bop) {
 #pragma unroll
                 for (int ti = 0; ti < NT; ++ti) {
-                    const unsigned char *xp = xt + ch * 16 * ROWB + t_read_step(v0, ti);
+                    lds_cu8 *xp = xt + ch * 16 * ROWB + voff[ti];
                     const uint2 lo = lds_read_tr16(xp), hi = lds_read_tr16(xp + 8 * ROWB);
                     const bf16x8 xf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
                     acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bop, acc[ti], 0, 0, 0);
                 }
             };
             if (!dk_role) {
-                // dV^T += dO'^T P
+                // S, P; P to the partner wave; dV^T += dO'^T P
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
                     f32x16 sacc;
 #pragma unroll
                     for (int s = 0; s < NS; ++s) {
-                        const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(qa + qb * 32 * ROWB + a_frag_step(k0, s));
-                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[s], s ? sacc : f32x16{}, 0, 0, 0);
+                        const bf16x8 qf = lds_read_b128(qa + qb * 32 * ROWB + koff[s]);
+                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, bf[s], s ? sacc : f32x16{}, 0, 0, 0);
                     }
+                    bf16x8 pf[2];
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         float pv[8];
                         probs(qb, half, sacc, pv);
-                        accumulate(gt_, qb * 2 + half, pack8(pv));
+                        pf[half] = pack8(pv);
+                        pbuf[qb][kw][half][lane] = __builtin_bit_cast(uint4, pf[half]);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
+                    lds_handoff_barrier();  // P of block qb is visible to the dK waves
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) accumulate(gt_, qb * 2 + half, pf[half]);
                 }
             } else {
-                // dK^T += Q^T dS,  dS = P (dP - D)
+                // dP; P from the partner wave; dS = P (dP - D); dK^T += Q^T dS
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
-                    f32x16 sacc, pacc;
+                    f32x16 pacc;
 #pragma unroll
                     for (int s = 0; s < NS; ++s) {
-                        const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(qa + qb * 32 * ROWB + a_frag_step(k0, s));
-                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[s], s ? sacc : f32x16{}, 0, 0, 0);
-                        const bf16x8 gf = *reinterpret_cast<const bf16x8 *>(ga + qb * 32 * ROWB + a_frag_step(k0, s));
-                        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, vf[s], s ? pacc : f32x16{}, 0, 0, 0);
+                        const bf16x8 gf = lds_read_b128(ga + qb * 32 * ROWB + koff[s]);
+                        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, bf[s], s ? pacc : f32x16{}, 0, 0, 0);
                     }
+                    lds_handoff_barrier();  // P of block qb is in pbuf
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
-                        float pv[8];
-                        probs(qb, half, sacc, pv);
+                        const uint4 pw = pbuf[qb][kw][half][lane];
+                        const uint32_t w4[4] = {pw.x, pw.y, pw.z, pw.w};
                         float4 d4[2];
 #pragma unroll
                         for (int k2 = 0; k2 < 2; ++k2)
                             d4[k2] = *reinterpret_cast<const float4 *>(
                                 &rowv[buf][1][qb * 32 + 8 * (2 * half + k2) + 4 * hh]);
+                        float ds[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            pv[e] *= pacc[half * 8 + e] - (&d4[e >> 2].x)[e & 3];
-                        accumulate(qt_, qb * 2 + half, pack8(pv));
+                        for (int e = 0; e < 8; ++e) {
+                            const float p = __uint_as_float(e & 1 ? (w4[e >> 1] & 0xffff0000u) : (w4[e >> 1] << 16));
+                            ds[e] = p * (pacc[half * 8 + e] - (&d4[e >> 2].x)[e & 3]);
+                        }
+                        accumulate(qt_, qb * 2 + half, pack8(ds));
                     }
-                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed

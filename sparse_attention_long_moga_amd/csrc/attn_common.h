@@ -60,6 +60,36 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// LDS reads through pointers that are in the LDS address space from the start (a cast of the
+// __shared__ array's own address, which the compiler resolves to the array): offsets added to
+// them keep their value ranges visible, and no generic-to-LDS conversion is left to emit.
+typedef __attribute__((address_space(3))) const unsigned char lds_cu8;
+__device__ __forceinline__ lds_cu8 *lds_ptr(const unsigned char *shared_array) {
+    return (lds_cu8 *)shared_array;
+}
+__device__ __forceinline__ bf16x8 lds_read_b128(lds_cu8 *p) {
+    return *(__attribute__((address_space(3))) const bf16x8 *)p;
+}
+__device__ __forceinline__ uint2 lds_read_tr16(lds_cu8 *p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Workgroup barrier for handing data between waves through LDS with ordinary LDS stores,
+// while direct-to-LDS loads of another buffer stay in flight.  Any fence would wait for those
+// loads too (they write LDS and share the vector-memory counter), so there is none: the wave's
+// own LDS stores are waited for explicitly (lgkmcnt(0)), LDS is coherent within the workgroup,
+// and the empty asm statements keep the compiler from moving memory accesses across.  Only
+// for data written with ds_write by the waves of this workgroup.
+__device__ __forceinline__ void lds_handoff_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // max(v, value of the lane 32 apart): v_permlane32_swap exchanges the upper half of one
 // operand with the lower half of the other, so with both operands v each lane sees both
 __device__ __forceinline__ float max_across_halves(float v) {
