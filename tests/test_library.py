@@ -119,3 +119,29 @@ def test_no_device_reported_as_unsupported(lib):
     p = ctypes.c_void_p(256)
     st = lib.moga_balance_loss(p, p, ctypes.byref(d), p, None, None, None)
     assert st == _capi.MOGA_ERR_UNSUPPORTED
+
+
+def test_backward_argument_checks(lib):
+    """moga_backward validates before touching a GPU: head_dim, NULL pointers, workspace."""
+    from sparse_attention_long_moga_amd._capi import MogaGrads, MogaInputs, MogaSaved
+    p = 256
+    ins = MogaInputs(p, 1, p, p, p, p, None)
+    sav = MogaSaved(p, p, p, p, p, p, p)
+    gr = MogaGrads(p, p, p, None, None, None)
+    d128 = _dims(head_dim=128)
+    ws = lib.moga_backward_workspace_bytes(ctypes.byref(d128))
+    assert ws > lib.moga_workspace_bytes(ctypes.byref(d128), None)  # seven group-order tensors
+    call = lambda d, i=ins, s=sav, g=gr, dout=p, w=ws, wsp=p: lib.moga_backward(
+        ctypes.byref(i) if i else None, ctypes.byref(s) if s else None, dout, 0.5,
+        ctypes.byref(d), ctypes.byref(g) if g else None, wsp, w, None)
+    assert call(_dims(head_dim=64)) == _capi.MOGA_ERR_UNSUPPORTED
+    assert "head_dim 128" in lib.moga_last_error().decode()
+    assert call(d128, s=None) == _capi.MOGA_ERR_ARG
+    assert call(d128, dout=None) == _capi.MOGA_ERR_ARG
+    assert call(d128, s=MogaSaved(p, p, p, p, p, p, None)) == _capi.MOGA_ERR_ARG  # no lse
+    assert "saved" in lib.moga_last_error().decode()
+    assert call(d128, g=MogaGrads(p, None, p, None, None, None)) == _capi.MOGA_ERR_ARG
+    assert call(d128, dout=258) == _capi.MOGA_ERR_ARG  # misaligned
+    assert call(d128, w=16) == _capi.MOGA_ERR_WORKSPACE
+    assert call(d128, wsp=None) == _capi.MOGA_ERR_WORKSPACE
+    assert lib.moga_backward_workspace_bytes(ctypes.byref(_dims(n_groups=0))) == 0
