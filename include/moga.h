@@ -220,8 +220,8 @@ typedef struct {
 
 typedef struct {
     void *dq, *dk, *dv;  /* required, bf16 [H][N][head_dim], token order */
-    float *dx;           /* optional [N][d_model] fp32 (for bf16 x too) */
-    float *dw;           /* optional [d_model][M] fp32 */
+    float *dx;           /* optional [N][d_model] fp32 (for bf16 x too), 16-byte aligned */
+    float *dw;           /* optional [d_model][M] fp32, 16-byte aligned */
     float *dp;           /* optional [N] fp32: dp_t above */
 } moga_grads;
 

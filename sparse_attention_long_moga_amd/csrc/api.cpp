@@ -541,6 +541,8 @@ moga_status moga_backward(const moga_inputs *in, const moga_saved *saved, const 
     const void *vec[8] = {in->q, in->k, in->v, d_out, saved->out, grads->dq, grads->dk, grads->dv};
     for (const void *p : vec)
         if (!aligned16(p)) return fail(MOGA_ERR_ARG, "q, k, v, d_out, out, dq, dk, dv must be 16-byte aligned");
+    if ((grads->dx && !aligned16(grads->dx)) || (grads->dw && !aligned16(grads->dw)))
+        return fail(MOGA_ERR_ARG, "dx and dw must be 16-byte aligned");
     if (!std::isfinite(d_loss)) return fail(MOGA_ERR_ARG, "d_loss is not finite");
     const BwdLayout B = make_bwd_layout(dims);
     if ((st = check_ws(ws, ws_bytes, B.total)) != MOGA_OK) return st;

@@ -301,7 +301,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) acc[ti] = f32x16{};
 
-        auto tile = [&](auto bufc, auto maskc, int t) {
+        auto tile = [&](auto rolec, auto bufc, auto maskc, int t) {
+            constexpr bool DK = decltype(rolec)::value;
             constexpr int buf = decltype(bufc)::value;
             constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
             if (t + 1 < ntiles) issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
                     acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bop, acc[ti], 0, 0, 0);
                 }
             };
-            if (!dk_role) {
+            if constexpr (!DK) {
                 // S, P; P to the partner wave; dV^T += dO'^T P
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
@@ -410,19 +411,25 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
         using B1 = std::integral_constant<int, 1>;
         using NoMask = std::integral_constant<bool, false>;
         using Mask = std::integral_constant<bool, true>;
-        int t = 0;
-        for (; t + 1 < nfull; t += 2) {
-            tile(B0{}, NoMask{}, t);
-            tile(B1{}, NoMask{}, t + 1);
-        }
-        if (t < nfull) {
-            tile(B0{}, NoMask{}, t);
-            ++t;
-        }
-        if (t < ntiles) {
-            if (t & 1) tile(B1{}, Mask{}, t);
-            else tile(B0{}, Mask{}, t);
-        }
+        // one copy of the tile loop per role, so that the compiler's tracking of outstanding
+        // loads never merges the two roles' paths (merged, it adds waits for loads in flight)
+        auto run = [&](auto rolec) {
+            int t = 0;
+            for (; t + 1 < nfull; t += 2) {
+                tile(rolec, B0{}, NoMask{}, t);
+                tile(rolec, B1{}, NoMask{}, t + 1);
+            }
+            if (t < nfull) {
+                tile(rolec, B0{}, NoMask{}, t);
+                ++t;
+            }
+            if (t < ntiles) {
+                if (t & 1) tile(rolec, B1{}, Mask{}, t);
+                else tile(rolec, B0{}, Mask{}, t);
+            }
+        };
+        if (dk_role) run(std::true_type{});
+        else run(std::false_type{});
         if (kvalid) {
             bf16 *op = (dk_role ? a.dk : a.dv) + (hrow + krow) * HD + 4 * hh;
             const float mul = dk_role ? a.scale : 1.0f;

@@ -64,113 +64,229 @@ __global__ __launch_bounds__(256) void bwd_gather_f32_kernel(const float *src, c
     }
 }
 
-// One wave per token: logits x_t W (fp32), softmax, dr_t, dx_t.  Lanes stride over d.
-template <int MM>
+// Router backward for the tokens of one wave: logits x_t W (fp32), softmax, dr_t, dx_t.  A wave
+// takes TPW tokens at once so that each weight it loads serves all of them; lane l handles the
+// CPL consecutive columns CPL*l, CPL*l + 64*CPL, ... (16-byte loads of x, 16-byte stores of dx);
+// the column sums are reduced over the wave with butterfly shuffles in a fixed order.
+template <int MM, bool XB, bool WL>
 __global__ __launch_bounds__(256) void bwd_router_rows_kernel(BwdRouterLaunch a) {
+    // WL: the block first copies W ([d][m] fp32) into LDS and reads it from there
+    extern __shared__ __attribute__((aligned(16))) float wsh[];
+    constexpr int TPW = MM <= 16 ? 4 : 1;
+    constexpr int CPL = XB ? 8 : 4, STRIDE = 64 * CPL;
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= a.n) return;
     const int d = a.d, m = a.m;
-    float r[MM];
+    const float *w = a.w;
+    if constexpr (WL) {
+        const int nw = d * m;  // w carries no alignment promise: element-wise copy
+        for (int k = threadIdx.x; k < nw; k += 256) wsh[k] = a.w[k];
+        __syncthreads();
+        w = wsh;
+    }
+    const int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
+    if (t0 >= a.n) return;
+    const int nt = (int)min((int64_t)TPW, a.n - t0);
+    float r[TPW][MM];
 #pragma unroll
-    for (int i = 0; i < MM; ++i) r[i] = 0.0f;
-    for (int c = lane; c < d; c += 64) {
-        const float xv = a.x_is_bf16 ? (float)static_cast<const bf16 *>(a.x)[t * d + c]
-                                     : static_cast<const float *>(a.x)[t * d + c];
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int i = 0; i < MM; ++i) r[tt][i] = 0.0f;
+    for (int c0 = CPL * lane; c0 < d; c0 += STRIDE) {  // d is a multiple of CPL
+        float xv[TPW][CPL];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int64_t row = t0 + min(tt, nt - 1);  // rows past the end repeat the last one
+            if constexpr (XB) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(a.x) + row * d + c0);
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    xv[tt][2 * q] = bf16_lo(w4[q]);
+                    xv[tt][2 * q + 1] = bf16_hi(w4[q]);
+                }
+            } else {
+                const float4 f = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + row * d + c0);
+                xv[tt][0] = f.x; xv[tt][1] = f.y; xv[tt][2] = f.z; xv[tt][3] = f.w;
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const float *wr = w + (c0 + cc) * m;
+#pragma unroll
+            for (int i = 0; i < MM; ++i)
+                if (i < m) {
+                    const float wv = wr[i];
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt) r[tt][i] = __builtin_fmaf(xv[tt][cc], wv, r[tt][i]);
+                }
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
         for (int i = 0; i < MM; ++i)
-            if (i < m) r[i] = __builtin_fmaf(xv, a.w[(int64_t)c * m + i], r[i]);
+            if (i < m) {
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) r[tt][i] += __shfl_xor(r[tt][i], off, 64);
+            }
+    // softmax and its backward, per token (every lane holds every logit)
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        if (tt >= nt) break;
+        const int64_t t = t0 + tt;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < MM; ++i)
+            if (i < m) mx = fmaxf(mx, r[tt][i]);
+        float z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < MM; ++i)
+            if (i < m) { r[tt][i] = __expf(r[tt][i] - mx); z += r[tt][i]; }
+        const int g = a.group_id[t];
+        const float dp = a.dp[t];
+        float dot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < MM; ++i)
+            if (i < m) {
+                r[tt][i] /= z;  // p_ti
+                const float ai = (i == g ? dp : 0.0f) + a.loss_coef * (float)a.counts[i];
+                dot += ai * r[tt][i];
+            }
+#pragma unroll
+        for (int i = 0; i < MM; ++i)
+            if (i < m) {
+                const float ai = (i == g ? dp : 0.0f) + a.loss_coef * (float)a.counts[i];
+                r[tt][i] = r[tt][i] * (ai - dot);  // dr_ti
+                if (lane == 0) a.dr[t * m + i] = r[tt][i];
+            }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < MM; ++i) {
-        if (i < m) {
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) r[i] += __shfl_xor(r[i], off, 64);
-            mx = fmaxf(mx, r[i]);
-        }
-    }
-    float z = 0.0f;
-#pragma unroll
-    for (int i = 0; i < MM; ++i)
-        if (i < m) { r[i] = __expf(r[i] - mx); z += r[i]; }
-    const int g = a.group_id[t];
-    const float dp = a.dp[t];
-    float dot = 0.0f;
-#pragma unroll
-    for (int i = 0; i < MM; ++i)
-        if (i < m) {
-            r[i] /= z;  // p_ti
-            const float ai = (i == g ? dp : 0.0f) + a.loss_coef * (float)a.counts[i];
-            dot += ai * r[i];
-        }
-#pragma unroll
-    for (int i = 0; i < MM; ++i)
-        if (i < m) {
-            const float ai = (i == g ? dp : 0.0f) + a.loss_coef * (float)a.counts[i];
-            r[i] = r[i] * (ai - dot);  // dr_ti
-            if (lane == 0) a.dr[t * m + i] = r[i];
-        }
     if (!a.dx) return;
-    for (int c = lane; c < d; c += 64) {
-        float acc = 0.0f;
+    for (int c0 = CPL * lane; c0 < d; c0 += STRIDE) {
+        float acc[TPW][CPL];
 #pragma unroll
-        for (int i = 0; i < MM; ++i)
-            if (i < m) acc = __builtin_fmaf(r[i], a.w[(int64_t)c * m + i], acc);
-        a.dx[t * d + c] = acc;
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) acc[tt][cc] = 0.0f;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const float *wr = w + (c0 + cc) * m;
+#pragma unroll
+            for (int i = 0; i < MM; ++i)
+                if (i < m) {
+                    const float wv = wr[i];
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt) acc[tt][cc] = __builtin_fmaf(r[tt][i], wv, acc[tt][cc]);
+                }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+            if (tt < nt) {
+                float *dst = a.dx + (t0 + tt) * d + c0;
+#pragma unroll
+                for (int q = 0; q < CPL / 4; ++q)
+                    *reinterpret_cast<float4 *>(dst + 4 * q) =
+                        make_float4(acc[tt][4 * q], acc[tt][4 * q + 1], acc[tt][4 * q + 2], acc[tt][4 * q + 3]);
+            }
     }
 }
 
-// dW partials: block (chunk of tokens, 256 columns); thread c sums x[t][c] dr[t][i] over the
-// chunk's tokens in token order for all i < m.
-constexpr int kDwChunk = 1024;
+// dW partials: block (chunk of tokens, 256 * CPT columns); thread k sums x[t][c] dr[t][i] over
+// the chunk's tokens in token order for its CPT consecutive columns c and all i < m.  The dr
+// values of a token are the same for every thread of the block.
+constexpr int kDwChunk = 256;
 
-template <int MM>
+template <int MM, bool XB>
 __global__ __launch_bounds__(256) void bwd_router_dw_kernel(BwdRouterLaunch a) {
-    const int c = blockIdx.y * 256 + threadIdx.x;
+    constexpr int CPT = MM <= 8 ? (XB ? 8 : 4) : (MM <= 16 ? 4 : (MM <= 32 ? 2 : 1));
+    const int c0 = (blockIdx.y * 256 + threadIdx.x) * CPT;
     const int64_t t0 = (int64_t)blockIdx.x * kDwChunk;
     const int64_t t1 = std::min<int64_t>(t0 + kDwChunk, a.n);
     const int d = a.d, m = a.m;
-    float acc[MM];
+    float acc[CPT][MM];
 #pragma unroll
-    for (int i = 0; i < MM; ++i) acc[i] = 0.0f;
-    if (c < d) {
+    for (int cc = 0; cc < CPT; ++cc)
+#pragma unroll
+        for (int i = 0; i < MM; ++i) acc[cc][i] = 0.0f;
+    if (c0 < d) {  // d is a multiple of CPT (of 8 for bf16 x, of 4 for fp32 x)
         for (int64_t t = t0; t < t1; ++t) {
-            const float xv = a.x_is_bf16 ? (float)static_cast<const bf16 *>(a.x)[t * d + c]
-                                         : static_cast<const float *>(a.x)[t * d + c];
+            float xv[CPT];
+            if constexpr (XB) {
+                const bf16 *xp = static_cast<const bf16 *>(a.x) + t * d + c0;
+                if constexpr (CPT == 8) {
+                    const uint4 u = *reinterpret_cast<const uint4 *>(xp);
+                    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) { xv[2 * q] = bf16_lo(w4[q]); xv[2 * q + 1] = bf16_hi(w4[q]); }
+                } else {
+#pragma unroll
+                    for (int cc = 0; cc < CPT; ++cc) xv[cc] = (float)xp[cc];
+                }
+            } else {
+                const float *xp = static_cast<const float *>(a.x) + t * d + c0;
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) xv[cc] = xp[cc];
+            }
+            const float *drt = a.dr + t * m;
 #pragma unroll
             for (int i = 0; i < MM; ++i)
-                if (i < m) acc[i] = __builtin_fmaf(xv, a.dr[t * m + i], acc[i]);
+                if (i < m) {
+                    const float dv = drt[i];
+#pragma unroll
+                    for (int cc = 0; cc < CPT; ++cc) acc[cc][i] = __builtin_fmaf(xv[cc], dv, acc[cc][i]);
+                }
         }
 #pragma unroll
-        for (int i = 0; i < MM; ++i)
-            if (i < m) a.dw_part[((int64_t)blockIdx.x * d + c) * m + i] = acc[i];
+        for (int cc = 0; cc < CPT; ++cc)
+#pragma unroll
+            for (int i = 0; i < MM; ++i)
+                if (i < m) a.dw_part[((int64_t)blockIdx.x * d + c0 + cc) * m + i] = acc[cc][i];
     }
 }
 
-__global__ __launch_bounds__(256) void bwd_router_dw_sum_kernel(const float *part, int64_t nchunk,
-                                                                 int64_t dm, float *dw) {
-    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// dW = sum of the chunk partials: eight running sums over chunks b = 8q + u, added in a fixed
+// order at the end (the result is reproducible; eight loads are in flight per thread)
+__global__ __launch_bounds__(64) void bwd_router_dw_sum_kernel(const float *part, int64_t nchunk,
+                                                                int64_t dm, float *dw) {
+    const int64_t k = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (k >= dm) return;
-    float s = 0.0f;
-    for (int64_t b = 0; b < nchunk; ++b) s += part[b * dm + k];
-    dw[k] = s;
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    int64_t b = 0;
+    for (; b + 8 <= nchunk; b += 8)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] += part[(b + u) * dm + k];
+    for (int u = 0; b + u < nchunk; ++u) acc[u] += part[(b + u) * dm + k];
+    dw[k] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
 
-template <int MM>
+template <int MM, bool XB>
 hipError_t launch_router_bwd_mm(const BwdRouterLaunch &a, hipStream_t s) {
-    hipLaunchKernelGGL((bwd_router_rows_kernel<MM>), dim3((unsigned)((a.n + 3) / 4)), dim3(256), 0,
-                       s, a);
+    constexpr int TPW = MM <= 16 ? 4 : 1;
+    const int64_t waves = (a.n + TPW - 1) / TPW;
+    const size_t wbytes = sizeof(float) * (size_t)a.d * a.m;
+    if (wbytes <= 48 * 1024)
+        hipLaunchKernelGGL((bwd_router_rows_kernel<MM, XB, true>), dim3((unsigned)((waves + 3) / 4)),
+                           dim3(256), wbytes, s, a);
+    else
+        hipLaunchKernelGGL((bwd_router_rows_kernel<MM, XB, false>), dim3((unsigned)((waves + 3) / 4)),
+                           dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.dw) return e;
+    constexpr int CPT = MM <= 8 ? (XB ? 8 : 4) : (MM <= 16 ? 4 : (MM <= 32 ? 2 : 1));
     const int64_t nchunk = bwd_dw_chunks(a.n);
-    hipLaunchKernelGGL((bwd_router_dw_kernel<MM>), dim3((unsigned)nchunk, (unsigned)((a.d + 255) / 256)),
+    const int cols_per_block = 256 * CPT;
+    hipLaunchKernelGGL((bwd_router_dw_kernel<MM, XB>),
+                       dim3((unsigned)nchunk, (unsigned)((a.d + cols_per_block - 1) / cols_per_block)),
                        dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t dm = (int64_t)a.d * a.m;
-    hipLaunchKernelGGL(bwd_router_dw_sum_kernel, dim3((unsigned)((dm + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(bwd_router_dw_sum_kernel, dim3((unsigned)((dm + 63) / 64)), dim3(64), 0, s,
                        a.dw_part, nchunk, dm, a.dw);
     return hipGetLastError();
+}
+
+template <int MM>
+hipError_t launch_router_bwd_x(const BwdRouterLaunch &a, hipStream_t s) {
+    return a.x_is_bf16 ? launch_router_bwd_mm<MM, true>(a, s) : launch_router_bwd_mm<MM, false>(a, s);
 }
 
 }  // namespace
@@ -199,11 +315,11 @@ hipError_t launch_bwd_gather_f32(const float *src, const int32_t *perm, int64_t 
 }
 
 hipError_t launch_router_bwd(const BwdRouterLaunch &a, hipStream_t s) {
-    if (a.m <= 4) return launch_router_bwd_mm<4>(a, s);
-    if (a.m <= 8) return launch_router_bwd_mm<8>(a, s);
-    if (a.m <= 16) return launch_router_bwd_mm<16>(a, s);
-    if (a.m <= 32) return launch_router_bwd_mm<32>(a, s);
-    return launch_router_bwd_mm<64>(a, s);
+    if (a.m <= 4) return launch_router_bwd_x<4>(a, s);
+    if (a.m <= 8) return launch_router_bwd_x<8>(a, s);
+    if (a.m <= 16) return launch_router_bwd_x<16>(a, s);
+    if (a.m <= 32) return launch_router_bwd_x<32>(a, s);
+    return launch_router_bwd_x<64>(a, s);
 }
 
 }  // namespace moga
