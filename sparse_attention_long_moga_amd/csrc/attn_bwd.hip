@@ -344,7 +344,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
                 }
             };
             if constexpr (!DK) {
-                // S, P; P to the partner wave; dV^T += dO'^T P
+                // S, P of both 32-query blocks; P to the partner wave; dV^T += dO'^T P
+                bf16x8 pf[2][2];
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
                     f32x16 sacc;
@@ -353,29 +354,32 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
                         const bf16x8 qf = lds_read_b128(qa + qb * 32 * ROWB + koff[s]);
                         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, bf[s], s ? sacc : f32x16{}, 0, 0, 0);
                     }
-                    bf16x8 pf[2];
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         float pv[8];
                         probs(qb, half, sacc, pv);
-                        pf[half] = pack8(pv);
-                        pbuf[qb][kw][half][lane] = __builtin_bit_cast(uint4, pf[half]);
+                        pf[qb][half] = pack8(pv);
+                        pbuf[qb][kw][half][lane] = __builtin_bit_cast(uint4, pf[qb][half]);
                     }
-                    lds_handoff_barrier();  // P of block qb is visible to the dK waves
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) accumulate(gt_, qb * 2 + half, pf[half]);
                 }
-            } else {
-                // dP; P from the partner wave; dS = P (dP - D); dK^T += Q^T dS
+                lds_handoff_barrier();  // P of the tile is visible to the dK waves
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    f32x16 pacc;
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) accumulate(gt_, qb * 2 + half, pf[qb][half]);
+            } else {
+                // dP of both blocks; P from the partner wave; dS = P (dP - D); dK^T += Q^T dS
+                f32x16 pacc[2];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                     for (int s = 0; s < NS; ++s) {
                         const bf16x8 gf = lds_read_b128(ga + qb * 32 * ROWB + koff[s]);
-                        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, bf[s], s ? pacc : f32x16{}, 0, 0, 0);
+                        pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, bf[s], s ? pacc[qb] : f32x16{}, 0, 0, 0);
                     }
-                    lds_handoff_barrier();  // P of block qb is in pbuf
+                lds_handoff_barrier();  // P of the tile is in pbuf
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         const uint4 pw = pbuf[qb][kw][half][lane];
@@ -389,11 +393,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const float p = __uint_as_float(e & 1 ? (w4[e >> 1] & 0xffff0000u) : (w4[e >> 1] << 16));
-                            ds[e] = p * (pacc[half * 8 + e] - (&d4[e >> 2].x)[e & 3]);
+                            ds[e] = p * (pacc[qb][half * 8 + e] - (&d4[e >> 2].x)[e & 3]);
                         }
                         accumulate(qt_, qb * 2 + half, pack8(ds));
                     }
-                }
             }
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed
             __syncthreads();
