@@ -14,11 +14,6 @@ namespace {
 
 constexpr float kLog2eB = 1.4426950408889634f;
 
-// instruction classes of __builtin_amdgcn_sched_group_barrier
-constexpr int kValu = 0x0002 | 0x0400;  // vector ALU, transcendental included
-constexpr int kMfma = 0x0008;
-constexpr int kDsRead = 0x0100;
-#define SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 
 // ------------------------------------------------------------------------------------- dQ

@@ -117,12 +117,6 @@ __device__ __forceinline__ int t_read_off(int lane, int ti) {
     return (4 * (g >> 1) + (s16 >> 2)) * ROWB128 +
            ((((ti ^ (s16 >> 2)) << 2) + 2 * (g & 1) + ((s16 & 3) >> 1)) << 4) + (s16 & 1) * 8;
 }
-// The swizzles keep the step- and block-dependent bits apart from the rest, so that
-//   a_frag_off(j, hh, s) == a_frag_off(j, hh, 0) ^ (32 * s)   and
-//   t_read_off(lane, ti) == t_read_off(lane, 0) ^ (ti << 6):
-// one base register per lane and an XOR with a constant per read.
-__device__ __forceinline__ int a_frag_step(int base, int s) { return base ^ (32 * s); }
-__device__ __forceinline__ int t_read_step(int base, int ti) { return base ^ (ti << 6); }
 // byte offset within a global row of the 16-byte chunk that lands in LDS chunk s16 of row r
 __device__ __forceinline__ int a_dma_chunk(int r, int s16) { return (s16 ^ (r & 15)) << 4; }
 __device__ __forceinline__ int t_dma_chunk(int r, int s16) { return (s16 ^ (4 * (r & 3))) << 4; }
