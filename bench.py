@@ -32,7 +32,7 @@ METRIC = "MoGA fwd tokens/s + group-attn TFLOP/s (% bf16 MFMA peak) at N=282k, M
 # plain 1 GiB device copy (FETCH 2.0x, WRITE 1.0x); the summary with the commands is under
 # profiles/.  The figure belongs to one version of the kernel source: any other attn.hip
 # reports null until the counters are taken again.
-ATTN_TRAFFIC = {"bytes": 10_322_720 * 1024 * 2 + 848_048 * 1024, "attn_hip_sha256_16": "2210d8d379111dcd"}
+ATTN_TRAFFIC = {"bytes": 10_434_186 * 1024 * 2 + 848_020 * 1024, "attn_hip_sha256_16": "dcc89d089b4108cb"}
 
 
 def attn_traffic_bytes():
