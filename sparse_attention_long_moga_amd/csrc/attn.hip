@@ -206,7 +206,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel(AttnLaunch 
             const int key0 = t * KT;
             if constexpr (!IDX) {
                 // rows [kb + key0, ke) of this head; rows past ke read as zeros
-                const uint32_t bytes = (uint32_t)min(max(klen - key0, 0), KT) * HD * 2;  // one tile at most
+                // one tile at most; readfirstlane keeps the count (and so the descriptor) in scalar
+                // registers: the compiler clamps with a vector instruction, and a descriptor in
+                // vector registers costs a waterfall loop around every load
+                const uint32_t bytes = (uint32_t)uniform(min(max(klen - key0, 0), KT)) * HD * 2;
                 const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)(kb + key0) * HD, bytes);
                 const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)(kb + key0) * HD, bytes);
 #pragma unroll
@@ -483,7 +486,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
             constexpr int buf = decltype(bufc)::value;
             const int key0 = t * KT;
             if constexpr (!IDX) {
-                const uint32_t bytes = (uint32_t)min(max(klen - key0, 0), KT) * ROWB;  // one tile at most
+                // one tile at most, kept scalar (see the generic kernel)
+                const uint32_t bytes = (uint32_t)uniform(min(max(klen - key0, 0), KT)) * ROWB;
                 const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)(kb + key0) * HD, bytes);
                 const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)(kb + key0) * HD, bytes);
 #pragma unroll

@@ -86,7 +86,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunc
         auto issue = [&](auto bufc, int t) {
             constexpr int buf = decltype(bufc)::value;
             const int key0 = t * KT;
-            const uint32_t bytes = (uint32_t)min(max(klen - key0, 0), KT) * ROWB;  // one tile at most
+            // one tile at most; readfirstlane keeps the count (and so the descriptor) scalar
+            const uint32_t bytes = (uint32_t)uniform(min(max(klen - key0, 0), KT)) * ROWB;
             const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)(rb + key0) * HD, bytes);
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)(rb + key0) * HD, bytes);
 #pragma unroll
@@ -272,7 +273,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
         auto issue = [&](auto bufc, int t) {
             constexpr int buf = decltype(bufc)::value;
             const int q0 = t * KT;
-            const uint32_t bytes = (uint32_t)min(max(qlen - q0, 0), KT) * ROWB;  // one tile at most
+            // one tile at most; readfirstlane keeps the count (and so the descriptor) scalar
+            const uint32_t bytes = (uint32_t)uniform(min(max(qlen - q0, 0), KT)) * ROWB;
             const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (int64_t)(rb + q0) * HD, bytes);
             const __amdgpu_buffer_rsrc_t rg = make_rsrc(gbase + (int64_t)(rb + q0) * HD, bytes);
 #pragma unroll
@@ -284,7 +286,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
                 load_lds16(rg, &lds[buf][3][slot], tgo[i]);
             }
             if (wave == 0) {  // lse2 and D of the tile's queries (256 entries; 64 are used)
-                const uint32_t rbytes = (uint32_t)min(max(qlen - q0, 0), 256) * 4;  // what one load reads
+                // what one load reads, kept scalar
+                const uint32_t rbytes = (uint32_t)uniform(min(max(qlen - q0, 0), 256)) * 4;
                 const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse2 + hrow + rb + q0, rbytes);
                 const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.D + hrow + rb + q0, rbytes);
                 load_lds16(rl, reinterpret_cast<unsigned char *>(&rowv[buf][0][0]), 16 * lane);

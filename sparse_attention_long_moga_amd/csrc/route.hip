@@ -6,10 +6,12 @@
 // exactly into three bf16 terms, w = w1 + w2 + w3 (w1 = bf16(w), w2 = bf16(w - w1),
 // w3 = w - w1 - w2, which needs at most 8 significant bits): every product x*w_j is exact
 // in fp32 and the MFMA accumulates in fp32, so the logits carry fp32 accuracy.  One
-// 16x16x32 MFMA takes 16 groups (A, from the split W) against 16 tokens (B, one 16-byte
-// load of x per lane), so each logit's reduction over d happens inside the matrix core and
-// only the softmax needs two cross-lane steps.  Each wave owns a contiguous run of token
-// tiles (a balanced static split), so the group statistics are summed in a fixed order.
+// 16x16x32 MFMA takes 16 groups (A, from the split W) against 16 tokens (B), so each logit's
+// reduction over d happens inside the matrix core and only the softmax needs two cross-lane
+// steps.  route_stage_kernel (m <= 16, W image within 64 KiB) reads x rows in whole-row
+// pieces and transposes them through LDS; route_mfma_kernel (larger m * d) loads the B
+// operand straight from memory and streams W from L2.  Group statistics are written per
+// wave or per work item and summed in a fixed order, so they are bitwise reproducible.
 //
 // fp32 x: VALU pass.  Each wave streams TPW token rows at a time with 16-byte coalesced
 // loads (lane l holds columns [VEC*l, VEC*l+VEC) of every 64*VEC-wide stripe), multiplies
@@ -177,6 +179,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// a value the caller knows to be the same in every lane, made visibly so to the compiler
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // wf[j][mt][s][lane] = 8 bf16: term j of W[32s + 8(lane/16) + i][16mt + lane%16], i < 8
 // (zero outside d x m): the A operand of a 16x16x32 MFMA for group tile mt, k-step s.
@@ -436,141 +441,281 @@ void route_mfma_kernel(RouteLaunch a, const bf16x8 *wf,
     }
 }
 
-// W resident in LDS.  When the three bf16 terms of W fit (3 * m * row bytes <= kRouteLdsW),
-// every persistent block splits W once into LDS, [term][group][k] with rows padded to whole
-// k-steps (zeros past d).  The A fragments then come from LDS just before their MFMAs, on
-// the LDS counter, so the x loads can run DX k-steps ahead in a ring of registers without
-// W loads queued behind them (global loads complete in issue order).  m <= 16.
+// The three-term W image held in LDS by route_stage_kernel: at most kRouteLdsW bytes.
 constexpr int kRouteLdsW = 64 * 1024;
 
-inline int route_lds_row_bytes(int d) { return ((d + 31) / 32) * 64 + 64; }
+// Row stride of the W image: whole k-steps plus 16 bytes, an odd number of 16-byte chunks,
+// so the 16 group rows that one k-slice read touches start in 16 different LDS bank groups.
+__host__ __device__ inline int route_stage_row_bytes(int d) { return ((d + 31) / 32) * 64 + 16; }
 
-// The LDS image of W, built once per call: term j of W[k][g] at byte (j*m + g)*rs + 2k, zeros
-// for k >= d, then one zero row.  One thread per (k, g) pair and one per zero-row chunk.
-__global__ __launch_bounds__(256) void route_image_kernel(const float *w, int d, int m, int kp,
-                                                          int rs, char *img) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t pairs = (int64_t)kp * m;
-    if (idx < pairs) {
-        const int k = (int)(idx / m), g = (int)(idx - (int64_t)k * m);
-        const float v = k < d ? w[idx] : 0.0f;  // w[k*m + g]
-        const bf16 h = (bf16)v;
-        const float r1 = v - (float)h;  // exact
-        const bf16 md = (bf16)r1;
-        const float r2 = r1 - (float)md;  // exact, at most 8 significant bits
-        *reinterpret_cast<bf16 *>(img + (int64_t)g * rs + 2 * k) = h;
-        *reinterpret_cast<bf16 *>(img + (int64_t)(m + g) * rs + 2 * k) = md;
-        *reinterpret_cast<bf16 *>(img + (int64_t)(2 * m + g) * rs + 2 * k) = (bf16)r2;
-    } else if (idx < pairs + rs / 16) {
-        *reinterpret_cast<u32x4 *>(img + (int64_t)3 * m * rs + 16 * (idx - pairs)) =
-            u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-template <int T, int DX, int NT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 512 ? 4 : 3)))
-void route_lds_kernel(RouteLaunch a, const char *img, int lds_bytes, int *queue) {
-    extern __shared__ __attribute__((aligned(16))) char wsm[];  // [3][m][rs] bf16, zero row
+// Row-contiguous reads for the matrix cores (bf16 x, m <= 16, the three-term W image of at
+// most kRouteLdsW bytes).  A load instruction in the MFMA operand layout covers 16 rows x 64
+// bytes, which streams from HBM at about half the rate of whole-row reads; here each wave
+// instead reads UB contiguous bytes of a token row per 64/(UB/16) lanes (one instruction
+// covers 64*16/UB rows), writes them into its own LDS tile of 16 rows x UB bytes (16-byte
+// chunk c of row r at chunk position c ^ (r & 15)), and reads the B fragments of the
+// 16x16x32 MFMAs from there: the 16 lanes that read one k-slice of 16 rows hit 16 different
+// bank groups.  A unit of work is UB/2 columns of a 16-token tile; the rows of the next NH
+// units are in flight (a ring of registers) while a unit is written to LDS and multiplied.
+// A wave reads only what it wrote itself, so no barrier is needed after the W image is
+// built.  Each wave owns a contiguous, balanced range of tiles; its group statistics go to
+// row `wave` of part_p / part_c.
+template <int NW, int NH, int UB>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void route_stage_kernel(RouteLaunch a, int n_waves) {
+    constexpr int LPR = UB / 16;      // lanes per row in a load
+    constexpr int RPI = 64 / LPR;     // rows per load instruction
+    constexpr int NL = 16 / RPI;      // load instructions per unit
+    constexpr int KS = UB / 64;       // k-steps per unit
+    constexpr int UC = UB / 2;        // columns per unit
+    extern __shared__ __attribute__((aligned(16))) char smem[];  // W image, then NW x 16 UB
     const int d = a.d, m = a.m;
     const int64_t n = a.n;
-    const int steps = (d + 31) / 32, full = d / 32;
-    const int rs = steps * 64 + 64;
+    const int steps = (d + 31) / 32, units_per_tile = (d + UC - 1) / UC;
+    const int rs = route_stage_row_bytes(d);  // bytes per image row: whole k-steps + 16
+    const int img_bytes = (3 * m + 1) * rs;
+    const int img_pad = (img_bytes + 1023) & ~1023;
+    const int lane = threadIdx.x & 63, tok = lane & 15, kq = lane >> 4;
+    const int lrow = lane / LPR, lchunk = lane % LPR;  // the row and chunk this lane loads
+    const int wave_in_block = threadIdx.x >> 6;
+    const int wave = uniform_int(blockIdx.x * NW + wave_in_block);
+    const int64_t n_tiles = (n + 15) / 16;
+    const int64_t t0 = wave < n_waves ? (int64_t)wave * n_tiles / n_waves : 0;
+    const int64_t t1 = wave < n_waves ? (int64_t)(wave + 1) * n_tiles / n_waves : 0;
+    const bf16 *x = static_cast<const bf16 *>(a.x);
+    const uint32_t rowb = (uint32_t)d * 2;
+    // this lane's byte offset within the tile for unit j's load i, or an offset past any
+    // descriptor (columns at or past d)
+    auto xoff = [&](int j) -> uint32_t {
+        return UC * j + 8 * lchunk < d ? (uint32_t)lrow * rowb + (uint32_t)UB * j + 16u * lchunk
+                                       : 0x80000000u;
+    };
+    // rows of one tile (none past this wave's range: those loads read zeros, touching nothing)
+    auto tile_rsrc = [&](int64_t tile) {
+        const int64_t rows = tile < t1 ? min((int64_t)16, n - 16 * tile) : 0;
+        return make_rsrc(x + (tile < t1 ? 16 * tile : 0) * (int64_t)d, (uint32_t)rows * rowb);
+    };
+    // units in order: (tile, column range), column ranges fastest
+    auto advance = [&](int64_t &tile, int &j) {
+        if (++j == units_per_tile) { j = 0; ++tile; }
+    };
+    // The W image, built from W by the block: term t of W[k][g] at byte (t m + g) rs + 2k
+    // (w = t0 + t1 + t2 exactly, each term bf16), zeros for k >= d, then one zero row.  Thread
+    // i takes the (pair of k, g) entries i, i + 64 NW, ... (at most kImgPairs of them) and
+    // writes one dword per term.  Its loads of W are issued first, then the first NH units'
+    // rows: loads complete in order, so the image is built while the rows are in flight
+    // (entries past the end read zeros and are not written).
+    // each entry writes 12 bytes of the image, which holds at most kRouteLdsW bytes
+    constexpr int kImgPairs = (kRouteLdsW / 12 + 64 * NW - 1) / (64 * NW);
+    const int pairs = steps * 16 * m;  // (pair of k over whole k-steps, g)
+    float wv[kImgPairs][2];
     {
-        // copy the image in batches of 16 loads per thread (<= 64 KiB each), all in flight
-        const __amdgpu_buffer_rsrc_t ri = make_rsrc(img, (uint32_t)lds_bytes);
-        constexpr int STRIDE = 16 * NT;
-        for (int b0 = 0; b0 < lds_bytes; b0 += 16 * STRIDE) {
-            u32x4 v[16];
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (uint32_t)d * m * 4);
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                v[i] = __builtin_amdgcn_raw_buffer_load_b128(ri, b0 + STRIDE * i + 16 * threadIdx.x, 0, 0);
+        for (int i = 0; i < kImgPairs; ++i) {
+            const int idx = threadIdx.x + i * 64 * NW;
+            const int k2 = idx / m, g = idx - k2 * m;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int b = b0 + STRIDE * i + 16 * threadIdx.x;
-                if (b < lds_bytes) *reinterpret_cast<u32x4 *>(wsm + b) = v[i];
+            for (int h = 0; h < 2; ++h) {
+                const int k = 2 * k2 + h;
+                wv[i][h] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    rw, (idx < pairs && k < d) ? (uint32_t)(k * m + g) * 4 : 0x80000000u, 0, 0));
             }
         }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 ring[NH][NL];
+    int64_t tp = t0;
+    int jp = 0;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(tp);
+        const uint32_t o = xoff(jp);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            ring[h][i] = __builtin_amdgcn_raw_buffer_load_b128(r0, o + i * RPI * rowb, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);  // the order the loop consumes them in
+        }
+        advance(tp, jp);
+    }
+    {
+#pragma unroll
+        for (int i = 0; i < kImgPairs; ++i) {
+            const int idx = threadIdx.x + i * 64 * NW;
+            if (idx < pairs) {
+                const int k2 = idx / m, g = idx - k2 * m;
+                uint32_t packed[3] = {0u, 0u, 0u};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float v = wv[i][h];
+                    const bf16 b0 = (bf16)v;
+                    const float r1 = v - (float)b0;  // exact
+                    const bf16 b1 = (bf16)r1;
+                    const bf16 b2 = (bf16)(r1 - (float)b1);  // exact, at most 8 significant bits
+                    packed[0] |= (uint32_t)__builtin_bit_cast(uint16_t, b0) << (16 * h);
+                    packed[1] |= (uint32_t)__builtin_bit_cast(uint16_t, b1) << (16 * h);
+                    packed[2] |= (uint32_t)__builtin_bit_cast(uint16_t, b2) << (16 * h);
+                }
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+                    *reinterpret_cast<uint32_t *>(smem + (t * m + g) * rs + 4 * k2) = packed[t];
+            }
+        }
+        for (int b = 4 * threadIdx.x; b < rs; b += 4 * 64 * NW)
+            *reinterpret_cast<uint32_t *>(smem + 3 * m * rs + b) = 0u;
     }
     __syncthreads();
-    const int lane = threadIdx.x & 63, tok = lane & 15, kq = lane >> 4;
-    // lanes of padding groups (>= m) read the zero row for every term: no branch in the loop
-    const bool wact = (lane & 15) < m;
-    const char *wl0 = wsm + (wact ? (lane & 15) * rs : 3 * m * rs) + 16 * kq;
+    // W fragments as in route_lds_kernel: lanes of padding groups read the zero row
+    const bool wact = tok < m;
+    const char *wl0 = smem + (wact ? tok * rs : 3 * m * rs) + 16 * kq;
     const int wterm = wact ? m * rs : 0;
-    const int64_t n_items = (n + 16 * T - 1) / (16 * T);
-    const bf16 *x = static_cast<const bf16 *>(a.x);
-    uint32_t xoff[T];
-#pragma unroll
-    for (int i = 0; i < T; ++i) xoff[i] = (uint32_t)(((16 * i + tok) * d + 8 * kq) * 2);
+    char *xs = smem + img_pad + wave_in_block * (16 * UB);
+    const char *xr = xs + tok * UB;
 
-    int next = 0;
-    if (lane == 0) next = atomicAdd(queue, 1);
-    for (;;) {
-        const int item = __builtin_amdgcn_readfirstlane(next);
-        if (item >= n_items) break;
-        if (lane == 0) next = atomicAdd(queue, 1);  // the following item, fetched early
-        const int64_t t0 = (int64_t)item * (16 * T);
-        const int64_t rows = min((int64_t)(16 * T), n - t0);
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + t0 * d, (uint32_t)(rows * d * 2));
-        f32x4 acc[T][1];
+    double psum[4];
+    int cnt[4];
 #pragma unroll
-        for (int i = 0; i < T; ++i) acc[i][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        auto mma = [&](const bf16x8 (&xv)[T], int st) {
-            bf16x8 wv[3];
+    for (int v = 0; v < 4; ++v) { psum[v] = 0.0; cnt[v] = 0; }
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    int pin_raw = -1;
+
+    // one unit: write ring part H (unit (tc, jc)) into the LDS tile and refill it with unit
+    // (tp, jp), NH units ahead; multiply; finish the tile after its last unit
+    auto unit = [&](auto hc, int64_t tc, int jc) {
+        constexpr int H = decltype(hc)::value;
+        // the pin of this row's token, read in every unit of the tile (none: zero records);
+        // issued before the refills, so waiting for it waits for nothing newer
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(
+            a.pin ? a.pin + (tc < t1 ? 16 * tc : 0) : nullptr,
+            (a.pin && tc < t1) ? (uint32_t)min((int64_t)16, n - 16 * tc) * 4 : 0u);
+        pin_raw = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, 4u * tok, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (jc == 0) acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const __amdgpu_buffer_rsrc_t rn = tile_rsrc(tp);
+        const uint32_t on = xoff(jp);
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
-                wv[j] = *reinterpret_cast<const bf16x8 *>(wl0 + j * wterm + 64 * st);
+        for (int i = 0; i < NL; ++i) {
+            const int r = RPI * i + lrow;
+            *reinterpret_cast<u32x4 *>(xs + r * UB + ((lchunk ^ (r & 15)) << 4)) = ring[H][i];
+            __builtin_amdgcn_sched_barrier(0);
+            ring[H][i] = __builtin_amdgcn_raw_buffer_load_b128(rn, on + i * RPI * rowb, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // operands of k-step s of this unit: the three W terms and the x tile's k-slice
+        auto frag_read = [&](bf16x8 (&f)[4], int s) {
+            const int st = KS * jc + s;
 #pragma unroll
-            for (int j = 2; j >= 0; --j)
-#pragma unroll
-                for (int i = 0; i < T; ++i)
-                    acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[j], xv[i], acc[i][0], 0,
-                                                                        0, 0);
+            for (int t = 0; t < 3; ++t)
+                f[t] = *reinterpret_cast<const bf16x8 *>(wl0 + t * wterm + 64 * st);
+            f[3] = *reinterpret_cast<const bf16x8 *>(xr + (((4 * s + kq) ^ tok) << 4));
         };
-        auto xload = [&](bf16x8 (&xv)[T], int st) {
+        auto frag_mma = [&](const bf16x8 (&f)[4]) {
 #pragma unroll
-            for (int i = 0; i < T; ++i)
-                xv[i] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], 64 * st, 0));
+            for (int t = 2; t >= 0; --t)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[t], f[3], acc, 0, 0, 0);
         };
-        if (full > 0) {
-            // whole groups of DX steps in a loop without branches (a branch inside it would
-            // make the compiler wait for every load in flight), then the remaining steps,
-            // whose operands the last group has already loaded
-            bf16x8 ring[DX][T];
+        const int ks = min(KS, steps - KS * jc);
+        if (ks == KS) {
+            // reads two k-steps ahead of the products (a ring of three operand sets), so the
+            // LDS latency is covered by the products of the two steps in between
+            bf16x8 fr[3][4];
+            frag_read(fr[0], 0);
+            frag_read(fr[1], 1);
 #pragma unroll
-            for (int u = 0; u < DX; ++u) {
-                xload(ring[u], min(u, full - 1));
-                __builtin_amdgcn_sched_barrier(0);  // slots in order, as the loop refills them
+            for (int s2 = 0; s2 < KS; ++s2) {
+                if (s2 + 2 < KS) frag_read(fr[(s2 + 2) % 3], s2 + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                frag_mma(fr[s2 % 3]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            const int whole = full / DX;
-            for (int gi = 0; gi < whole; ++gi) {
+        } else {
+            for (int s2 = 0; s2 < ks; ++s2) {
+                bf16x8 f[4];
+                frag_read(f, s2);
+                frag_mma(f);
+            }
+        }
+        if (jc + 1 == units_per_tile && tc < t1) {
+            // lane (tok, kq) holds the logits of groups 4 kq + v (v < 4) of token 16 tc + tok
+            const int64_t tt = 16 * tc + tok;
+            const bool valid = tt < n;
+            float best = 0.0f;
+            int bi = kNoGroup;
 #pragma unroll
-                for (int u = 0; u < DX; ++u) {
-                    mma(ring[u], gi * DX + u);
-                    xload(ring[u], min(gi * DX + u + DX, full - 1));  // past the end: repeats
-                    // keep the refill here: the scheduler would otherwise sink it to the end
-                    // of the group and the next group would wait for loads just issued
-                    __builtin_amdgcn_sched_barrier(0);
+            for (int v = 0; v < 4; ++v) {
+                const int g = 4 * kq + v;
+                if (g < m && (bi == kNoGroup || acc[v] > best)) { best = acc[v]; bi = g; }
+            }
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float ob = __shfl_xor(best, off, 64);
+                const int oi = __shfl_xor(bi, off, 64);
+                if (oi != kNoGroup && (bi == kNoGroup || ob > best || (ob == best && oi < bi))) {
+                    best = ob;
+                    bi = oi;
                 }
             }
+            const int gs = (a.pin && valid && pin_raw >= 0 && pin_raw < m) ? pin_raw : bi;
+            float e[4];
+            float z = 0.0f;
 #pragma unroll
-            for (int u = 0; u < DX - 1; ++u)
-                if (whole * DX + u < full) mma(ring[u], whole * DX + u);
-        }
-        if (full < steps) {  // last k-step: columns past d are zero (W is zero there too)
-            bf16x8 xv[T];
-            xload(xv, full);
-            if (32 * full + 8 * kq >= d)
+            for (int v = 0; v < 4; ++v) {
+                const int g = 4 * kq + v;
+                e[v] = g < m ? __builtin_amdgcn_exp2f((acc[v] - best) * kLog2e) : 0.0f;
+                z += e[v];
+            }
+            z += __shfl_xor(z, 16, 64);
+            z += __shfl_xor(z, 32, 64);
 #pragma unroll
-                for (int i = 0; i < T; ++i) xv[i] = bf16x8{};
-            mma(xv, full);
+            for (int v = 0; v < 4; ++v) {
+                const int g = 4 * kq + v;
+                if (g < m && valid) {
+                    const float p = e[v] / z;
+                    psum[v] += (double)p;
+                    if (g == gs) {
+                        cnt[v] += 1;
+                        a.group_id[tt] = gs;
+                        a.p_sel[tt] = p;
+                    }
+                }
+            }
         }
-        route_finish<1, T>(a, acc, t0, item, tok, kq);
-    }
-}
+        advance(tp, jp);
+    };
 
-__global__ void route_queue_reset(int *queue) {
-    if (threadIdx.x == 0) *queue = 0;
+    // NH units per iteration (one per ring part); a count that is not a multiple of NH ends
+    // with units past the range, whose loads read nothing and whose tiles are not finished
+    const int64_t n_units = (t1 - t0) * units_per_tile;
+    int64_t tc = t0;
+    int jc = 0;
+    for (int64_t u = 0; u < n_units; u += NH) {
+        unit(std::integral_constant<int, 0>{}, tc, jc);
+        advance(tc, jc);
+        if constexpr (NH == 2) {
+            unit(std::integral_constant<int, 1>{}, tc, jc);
+            advance(tc, jc);
+        }
+    }
+    if (wave < n_waves) {
+        // statistics of the wave: the 16 lanes of one k-quarter hold the same groups
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                psum[v] += __shfl_xor(psum[v], off, 64);
+                cnt[v] += __shfl_xor(cnt[v], off, 64);
+            }
+        if (tok == 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int g = 4 * kq + v;
+                if (g < m) {
+                    a.part_p[(int64_t)wave * m + g] = psum[v];
+                    a.part_c[(int64_t)wave * m + g] = cnt[v];
+                }
+            }
+        }
+    }
 }
 
 // One block per group: fixed-order sum of the per-block partials.
@@ -582,9 +727,20 @@ __global__ __launch_bounds__(256) void route_finalize(const double *part_p, cons
     const int g = blockIdx.x;
     double s = 0.0;
     int c = 0;
-    for (int64_t b = threadIdx.x; b < nblk; b += 256) {
-        s += part_p[b * stride + g];
-        c += part_c[b * stride + g];
+    // rows tid, tid + 256, ... added in that order; eight loads in flight at a time (clamped
+    // rows, whose values are not used, keep them unconditional)
+    for (int64_t b0 = threadIdx.x; b0 < nblk; b0 += 256 * 8) {
+        double vp[8];
+        int vc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t b = min(b0 + 256 * i, nblk - 1);
+            vp[i] = part_p[b * stride + g];
+            vc[i] = part_c[b * stride + g];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (b0 + 256 * i < nblk) { s += vp[i]; c += vc[i]; }
     }
     sp[threadIdx.x] = s;
     sc[threadIdx.x] = c;
@@ -625,37 +781,29 @@ hipError_t launch_mm(const RouteLaunch &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int T, int DX, int NT>
-hipError_t launch_lds(const RouteLaunch &a, size_t lds, hipStream_t s) {
-    static int vgpr_blocks = 0;  // blocks per CU allowed by registers (same on every gfx950)
+template <int NW, int NH, int UB>
+hipError_t launch_stage(const RouteLaunch &a, size_t lds, hipStream_t s) {
     int cus = 0;
     hipError_t e = device_cus(&cus);
     if (e != hipSuccess) return e;
-    if (vgpr_blocks == 0) {
-        int b = 0;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                 &b, reinterpret_cast<const void *>(&route_lds_kernel<T, DX, NT>), NT, 0)) !=
-            hipSuccess)
+    const size_t smem = ((lds + 1023) & ~(size_t)1023) + (size_t)NW * 16 * UB;
+    static bool attr_set = false;  // the largest image: kRouteLdsW + NW x 16 UB
+    if (!attr_set) {
+        if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&route_stage_kernel<NW, NH, UB>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     kRouteLdsW + NW * 16 * UB)) != hipSuccess)
             return e;
-        vgpr_blocks = b > 0 ? b : 1;
+        attr_set = true;
     }
-    const int bpc = std::max(1, std::min(vgpr_blocks, (int)(160 * 1024 / lds)));
-    int *queue = reinterpret_cast<int *>(a.wsplit);
-    char *img = static_cast<char *>(a.wsplit) + 256;
-    const int kp = (a.d + 31) / 32 * 32, rs = route_lds_row_bytes(a.d);
-    const int64_t threads = (int64_t)kp * a.m + rs / 16;
-    hipLaunchKernelGGL(route_image_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                       a.w, a.d, a.m, kp, rs, img);
+    // one block of NW waves per CU, at least two tiles (32 tokens) per wave, and no more waves
+    // than rows of partial statistics
+    const int64_t n_tiles = (a.n + 15) / 16;
+    const int64_t n_waves = std::max<int64_t>(
+        1, std::min<int64_t>({(int64_t)cus * NW, (n_tiles + 1) / 2, route_partials(a.n)}));
+    hipLaunchKernelGGL((route_stage_kernel<NW, NH, UB>), dim3((unsigned)((n_waves + NW - 1) / NW)),
+                       dim3(64 * NW), smem, s, a, (int)n_waves);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(route_queue_reset, dim3(1), dim3(64), 0, s, queue);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t n_items = (a.n + 16 * T - 1) / (16 * T);
-    const int64_t wpb = NT / 64;
-    const int64_t grid = std::min<int64_t>((int64_t)cus * bpc, (n_items + wpb - 1) / wpb);
-    hipLaunchKernelGGL((route_lds_kernel<T, DX, NT>), dim3((unsigned)grid), dim3(NT), lds, s, a,
-                       img, (int)lds, queue);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(route_finalize, dim3(a.m), dim3(256), 0, s, a.part_p, a.part_c, n_items,
+    hipLaunchKernelGGL(route_finalize, dim3(a.m), dim3(256), 0, s, a.part_p, a.part_c, n_waves,
                        a.m, a.prob_sum, a.counts);
     return hipGetLastError();
 }
@@ -703,14 +851,13 @@ int64_t route_partials(int64_t n) {
 
 size_t route_split_bytes(int d, int m) {
     const size_t frags = (size_t)3 * ((m + 15) / 16) * ((d + 31) / 32) * 64 * sizeof(bf16x8);
-    const size_t image = (size_t)(3 * m + 1) * route_lds_row_bytes(d);
-    return 256 + std::max(frags, image);
+    return 256 + frags;
 }
 
 hipError_t launch_route(const RouteLaunch &a, hipStream_t s) {
     if (a.x_is_bf16) {
-        const size_t lds = (size_t)(3 * a.m + 1) * route_lds_row_bytes(a.d);
-        if (a.m <= 16 && lds <= (size_t)kRouteLdsW) return launch_lds<4, 4, 256>(a, lds, s);
+        const size_t lds_img = (size_t)(3 * a.m + 1) * route_stage_row_bytes(a.d);
+        if (a.m <= 16 && lds_img <= (size_t)kRouteLdsW) return launch_stage<8, 1, 512>(a, lds_img, s);
         if (a.m <= 16) return launch_mfma<1, 4, 2>(a, s);
         if (a.m <= 32) return launch_mfma<2, 4, 1>(a, s);
         if (a.m <= 48) return launch_mfma<3, 2, 1>(a, s);

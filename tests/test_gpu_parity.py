@@ -36,6 +36,10 @@ def _router_case(n, d, m, seed, x_dtype="bf16", dirichlet=None):
     (1234, 200, 37, "bf16", 8),      # d not a multiple of 32: a partial last k-step
     (1, 64, 3, "bf16", 6),           # a single token
     (333, 128, 1, "f32", 7),         # one group: p == 1
+    (2000, 1024, 8, "bf16", 9),      # two 512-column stripes, eight groups
+    (999, 1000, 7, "bf16", 10),      # a partial last stripe (columns 512..999)
+    (4099, 1536, 4, "bf16", 11),     # fewer groups than the kernel's slots; a 3-token tail
+    (70000, 1536, 5, "bf16", 12),    # many waves, each over a range of 4-token batches
 ])
 def test_route_parity(n, d, m, x_dtype, seed):
     _announce("route", n=n, d=d, m=m, x_dtype=x_dtype)
