@@ -479,9 +479,20 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         const __amdgpu_buffer_rsrc_t rk_head = make_rsrc(kbase, (uint32_t)(a.kv_rows * ROWB));
         const __amdgpu_buffer_rsrc_t rv_head = make_rsrc(vbase, (uint32_t)(a.kv_rows * ROWB));
 
+        // Gathered rows: the row indices of the next tile to issue, fetched while the tile
+        // before it is computed, so issuing a tile never waits for its indices.  Rows past the
+        // segment are clamped to its last row (finite data whose scores are masked and whose
+        // probabilities are zero), which also keeps the fetch past the last tile in bounds.
+        int nrow[LOADS];
+        auto load_rows = [&](int t) {
+            if constexpr (IDX) {
+                const int last = klen - 1;
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) nrow[i] = a.kv_idx[kb + min(t * KT + lrow[i], last)];
+            }
+        };
+
         // tile t -> LDS buffer BUF.  Contiguous rows: rows past the segment read as zeros.
-        // Gathered rows: rows past the segment are clamped to its last row (finite data whose
-        // scores are masked and whose probabilities are zero).
         auto issue = [&](auto bufc, int t) {
             constexpr int buf = decltype(bufc)::value;
             const int key0 = t * KT;
@@ -497,13 +508,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                     load_lds16(rv, &lds[buf][1][slot], vgo[i]);
                 }
             } else {
-                const int last = klen - 1;
+                // the rows were fetched a tile earlier (load_rows)
 #pragma unroll
                 for (int i = 0; i < LOADS; ++i) {
                     const int slot = (i * WAVES + wave) * 1024;
-                    const int row = a.kv_idx[kb + min(key0 + lrow[i], last)];
-                    load_lds16(rk_head, &lds[buf][0][slot], row * ROWB + kgo[i]);
-                    load_lds16(rv_head, &lds[buf][1][slot], row * ROWB + vgo[i]);
+                    load_lds16(rk_head, &lds[buf][0][slot], nrow[i] * ROWB + kgo[i]);
+                    load_lds16(rv_head, &lds[buf][1][slot], nrow[i] * ROWB + vgo[i]);
                 }
             }
         };
@@ -516,7 +526,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         auto tile = [&](auto bufc, auto maskc, int t) {
             constexpr int buf = decltype(bufc)::value;
             constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
-            if (t + 1 < ntiles) issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
+            if (t + 1 < ntiles) {
+                issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
+                load_rows(t + 2);
+            }
             const unsigned char *kt = lds[buf][0];
             const unsigned char *vt_ = lds[buf][1];
 
@@ -600,7 +613,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         };
 
         if (ntiles > 0) {
+            load_rows(0);
             issue(std::integral_constant<int, 0>{}, 0);
+            load_rows(1);
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
             __syncthreads();
         }
