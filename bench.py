@@ -32,8 +32,9 @@ METRIC = "MoGA fwd tokens/s + group-attn TFLOP/s (% bf16 MFMA peak) at N=282k, M
 # plain 1 GiB device copy (FETCH 2.0x, WRITE 1.0x); the summary with the commands is under
 # profiles/.  The figure belongs to one version of the kernel source: any other attn.hip
 # reports null until the counters are taken again.
-STAGE_REPS = 20  # back-to-back calls per short stage in the stage breakdown
-ATTN_TRAFFIC = {"bytes": 10_333_289 * 1024 * 2 + 848_071 * 1024, "attn_hip_sha256_16": "5201f20e9291bb25"}
+STAGE_REPS = 20  # timed calls per short stage and pass in the stage breakdown
+FLUSH_BYTES = 512 << 20  # scratch read before every timed stage call
+ATTN_TRAFFIC = {"bytes": 10_370_624 * 1024 * 2 + 848_058 * 1024, "attn_hip_sha256_16": "5efea73d0723863d"}
 
 
 def attn_traffic_bytes():
@@ -173,10 +174,13 @@ def main():
 
 def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
     """Time each stage through its own C-ABI call (the same kernels moga_forward
-    launches), with HIP events on the stream the kernels run on.  The short stages run
-    STAGE_REPS times back to back between their two events, so the host's argument marshalling
-    and output allocation overlap the previous call's kernels instead of showing up as idle
-    device time; the attention stages run once."""
+    launches), with HIP events on the stream the kernels run on.  Every timed call is
+    preceded by a read of a FLUSH_BYTES scratch buffer (so L2 and the 256 MB MALL hold none
+    of its inputs; a read rather than a write, whose dirty lines would be written back
+    during the timed call: +54 us on the router) and bracketed alone by its two events; the
+    flush also keeps the device busy while the host prepares the call, so the host's
+    argument marshalling does not show up as idle device time.  Short stages run STAGE_REPS
+    such calls per pass, the attention stages one; the median over all passes is reported."""
     import numpy as np
     import torch
 
@@ -187,6 +191,7 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
     names = ["route", "permute", "group_attn", "unpermute", "loss"] + (["stga"] if lay else [])
     acc = {s: [] for s in names}
     log(f"stage breakdown over {args.steps} passes")
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=x.device)
     # one pass of the whole path for the later stages' inputs
     r = api.moga_route(x, w, m, ws=ws)
     cu, perm, (qp, kp, vp), pp = api.moga_permute(r["group_id"], [q, k, v], m,
@@ -206,16 +211,19 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
     for it in range(args.steps + 1):
         for s in names:
             fn, reps = calls[s]
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
+            evs = []
+            for i in range(reps):
+                flush.sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
                 fn()
-            e1.record(stream)
+                e1.record(stream)
+                evs.append((e0, e1))
             torch.cuda.synchronize()
             if it > 0:  # the first pass warms the allocator
-                acc[s].append(e0.elapsed_time(e1) / reps)
-    del r, cu, perm, qp, kp, vp, pp, op
-    ms = {s: float(np.mean(v)) for s, v in acc.items()}
+                acc[s].extend(e0.elapsed_time(e1) for e0, e1 in evs)
+    del r, cu, perm, qp, kp, vp, pp, op, flush
+    ms = {s: float(np.median(v)) for s, v in acc.items()}
     e_bytes = h * n * hd * 2
     x_bytes = n * wl.d_model * (2 if wl.x_dtype == "bf16" else 4)
     route_bytes = x_bytes + wl.d_model * m * 4 + n * 8
