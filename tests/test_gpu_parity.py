@@ -39,7 +39,9 @@ def _router_case(n, d, m, seed, x_dtype="bf16", dirichlet=None):
     (2000, 1024, 8, "bf16", 9),      # two 512-column stripes, eight groups
     (999, 1000, 7, "bf16", 10),      # a partial last stripe (columns 512..999)
     (4099, 1536, 4, "bf16", 11),     # fewer groups than the kernel's slots; a 3-token tail
-    (70000, 1536, 5, "bf16", 12),    # many waves, each over a range of 4-token batches
+    (70000, 1536, 5, "bf16", 12),    # many waves, each over a range of 16-token tiles
+    (3000, 512, 16, "bf16", 13),     # sixteen groups: every lane of the row-contiguous kernel
+    (500, 768, 1, "bf16", 14),       # one group in bf16: p == 1
 ])
 def test_route_parity(n, d, m, x_dtype, seed):
     _announce("route", n=n, d=d, m=m, x_dtype=x_dtype)
