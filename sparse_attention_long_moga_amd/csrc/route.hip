@@ -396,7 +396,8 @@ void route_mfma_kernel(RouteLaunch a, const bf16x8 *wf,
                 route_load(fa[u], rx, xoff, rw, woff, frags, steps, min(u, full - 1));
                 __builtin_amdgcn_sched_barrier(0);  // issue order = consumption order
             }
-            // whole groups of 2U steps without branches (see route_lds_kernel), then the rest
+            // whole groups of 2U steps without branches (a branch inside the loop makes the
+            // compiler wait for every load in flight), then the rest
             const int whole = full / (2 * U);
             for (int gi = 0; gi < whole; ++gi) {
                 const int s = gi * 2 * U;
@@ -565,7 +566,8 @@ void route_stage_kernel(RouteLaunch a, int n_waves) {
             *reinterpret_cast<uint32_t *>(smem + 3 * m * rs + b) = 0u;
     }
     __syncthreads();
-    // W fragments as in route_lds_kernel: lanes of padding groups read the zero row
+    // A fragments: lane (g = tok, kq) reads term t of W[32 st + 8 kq .. +8][g]; lanes of padding
+    // groups (g >= m) read the zero row, so the k-step loop has no branch
     const bool wact = tok < m;
     const char *wl0 = smem + (wact ? tok * rs : 3 * m * rs) + 16 * kq;
     const int wterm = wact ? m * rs : 0;
