@@ -342,24 +342,27 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
                 }
             };
             if constexpr (!DK) {
-                // S, P of both 32-query blocks; P to the partner wave; dV^T += dO'^T P
+                // S, P of both 32-query blocks; P to the partner wave; dV^T += dO'^T P.  Both
+                // blocks' products are issued before the first exponentials, so block 0's vector
+                // work runs while block 1's products are still in the matrix core.
                 bf16x8 pf[2][2];
+                f32x16 sacc[2];
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    f32x16 sacc;
+                for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                     for (int s = 0; s < NS; ++s) {
                         const bf16x8 qf = lds_read_b128(qa + qb * 32 * ROWB + koff[s]);
-                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, bf[s], s ? sacc : f32x16{}, 0, 0, 0);
+                        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, bf[s], s ? sacc[qb] : f32x16{}, 0, 0, 0);
                     }
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         float pv[8];
-                        probs(qb, half, sacc, pv);
+                        probs(qb, half, sacc[qb], pv);
                         pf[qb][half] = pack8(pv);
                         pbuf[qb][kw][half][lane] = __builtin_bit_cast(uint4, pf[qb][half]);
                     }
-                }
                 lds_handoff_barrier();  // P of the tile is visible to the dK waves
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
