@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *gid, int64_t n
     }
     wc[wave][lane] = cnt;
     __syncthreads();
-    if (threadIdx.x < m)
+    if ((int)threadIdx.x < m)
         table[(int64_t)blockIdx.x * m + threadIdx.x] =
             wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] + wc[3][threadIdx.x];
 }
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t *table, int64_t
         __syncthreads();
         // Hillis-Steele inclusive scan over 256 entries
         for (int off = 1; off < 256; off <<= 1) {
-            const int add = threadIdx.x >= off ? s[threadIdx.x - off] : 0;
+            const int add = (int)threadIdx.x >= off ? s[threadIdx.x - off] : 0;
             __syncthreads();
             s[threadIdx.x] += add;
             __syncthreads();
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *gid, int64_
             perm[pos] = (int32_t)t;
         }
         __syncthreads();
-        if (threadIdx.x < m)
+        if ((int)threadIdx.x < m)
             base[threadIdx.x] += wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] +
                                  wc[3][threadIdx.x];
         __syncthreads();

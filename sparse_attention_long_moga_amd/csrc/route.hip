@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteLaunch a, int dc) {
     red_p[wave][lane] = psum;
     red_c[wave][lane] = cnt;
     __syncthreads();
-    if (threadIdx.x < m) {
+    if ((int)threadIdx.x < m) {
         double s = 0.0;
         int c = 0;
 #pragma unroll
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 3
 void route_mfma_kernel(RouteLaunch a, const bf16x8 *wf,
                                                          int *queue, int steps) {
     const int lane = threadIdx.x & 63, tok = lane & 15, kq = lane >> 4;
-    const int d = a.d, m = a.m;
+    const int d = a.d;
     const int64_t n = a.n;
     const int frags = MT * steps * 64;
     const int full = d / 32;  // k-steps whose 32 columns all lie inside the row
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(256) void route_finalize(const double *part_p, cons
     sc[threadIdx.x] = c;
     __syncthreads();
     for (int w = 128; w >= 1; w >>= 1) {
-        if (threadIdx.x < w) {
+        if ((int)threadIdx.x < w) {
             sp[threadIdx.x] += sp[threadIdx.x + w];
             sc[threadIdx.x] += sc[threadIdx.x + w];
         }
