@@ -462,8 +462,10 @@ __host__ __device__ inline int route_stage_row_bytes(int d) { return ((d + 31) /
 // built.  Each wave owns a contiguous, balanced range of tiles; its group statistics go to
 // row `wave` of part_p / part_c.
 template <int NW, int NH, int UB>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void route_stage_kernel(RouteLaunch a, int n_waves) {
+    static_assert(NH == 1 || NH == 2, "the unit loop below handles one or two ring parts");
+    static_assert(NW % 4 == 0, "whole waves per SIMD");
     constexpr int LPR = UB / 16;      // lanes per row in a load
     constexpr int RPI = 64 / LPR;     // rows per load instruction
     constexpr int NL = 16 / RPI;      // load instructions per unit
