@@ -51,8 +51,10 @@ typedef enum { MOGA_F32 = 0, MOGA_BF16 = 1 } moga_dtype;
 
 /* Problem sizes shared by the calls.
  *   n_tokens      N, 1 <= N < 2^31
- *   d_model       router input width d (a multiple of 8 for bf16 x, of 4 for f32 x)
- *   n_heads       H >= 1
+ *   d_model       router input width d, 1 <= d <= 2^20 (a multiple of 8 for bf16 x, of 4
+ *                 for f32 x)
+ *   n_heads       H >= 1, with H * (ceil(N/128) + M) < 2^31 (the attention work list;
+ *                 with a STGA layout M is replaced by the larger of its group and frame counts)
  *   head_dim      64 or 128
  *   n_groups      M, 1 <= M <= 64
  *   softmax_scale attention scale; <= 0 selects 1/sqrt(head_dim)

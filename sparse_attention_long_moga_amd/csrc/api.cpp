@@ -66,7 +66,8 @@ moga_status check_dims(const moga_dims *d) {
     if (!d) return fail(MOGA_ERR_ARG, "dims is NULL");
     if (d->n_tokens < 1 || d->n_tokens >= (int64_t(1) << 31))
         return fail(MOGA_ERR_ARG, "n_tokens %lld outside [1, 2^31)", (long long)d->n_tokens);
-    if (d->d_model < 1) return fail(MOGA_ERR_ARG, "d_model %d < 1", d->d_model);
+    if (d->d_model < 1 || d->d_model > kMaxDModel)
+        return fail(MOGA_ERR_ARG, "d_model %d outside [1, %d]", d->d_model, kMaxDModel);
     if (d->n_heads < 1) return fail(MOGA_ERR_ARG, "n_heads %d < 1", d->n_heads);
     if (d->head_dim != 64 && d->head_dim != 128)
         return fail(MOGA_ERR_ARG, "head_dim %d is not 64 or 128", d->head_dim);
@@ -74,6 +75,9 @@ moga_status check_dims(const moga_dims *d) {
         return fail(MOGA_ERR_ARG, "n_groups %d outside [1, %d]", d->n_groups, kMaxGroups);
     if (!std::isfinite(d->softmax_scale)) return fail(MOGA_ERR_ARG, "softmax_scale is not finite");
     if (!std::isfinite(d->alpha)) return fail(MOGA_ERR_ARG, "alpha is not finite");
+    // the attention work list is indexed with 32-bit integers on the device
+    if (attn_max_items(d->n_heads, d->n_tokens, d->n_groups) >= (int64_t(1) << 31))
+        return fail(MOGA_ERR_ARG, "n_heads x query tiles reaches 2^31 attention work items");
     return MOGA_OK;
 }
 
@@ -107,6 +111,9 @@ moga_status check_stga(const moga_dims *d, const stga_layout *s, StgaGeom *g) {
     for (int i = 0; i <= s->n_shots; ++i) g->shot_start[i] = s->shot_start[i];
     if (d->n_tokens + stga_extra_rows(*g) >= (int64_t(1) << 31))
         return fail(MOGA_ERR_ARG, "n_tokens plus borrowed key rows reaches 2^31");
+    const int32_t segs = std::max(stga_n_groups(*g), g->frames);
+    if (attn_max_items(d->n_heads, d->n_tokens, segs) >= (int64_t(1) << 31))
+        return fail(MOGA_ERR_ARG, "n_heads x stga query tiles reaches 2^31 attention work items");
     return MOGA_OK;
 }
 

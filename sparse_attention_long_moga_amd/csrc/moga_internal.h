@@ -13,6 +13,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxGroups = 64;    // M <= 64
+constexpr int kMaxDModel = 1 << 20;  // router width d; keeps 32-bit buffer offsets in range
 constexpr int kMaxShots = 256;    // STGA shots passed by value
 constexpr int kAttnBQMin = 128;   // smallest query rows per attention work item (4 waves x 32)
 constexpr int kAttnThreads = 256;

@@ -48,6 +48,8 @@ def _dims(**kw):
     (dict(n_tokens=0), "n_tokens"), (dict(n_tokens=1 << 31), "n_tokens"),
     (dict(head_dim=96), "head_dim"), (dict(n_groups=0), "n_groups"),
     (dict(n_groups=65), "n_groups"), (dict(n_heads=0), "n_heads"), (dict(d_model=0), "d_model"),
+    (dict(d_model=(1 << 20) + 8), "d_model"),
+    (dict(n_tokens=1 << 30, n_heads=256), "work items"),
 ])
 def test_bad_dims_rejected(lib, kw, msg):
     d = _dims(**kw)
@@ -103,6 +105,17 @@ def test_stga_geometry_checks(lib):
         assert lib.moga_workspace_bytes(ctypes.byref(d), lay.ref()) == 0
         assert lib.stga_group_attn(p, p, p, ctypes.byref(d), lay.ref(), p, p, p, 1 << 40,
                                    None) == _capi.MOGA_ERR_ARG
+
+
+def test_stga_work_list_bound(lib):
+    # one-token windows and one-frame chunks make every token its own group: with two heads
+    # the attention work list would pass 2^31 items, so the layout is refused up front
+    f, h, w = 1 << 14, 256, 256
+    d = _dims(n_tokens=f * h * w, n_heads=2)
+    lay = make_stga_layout(f, h, w, [0, f], 1, 1, 1, 0)
+    assert lib.moga_workspace_bytes(ctypes.byref(d), lay.ref()) == 0
+    assert "work items" in lib.moga_last_error().decode()
+    assert lib.moga_workspace_bytes(ctypes.byref(d), None) > 0
 
 
 def test_workspace_sizes_scale_with_problem(lib):
