@@ -120,6 +120,11 @@ moga_status check_stga(const moga_dims *d, const stga_layout *s, StgaGeom *g) {
 // ---------------------------------------------------------------- workspace
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// query rows of an attention launch whose kernel may split key ranges (head_dim 128)
+int64_t split_rows(const moga_dims *d, int64_t len_q) {
+    return d->head_dim == 128 ? (int64_t)d->n_heads * len_q : 0;
+}
+
 struct Carver {
     size_t off = 0;
     size_t take(size_t bytes) {
@@ -184,7 +189,7 @@ Layout make_layout(const moga_dims *d, const StgaGeom *g) {
     }
     L.plan_seg = seg;
     L.plan_items = items;
-    L.plan = c.take(attn_plan_bytes(seg, items));
+    L.plan = c.take(attn_plan_bytes(seg, items, split_rows(d, n)));
     L.total = c.off;
     return L;
 }
@@ -217,7 +222,7 @@ BwdLayout make_bwd_layout(const moga_dims *d) {
     B.dr = c.take(sizeof(float) * n * d->n_groups);
     B.dw_part = c.take(sizeof(float) * bwd_dw_chunks(n) * d->d_model * d->n_groups);
     B.plan_items = attn_max_items(d->n_heads, n, d->n_groups);
-    B.plan = c.take(attn_plan_bytes(d->n_groups, B.plan_items));
+    B.plan = c.take(attn_plan_bytes(d->n_groups, B.plan_items, 0));
     B.total = c.off;
     return B;
 }
@@ -297,7 +302,7 @@ moga_status run_attn(const void *q, const void *k, const void *v, void *o, const
     a.lse = lse;
     if (a.max_items > plan_items || n_seg > plan_seg)
         return fail(MOGA_ERR_WORKSPACE, "attention plan larger than its workspace region");
-    attn_plan_carve(a.plan, plan_mem, n_seg, a.max_items);
+    attn_plan_carve(a.plan, plan_mem, n_seg, a.max_items, split_rows(d, len_q));
     HIP_TRY(launch_attention(a, s), "attention launch");
     return MOGA_OK;
 }
@@ -342,7 +347,7 @@ size_t moga_workspace_bytes(const moga_dims *dims, const stga_layout *stga) {
 
 size_t moga_group_attn_workspace_bytes(const moga_dims *dims, int32_t n_seg, int64_t len_q) {
     if (check_dims(dims) != MOGA_OK || n_seg < 1 || len_q < 0) return 0;
-    return attn_plan_bytes(n_seg, attn_max_items(dims->n_heads, len_q, n_seg));
+    return attn_plan_bytes(n_seg, attn_max_items(dims->n_heads, len_q, n_seg), split_rows(dims, len_q));
 }
 
 moga_status moga_route(const void *x, moga_dtype x_dtype, const float *w, const int32_t *pin,
@@ -402,7 +407,7 @@ moga_status moga_group_attn(const void *q, const void *k, const void *v, int64_t
     if (n_seg < 1) return fail(MOGA_ERR_ARG, "n_seg %d < 1", n_seg);
     const int64_t items = attn_max_items(dims->n_heads, len_q, n_seg);
     if (items >= (int64_t(1) << 31)) return fail(MOGA_ERR_ARG, "too many work items");
-    const size_t need = attn_plan_bytes(n_seg, items);
+    const size_t need = attn_plan_bytes(n_seg, items, split_rows(dims, len_q));
     if ((st = check_ws(ws, ws_bytes, need)) != MOGA_OK) return st;
     if ((st = check_device()) != MOGA_OK) return st;
     // long segments on average: 256-row query tiles; short ones: 128
@@ -593,7 +598,7 @@ moga_status moga_backward(const moga_inputs *in, const moga_saved *saved, const 
         a.dv = static_cast<bf16 *>(dvp);
         a.cu = saved->cu_seqlens; a.n_seg = m; a.len = n; a.n_heads = nh; a.scale = scale_of(dims);
         a.max_items = B.plan_items;
-        attn_plan_carve(a.plan, at<char>(ws, B.plan), m, B.plan_items);
+        attn_plan_carve(a.plan, at<char>(ws, B.plan), m, B.plan_items, 0);
         HIP_TRY(launch_attention_bwd(a, s), "attention backward launch");
     }
     // back to token order

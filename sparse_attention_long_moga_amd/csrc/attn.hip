@@ -20,6 +20,7 @@
 // share (segment, head), so the blocks running at one time stream the same K/V through L2.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -28,10 +29,11 @@ namespace moga {
 namespace {
 
 // ---------------------------------------------------------------------------- planning
+// slots: blocks of the persistent grid that will run the items (0: no key-range split).
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const int32_t *cu_k,
                                                      int n_seg, int64_t len_q, int64_t len_k,
                                                      int n_heads, int bq, int64_t max_items,
-                                                     AttnPlan p) {
+                                                     int slots, AttnPlan p) {
     __shared__ int s_klen[kPlanSortMax];
     __shared__ int s_order[kPlanSortMax];
     __shared__ int s_scan[1024];
@@ -87,13 +89,29 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const i
         p.item_base[n_seg] = carry;
         p.counter[0] = 0;
         // overlapping (non-monotone) offsets could ask for more items than the list holds
-        p.counter[1] = carry < max_items ? carry : (int)max_items;
+        const int n_items = carry < max_items ? carry : (int)max_items;
+        // Items of one launch cost about the same when its segments do (and the list runs
+        // longest first), so the last n_items mod slots of them would occupy a few blocks for a
+        // whole item's time while the rest of the grid idles.  When that remainder is at most
+        // half the grid, each of those items is cut into `parts` key ranges that run side by
+        // side and are merged afterwards (attn_split_combine).
+        int first = n_items, parts = 1;
+        const int cap = slots < p.split_cap ? slots : p.split_cap;
+        const int r = slots > 0 ? n_items % slots : 0;
+        if (r > 0 && 2 * r <= cap) {
+            parts = min(kSplitMaxParts, cap / r);
+            first = n_items - r;
+        }
+        p.counter[1] = first + (n_items - first) * parts;
+        p.counter[2] = first;
+        p.counter[3] = parts;
+        p.counter[4] = n_items;
     }
 }
 
 __global__ __launch_bounds__(256) void fill_items_kernel(AttnPlan p, int n_seg) {
     const int i = blockIdx.x * 256 + threadIdx.x;
-    const int total = p.counter[1];
+    const int total = p.counter[4];
     if (i >= total) return;
     int lo = 0, hi = n_seg;  // item_base[lo] <= i < item_base[hi]
     while (hi - lo > 1) {
@@ -423,11 +441,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, hh = lane >> 5;
     const int total = uniform(a.plan.counter[1]);
+    const int split_first = uniform(a.plan.counter[2]), split_parts = uniform(a.plan.counter[3]);
     const float c = a.scale * kLog2e;
     const float thr = kRescaleLog2 / c;
 
     // per-lane LDS byte offsets of the MFMA operands within a tile
     static_assert(ROWB == ROWB128, "direct-load layouts are for head_dim 128");
+    static_assert(BQ <= kSplitRows, "a split part holds one query tile");
     int koff[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) koff[s] = a_frag_off(j, hh, s);
@@ -451,13 +471,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         const int item = uniform(s_item);
         __syncthreads();
         if (item >= total) break;
-        const int4 itm = a.plan.items[item];
+        // dispatch entries from split_first on are parts of split items: part `sub % parts`
+        // of item split_first + sub / parts takes that share of the segment's key tiles
+        const int sub = item - split_first;
+        const int4 itm = a.plan.items[sub >= 0 ? split_first + sub / split_parts : item];
         const int seg = uniform(itm.x), h = uniform(itm.y), qt = uniform(itm.z);
         const int qb = uniform((int)clamp64(a.cu_q[seg], 0, a.len_q));
         const int qe = uniform((int)clamp64(a.cu_q[seg + 1], qb, a.len_q));
-        const int kb = uniform((int)clamp64(a.cu_k[seg], 0, a.len_k));
+        int kb = uniform((int)clamp64(a.cu_k[seg], 0, a.len_k));
         const int ke = uniform((int)clamp64(a.cu_k[seg + 1], kb, a.len_k));
-        const int klen = ke - kb;
+        int klen = ke - kb;
+        if (sub >= 0) {
+            const int part = sub % split_parts, nt = (klen + KT - 1) / KT;
+            const int t_lo = part * nt / split_parts, t_hi = (part + 1) * nt / split_parts;
+            kb = uniform(kb + t_lo * KT);
+            klen = uniform(max(min(t_hi * KT, klen) - t_lo * KT, 0));
+        }
 
         const int qrow = qb + qt * BQ + wave * 32 + j;
         const bool qvalid = qrow < qe;
@@ -639,6 +668,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         }
 
         const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+        if (sub >= 0) {
+            // a part of a split item: its rows unnormalised, with their maximum and sum
+            const int64_t row = (int64_t)sub * kSplitRows + wave * 32 + j;
+            float *po = a.plan.split_o + row * HD + 4 * hh;
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq)
+                    *reinterpret_cast<float4 *>(po + 32 * ti + 8 * kq) =
+                        make_float4(o[ti][kq * 4 + 0], o[ti][kq * 4 + 1], o[ti][kq * 4 + 2],
+                                    o[ti][kq * 4 + 3]);
+            if (hh == 0)
+                *reinterpret_cast<float2 *>(a.plan.split_ml + 2 * row) = make_float2(m_run, l_tot);
+            continue;
+        }
         if (a.lse && qvalid && hh == 0)  // log(sum exp(scale q.k)) = scale*m + ln(l)
             a.lse[(int64_t)h * a.o_rows + qphys] =
                 l_tot > 0.0f ? (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
@@ -657,6 +701,67 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                 }
         }
     }
+}
+
+// Merges the key-range parts of the split items.  Per row: with part u's maximum m_u and
+// sum l_u (probabilities formed as 2^(c (s - m_u))), the row's maximum is m = max m_u, its sum
+// l = sum_u l_u 2^(c (m_u - m)) and its output sum_u O_u 2^(c (m_u - m)) / l, scaled by the
+// row's factor and stored as the unsplit epilogue stores it (with its log-sum-exp when asked
+// for).  Half a wave per row, four columns per lane, eight rows per block and bq / 8 blocks per
+// split item; each lane issues all its parts' loads before it uses any of them.
+__global__ __launch_bounds__(256) void attn_split_combine(AttnLaunch a, int bq) {
+    constexpr int HD = 128;
+    const int first = a.plan.counter[2], parts = a.plan.counter[3];
+    const int n_split = (a.plan.counter[1] - first) / parts;
+    const int per_item = bq / 8;
+    const int b = blockIdx.x / per_item;
+    if (b >= n_split) return;
+    const int4 itm = a.plan.items[first + b];
+    const int seg = itm.x, h = itm.y, qt = itm.z;
+    const int r = (blockIdx.x % per_item) * 8 + (threadIdx.x >> 5);
+    const int64_t qb = clamp64(a.cu_q[seg], 0, a.len_q);
+    const int64_t qe = clamp64(a.cu_q[seg + 1], qb, a.len_q);
+    const int64_t qrow = qb + (int64_t)qt * bq + r;
+    if (qrow >= qe) return;
+    const int col = 4 * (threadIdx.x & 31);
+    const int64_t row0 = (int64_t)b * parts * kSplitRows + r;  // part u: row0 + u kSplitRows
+    float2 ml[kSplitMaxParts];
+    float4 ou[kSplitMaxParts];
+#pragma unroll
+    for (int u = 0; u < kSplitMaxParts; ++u) {
+        if (u < parts) {
+            const int64_t ru = row0 + (int64_t)u * kSplitRows;
+            ml[u] = *reinterpret_cast<const float2 *>(a.plan.split_ml + 2 * ru);
+            ou[u] = *reinterpret_cast<const float4 *>(a.plan.split_o + ru * HD + col);
+        }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kSplitMaxParts; ++u)
+        if (u < parts) m = fmaxf(m, ml[u].x);
+    const float c = a.scale * kLog2e;
+    float l = 0.0f;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (m > -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < kSplitMaxParts; ++u) {
+            if (u < parts) {
+                const float w = __builtin_amdgcn_exp2f((ml[u].x - m) * c);  // 0: an empty part
+                l += ml[u].y * w;
+                acc.x += ou[u].x * w; acc.y += ou[u].y * w;
+                acc.z += ou[u].z * w; acc.w += ou[u].w * w;
+            }
+        }
+    }
+    const int64_t qphys =
+        a.q_idx ? min(max((int64_t)a.q_idx[qrow], (int64_t)0), a.q_rows - 1) : qrow;
+    if (a.lse && col == 0)
+        a.lse[(int64_t)h * a.o_rows + qphys] =
+            l > 0.0f ? (m * c + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+    float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if (a.row_scale) inv *= a.row_scale[qphys];
+    *reinterpret_cast<uint2 *>(a.o + (int64_t)h * a.o_rows * HD + qphys * HD + col) =
+        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
 }
 
 int g_num_cus[64];  // per device
@@ -686,12 +791,20 @@ int64_t attn_max_items(int n_heads, int64_t len_q, int32_t n_seg) {
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-size_t attn_plan_bytes(int32_t n_seg, int64_t max_items) {
-    const size_t seg = align256(sizeof(int32_t) * (size_t)(n_seg + 1));
-    return 4 * seg + align256(sizeof(int4) * (size_t)max_items) + 256;
+// split parts the workspace holds: no more rows than the launch's queries, at most 512 parts
+static int64_t split_cap(int64_t split_rows) {
+    return std::min<int64_t>(kSplitMaxCap, std::max<int64_t>(split_rows, 0) / kSplitRows);
 }
 
-void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items) {
+size_t attn_plan_bytes(int32_t n_seg, int64_t max_items, int64_t split_rows) {
+    const size_t seg = align256(sizeof(int32_t) * (size_t)(n_seg + 1));
+    const size_t cap = (size_t)split_cap(split_rows);
+    return 4 * seg + align256(sizeof(int4) * (size_t)max_items) + 256 +
+           cap * kSplitRows * (128 + 2) * sizeof(float);
+}
+
+void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items,
+                     int64_t split_rows) {
     char *b = static_cast<char *>(base);
     const size_t seg = align256(sizeof(int32_t) * (size_t)(n_seg + 1));
     p.seg_klen = reinterpret_cast<int32_t *>(b); b += seg;
@@ -699,14 +812,17 @@ void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items) 
     p.order = reinterpret_cast<int32_t *>(b); b += seg;
     p.item_base = reinterpret_cast<int32_t *>(b); b += seg;
     p.items = reinterpret_cast<int4 *>(b); b += align256(sizeof(int4) * (size_t)max_items);
-    p.counter = reinterpret_cast<int32_t *>(b);
+    p.counter = reinterpret_cast<int32_t *>(b); b += 256;
+    p.split_cap = (int32_t)split_cap(split_rows);
+    p.split_o = reinterpret_cast<float *>(b); b += (size_t)p.split_cap * kSplitRows * 128 * sizeof(float);
+    p.split_ml = reinterpret_cast<float *>(b);
 }
 
 hipError_t launch_attn_plan(const int32_t *cu_q, const int32_t *cu_k, int32_t n_seg,
                             int64_t len_q, int64_t len_k, int n_heads, int bq, int64_t max_items,
                             const AttnPlan &plan, hipStream_t s) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, cu_q, cu_k, n_seg, len_q, len_k,
-                       n_heads, bq, max_items, plan);
+                       n_heads, bq, max_items, 0, plan);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)((max_items + 255) / 256)), dim3(256), 0,
@@ -723,18 +839,20 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     const bool direct = a.head_dim == 128 && a.kv_rows * 256 < (int64_t(1) << 31);
     const int waves = a.waves == 4 ? 4 : 8;
     const int bq = direct ? 32 * waves : (indexed ? 128 : 256);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_q, a.cu_k, a.n_seg, a.len_q,
-                       a.len_k, a.n_heads, bq, a.max_items, a.plan);
-    hipError_t e = hipGetLastError();
+    int cus = 0;
+    hipError_t e = device_cus(&cus);
     if (e != hipSuccess) return e;
+    // persistent grids: two waves per SIMD in every configuration; the head_dim 128 kernel
+    // may split the last items' key ranges over the grid's blocks
+    const int slots = cus * (8 / waves);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_q, a.cu_k, a.n_seg, a.len_q,
+                       a.len_k, a.n_heads, bq, a.max_items, direct ? slots : 0, a.plan);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t fill_blocks = (a.max_items + 255) / 256;
     hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, s, a.plan,
                        a.n_seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    int cus = 0;
-    if ((e = device_cus(&cus)) != hipSuccess) return e;
-    // persistent grids: two waves per SIMD in every configuration
-    const dim3 grid((unsigned)(cus * (8 / waves))), blk((unsigned)(64 * waves));
+    const dim3 grid((unsigned)slots), blk((unsigned)(64 * waves));
     const dim3 grid4((unsigned)(cus * 2)), blk4(256u);
     const dim3 grid8((unsigned)cus), blk8(512u);
     if (direct) {
@@ -744,6 +862,13 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
         } else {
             if (waves == 8) hipLaunchKernelGGL((attn_kernel_direct<8, false>), grid, blk, 0, s, a);
             else hipLaunchKernelGGL((attn_kernel_direct<4, false>), grid, blk, 0, s, a);
+        }
+        // split items number at most half of min(slots, split_cap) (the planner's rule)
+        const int most = std::min(slots, (int)a.plan.split_cap) / 2;
+        if (most > 0) {
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(attn_split_combine, dim3((unsigned)(most * (bq / 8))), dim3(256), 0,
+                               s, a, bq);
         }
     } else if (a.head_dim == 128) {
         if (indexed) hipLaunchKernelGGL((attn_kernel<128, true, 4>), grid4, blk4, 0, s, a);

@@ -83,11 +83,23 @@ struct AttnPlan {
     int32_t *order;      // [n_seg] segments by descending key length
     int32_t *item_base;  // [n_seg + 1]
     int4 *items;         // [max_items] (segment, head, q tile, 0)
-    int32_t *counter;    // [2]: dispatch counter, item count
+    // [5]: dispatch counter, dispatch count, first split item, parts per split item, item count
+    int32_t *counter;
+    // Key-range split of the last items (forward, head_dim 128): part u of the split items
+    // leaves its unnormalised rows in split_o [u][kSplitRows][128] and (row max, row sum) in
+    // split_ml [u][kSplitRows][2]; split_cap parts fit (0: no splitting).
+    float *split_o, *split_ml;
+    int32_t split_cap;
 };
-size_t attn_plan_bytes(int32_t n_seg, int64_t max_items);
+constexpr int kSplitRows = 256;     // rows per split part (the largest query tile)
+constexpr int kSplitMaxParts = 8;   // key ranges per split item
+constexpr int kSplitMaxCap = 512;   // split parts held in the workspace
+// split_rows: heads x query rows of the launches that use the plan when their kernel can split
+// key ranges (head_dim 128), else 0; the room for split parts is about their fp32 size
+size_t attn_plan_bytes(int32_t n_seg, int64_t max_items, int64_t split_rows);
 int64_t attn_max_items(int n_heads, int64_t len_q, int32_t n_seg);
-void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items);
+void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items,
+                     int64_t split_rows);
 
 struct AttnLaunch {
     const bf16 *q, *k, *v;

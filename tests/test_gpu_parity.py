@@ -153,6 +153,69 @@ def test_group_attn_leaves_rows_outside_segments():
     assert not torch.any(out[:, 10:300] == 7.0)
 
 
+def _split_tail(kl, n_q_tiles, heads, slots, cap):
+    """The planner's key-range split, restated: items run longest key range first (ties by
+    segment), head-major within a segment; the last n_items mod slots items are split when
+    they are at most half of min(slots, cap).  Returns ([(segment, head, q tile)] of the split
+    items, parts)."""
+    order = sorted(range(len(kl)), key=lambda s: (-kl[s], s))
+    items = [(s, hh, t) for s in order for hh in range(heads) for t in range(n_q_tiles[s])]
+    cap = min(slots, cap)
+    r = len(items) % slots
+    if r == 0 or 2 * r > cap:
+        return [], 1
+    return items[len(items) - r:], min(8, cap // r)
+
+
+@pytest.mark.parametrize("case", ["long_segments", "short_segments"])
+def test_group_attn_split_tail(case):
+    """The last items of a launch split into key ranges and merged: every row of those items
+    and a sample of the others against the oracle, including a segment with queries but no
+    keys, ragged last tiles and parts that get no key tile at all."""
+    _announce("group_attn_split_tail", case=case)
+    rng = np.random.Generator(np.random.PCG64(31 if case == "long_segments" else 37))
+    hd = 128
+    if case == "long_segments":   # 8-wave items of 256 rows
+        h = 2
+        ql = np.array([20000, 9000, 3000, 1300, 300])
+        kl = np.array([20000, 9050, 3000, 1300, 0])
+    else:                         # 4-wave items of 128 rows over short segments
+        h = 1
+        ql = rng.integers(257, 384, 180)
+        kl = ql + rng.integers(0, 130, 180)
+    cu_q, cu_k = _segments(ql), _segments(kl)
+    lq, lk = int(cu_q[-1]), int(cu_k[-1])
+    waves = 8 if lq // len(ql) >= 1024 else 4
+    bq = 32 * waves
+    slots = torch.cuda.get_device_properties(0).multi_processor_count * (8 // waves)
+    split, parts = _split_tail(list(kl), [-(-int(x) // bq) for x in ql], h, slots,
+                               min(512, h * lq // 256))
+    assert split and parts >= 2, "the shape no longer splits on this device"
+    q = torch.randn((h, lq, hd), device=DEV, dtype=torch.bfloat16)
+    k = torch.randn((h, lk, hd), device=DEV, dtype=torch.bfloat16)
+    v = torch.randn((h, lk, hd), device=DEV, dtype=torch.bfloat16)
+    rs = torch.rand(lq, device=DEV, dtype=torch.float32) + 0.5
+    out = api.moga_group_attn(q, k, v, torch.from_numpy(cu_q).to(DEV),
+                              torch.from_numpy(cu_k).to(DEV), row_scale=rs)
+    torch.cuda.synchronize()
+    rows = set()
+    for s_, hh, t in split:
+        for i in range(cu_q[s_] + t * bq, min(cu_q[s_] + (t + 1) * bq, cu_q[s_ + 1])):
+            rows.add((hh, int(i)))
+    for s_ in range(len(ql)):
+        if ql[s_]:
+            for i in rng.choice(np.arange(cu_q[s_], cu_q[s_ + 1]), size=min(8, int(ql[s_])),
+                                replace=False):
+                rows.add((int(rng.integers(0, h)), int(i)))
+    rows = sorted(rows)
+    rows_h = np.array([r[0] for r in rows])
+    rows_i = np.array([r[1] for r in rows])
+    ref, _ = oracle.varlen_attn(host(q), host(k), host(v), cu_q, cu_k, 1 / math.sqrt(hd),
+                                rows_h, rows_i, row_scale=host(rs))
+    have = host(out[torch.from_numpy(rows_h).to(DEV), torch.from_numpy(rows_i).to(DEV)])
+    assert_close_bf16(have, ref, f"group_attn split tail {case} ({len(split)} items x {parts})")
+
+
 # ------------------------------------------------------------------------------- STGA
 STGA_CASES = {
     "small_hd64": dict(frames=10, height=6, width=8, shot_start=[0, 3, 4, 8, 10], win_h=3,
