@@ -93,8 +93,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const i
         // Items of one launch cost about the same when its segments do (and the list runs
         // longest first), so the last n_items mod slots of them would occupy a few blocks for a
         // whole item's time while the rest of the grid idles.  When that remainder is at most
-        // half the grid, each of those items is cut into `parts` key ranges that run side by
-        // side and are merged afterwards (attn_split_combine).
+        // half the grid, each of those items is cut into `parts` key ranges that a second launch
+        // runs side by side, and attn_split_combine merges them.
         int first = n_items, parts = 1;
         const int cap = slots < p.split_cap ? slots : p.split_cap;
         const int r = slots > 0 ? n_items % slots : 0;
@@ -102,26 +102,31 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const i
             parts = min(kSplitMaxParts, cap / r);
             first = n_items - r;
         }
-        p.counter[1] = first + (n_items - first) * parts;
+        p.counter[1] = first;                       // whole items
         p.counter[2] = first;
         p.counter[3] = parts;
-        p.counter[4] = n_items;
+        p.counter[4] = 0;                           // dispatch counter of the split parts
+        p.counter[5] = (n_items - first) * parts;   // split parts
     }
 }
 
+// Dispatch entry i: item i before the first split item; from there, part u of split item b
+// (entry first + b parts + u) carries the item's (segment, head, q tile) and w = u + 1.
 __global__ __launch_bounds__(256) void fill_items_kernel(AttnPlan p, int n_seg) {
     const int i = blockIdx.x * 256 + threadIdx.x;
-    const int total = p.counter[4];
-    if (i >= total) return;
-    int lo = 0, hi = n_seg;  // item_base[lo] <= i < item_base[hi]
+    if (i >= p.counter[1] + p.counter[5]) return;
+    const int first = p.counter[2], parts = p.counter[3];
+    const int src = i < first ? i : first + (i - first) / parts;
+    const int part = i < first ? 0 : 1 + (i - first) % parts;
+    int lo = 0, hi = n_seg;  // item_base[lo] <= src < item_base[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (p.item_base[mid] <= i) lo = mid; else hi = mid;
+        if (p.item_base[mid] <= src) lo = mid; else hi = mid;
     }
     const int seg = p.order[lo];
-    const int local = i - p.item_base[lo];
+    const int local = src - p.item_base[lo];
     const int nt = p.seg_ntile[seg];
-    p.items[i] = make_int4(seg, local / nt, local % nt, 0);
+    p.items[i] = make_int4(seg, local / nt, local % nt, part);
 }
 
 // ---------------------------------------------------------------------------- attention
@@ -425,7 +430,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel(AttnLaunch 
 
 // IDX: rows are read through the index maps (STGA groups, or the permutation itself for
 // the permute-free MoGA variant); each lane then fetches its chunk's row index first.
-template <int WAVES, bool IDX>
+// SPLIT: the launch that runs the parts of split items (entries first + u of the item list,
+// dispatched from their own counter); otherwise the whole items.
+template <int WAVES, bool IDX, bool SPLIT>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(AttnLaunch a) {
     constexpr int HD = 128;
     constexpr int NS = HD / 16, NT = HD / 32;
@@ -440,8 +447,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, hh = lane >> 5;
-    const int total = uniform(a.plan.counter[1]);
-    const int split_first = uniform(a.plan.counter[2]), split_parts = uniform(a.plan.counter[3]);
+    const int total = uniform(a.plan.counter[SPLIT ? 5 : 1]);
+    [[maybe_unused]] const int split_first = SPLIT ? uniform(a.plan.counter[2]) : 0;
+    [[maybe_unused]] const int split_parts = SPLIT ? uniform(a.plan.counter[3]) : 1;
     const float c = a.scale * kLog2e;
     const float thr = kRescaleLog2 / c;
 
@@ -466,23 +474,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
     }
 
     for (;;) {
-        if (tid == 0) s_item = atomicAdd(a.plan.counter, 1);
+        if (tid == 0) s_item = atomicAdd(a.plan.counter + (SPLIT ? 4 : 0), 1);
         __syncthreads();
         const int item = uniform(s_item);
         __syncthreads();
         if (item >= total) break;
-        // dispatch entries from split_first on are parts of split items: part `sub % parts`
-        // of item split_first + sub / parts takes that share of the segment's key tiles
-        const int sub = item - split_first;
-        const int4 itm = a.plan.items[sub >= 0 ? split_first + sub / split_parts : item];
+        // a split part (entry split_first + item, w = part + 1) takes its share of the
+        // segment's key tiles and leaves its rows in split slot `item`
+        const int4 itm = a.plan.items[SPLIT ? split_first + item : item];
         const int seg = uniform(itm.x), h = uniform(itm.y), qt = uniform(itm.z);
         const int qb = uniform((int)clamp64(a.cu_q[seg], 0, a.len_q));
         const int qe = uniform((int)clamp64(a.cu_q[seg + 1], qb, a.len_q));
         int kb = uniform((int)clamp64(a.cu_k[seg], 0, a.len_k));
         const int ke = uniform((int)clamp64(a.cu_k[seg + 1], kb, a.len_k));
         int klen = ke - kb;
-        if (sub >= 0) {
-            const int part = sub % split_parts, nt = (klen + KT - 1) / KT;
+        if constexpr (SPLIT) {
+            const int part = uniform(itm.w) - 1, nt = (klen + KT - 1) / KT;
             const int t_lo = part * nt / split_parts, t_hi = (part + 1) * nt / split_parts;
             kb = uniform(kb + t_lo * KT);
             klen = uniform(max(min(t_hi * KT, klen) - t_lo * KT, 0));
@@ -668,9 +675,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         }
 
         const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-        if (sub >= 0) {
+        if constexpr (SPLIT) {
             // a part of a split item: its rows unnormalised, with their maximum and sum
-            const int64_t row = (int64_t)sub * kSplitRows + wave * 32 + j;
+            const int64_t row = (int64_t)item * kSplitRows + wave * 32 + j;
             float *po = a.plan.split_o + row * HD + 4 * hh;
 #pragma unroll
             for (int ti = 0; ti < NT; ++ti)
@@ -712,11 +719,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
 __global__ __launch_bounds__(256) void attn_split_combine(AttnLaunch a, int bq) {
     constexpr int HD = 128;
     const int first = a.plan.counter[2], parts = a.plan.counter[3];
-    const int n_split = (a.plan.counter[1] - first) / parts;
+    const int n_split = a.plan.counter[5] / parts;
     const int per_item = bq / 8;
     const int b = blockIdx.x / per_item;
     if (b >= n_split) return;
-    const int4 itm = a.plan.items[first + b];
+    const int4 itm = a.plan.items[first + b * parts];
     const int seg = itm.x, h = itm.y, qt = itm.z;
     const int r = (blockIdx.x % per_item) * 8 + (threadIdx.x >> 5);
     const int64_t qb = clamp64(a.cu_q[seg], 0, a.len_q);
@@ -799,7 +806,7 @@ static int64_t split_cap(int64_t split_rows) {
 size_t attn_plan_bytes(int32_t n_seg, int64_t max_items, int64_t split_rows) {
     const size_t seg = align256(sizeof(int32_t) * (size_t)(n_seg + 1));
     const size_t cap = (size_t)split_cap(split_rows);
-    return 4 * seg + align256(sizeof(int4) * (size_t)max_items) + 256 +
+    return 4 * seg + align256(sizeof(int4) * (size_t)(max_items + cap)) + 256 +
            cap * kSplitRows * (128 + 2) * sizeof(float);
 }
 
@@ -811,9 +818,10 @@ void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items,
     p.seg_ntile = reinterpret_cast<int32_t *>(b); b += seg;
     p.order = reinterpret_cast<int32_t *>(b); b += seg;
     p.item_base = reinterpret_cast<int32_t *>(b); b += seg;
-    p.items = reinterpret_cast<int4 *>(b); b += align256(sizeof(int4) * (size_t)max_items);
-    p.counter = reinterpret_cast<int32_t *>(b); b += 256;
     p.split_cap = (int32_t)split_cap(split_rows);
+    p.items = reinterpret_cast<int4 *>(b);
+    b += align256(sizeof(int4) * (size_t)(max_items + p.split_cap));
+    p.counter = reinterpret_cast<int32_t *>(b); b += 256;
     p.split_o = reinterpret_cast<float *>(b); b += (size_t)p.split_cap * kSplitRows * 128 * sizeof(float);
     p.split_ml = reinterpret_cast<float *>(b);
 }
@@ -825,7 +833,7 @@ hipError_t launch_attn_plan(const int32_t *cu_q, const int32_t *cu_k, int32_t n_
                        n_heads, bq, max_items, 0, plan);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)((max_items + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)((max_items + plan.split_cap + 255) / 256)), dim3(256), 0,
                        s, plan, n_seg);
     return hipGetLastError();
 }
@@ -848,7 +856,7 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_q, a.cu_k, a.n_seg, a.len_q,
                        a.len_k, a.n_heads, bq, a.max_items, direct ? slots : 0, a.plan);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t fill_blocks = (a.max_items + 255) / 256;
+    const int64_t fill_blocks = (a.max_items + a.plan.split_cap + 255) / 256;
     hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, s, a.plan,
                        a.n_seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -857,18 +865,28 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     const dim3 grid8((unsigned)cus), blk8(512u);
     if (direct) {
         if (indexed) {
-            if (waves == 8) hipLaunchKernelGGL((attn_kernel_direct<8, true>), grid, blk, 0, s, a);
-            else hipLaunchKernelGGL((attn_kernel_direct<4, true>), grid, blk, 0, s, a);
+            if (waves == 8) hipLaunchKernelGGL((attn_kernel_direct<8, true, false>), grid, blk, 0, s, a);
+            else hipLaunchKernelGGL((attn_kernel_direct<4, true, false>), grid, blk, 0, s, a);
         } else {
-            if (waves == 8) hipLaunchKernelGGL((attn_kernel_direct<8, false>), grid, blk, 0, s, a);
-            else hipLaunchKernelGGL((attn_kernel_direct<4, false>), grid, blk, 0, s, a);
+            if (waves == 8) hipLaunchKernelGGL((attn_kernel_direct<8, false, false>), grid, blk, 0, s, a);
+            else hipLaunchKernelGGL((attn_kernel_direct<4, false, false>), grid, blk, 0, s, a);
         }
-        // split items number at most half of min(slots, split_cap) (the planner's rule)
-        const int most = std::min(slots, (int)a.plan.split_cap) / 2;
-        if (most > 0) {
+        // the split parts, at most min(slots, split_cap) of them (one per block), then their
+        // merge: split items number at most half of that (the planner's rule)
+        const int room = std::min(slots, (int)a.plan.split_cap);
+        if (room >= 2) {
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            hipLaunchKernelGGL(attn_split_combine, dim3((unsigned)(most * (bq / 8))), dim3(256), 0,
-                               s, a, bq);
+            const dim3 gsplit((unsigned)room);
+            if (indexed) {
+                if (waves == 8) hipLaunchKernelGGL((attn_kernel_direct<8, true, true>), gsplit, blk, 0, s, a);
+                else hipLaunchKernelGGL((attn_kernel_direct<4, true, true>), gsplit, blk, 0, s, a);
+            } else {
+                if (waves == 8) hipLaunchKernelGGL((attn_kernel_direct<8, false, true>), gsplit, blk, 0, s, a);
+                else hipLaunchKernelGGL((attn_kernel_direct<4, false, true>), gsplit, blk, 0, s, a);
+            }
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(attn_split_combine, dim3((unsigned)(room / 2 * (bq / 8))), dim3(256),
+                               0, s, a, bq);
         }
     } else if (a.head_dim == 128) {
         if (indexed) hipLaunchKernelGGL((attn_kernel<128, true, 4>), grid4, blk4, 0, s, a);

@@ -82,7 +82,7 @@ struct AttnPlan {
     int32_t *seg_ntile;  // [n_seg]
     int32_t *order;      // [n_seg] segments by descending key length
     int32_t *item_base;  // [n_seg + 1]
-    int4 *items;         // [max_items] (segment, head, q tile, 0)
+    int4 *items;         // [max_items + split_cap] (segment, head, q tile, split part + 1 or 0)
     // [5]: dispatch counter, dispatch count, first split item, parts per split item, item count
     int32_t *counter;
     // Key-range split of the last items (forward, head_dim 128): part u of the split items
