@@ -93,14 +93,23 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const i
         // Items of one launch cost about the same when its segments do (and the list runs
         // longest first), so the last n_items mod slots of them would occupy a few blocks for a
         // whole item's time while the rest of the grid idles.  When that remainder is at most
-        // half the grid, each of those items is cut into `parts` key ranges that a second launch
-        // runs side by side, and attn_split_combine merges them.
+        // half the grid and its longest item has at least kSplitMinKeys keys (shorter items
+        // finish sooner than the extra launches take), each of those items is cut into `parts`
+        // key ranges that a second launch runs side by side, and attn_split_combine merges them.
         int first = n_items, parts = 1;
         const int cap = slots < p.split_cap ? slots : p.split_cap;
         const int r = slots > 0 ? n_items % slots : 0;
         if (r > 0 && 2 * r <= cap) {
-            parts = min(kSplitMaxParts, cap / r);
-            first = n_items - r;
+            const int t = n_items - r;
+            int lo = 0, hi = n_seg;  // item_base[lo] <= t < item_base[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (p.item_base[mid] <= t) lo = mid; else hi = mid;
+            }
+            if (p.seg_klen[p.order[lo]] >= kSplitMinKeys) {
+                parts = min(kSplitMaxParts, cap / r);
+                first = t;
+            }
         }
         p.counter[1] = first;                       // whole items
         p.counter[2] = first;
@@ -851,10 +860,11 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     hipError_t e = device_cus(&cus);
     if (e != hipSuccess) return e;
     // persistent grids: two waves per SIMD in every configuration; the head_dim 128 kernel
-    // may split the last items' key ranges over the grid's blocks
+    // with 256-row items (long segments) may split the last items' key ranges over the grid
     const int slots = cus * (8 / waves);
+    const bool splits = direct && waves == 8;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_q, a.cu_k, a.n_seg, a.len_q,
-                       a.len_k, a.n_heads, bq, a.max_items, direct ? slots : 0, a.plan);
+                       a.len_k, a.n_heads, bq, a.max_items, splits ? slots : 0, a.plan);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t fill_blocks = (a.max_items + a.plan.split_cap + 255) / 256;
     hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, s, a.plan,
@@ -873,7 +883,7 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
         }
         // the split parts, at most min(slots, split_cap) of them (one per block), then their
         // merge: split items number at most half of that (the planner's rule)
-        const int room = std::min(slots, (int)a.plan.split_cap);
+        const int room = splits ? std::min(slots, (int)a.plan.split_cap) : 0;
         if (room >= 2) {
             if ((e = hipGetLastError()) != hipSuccess) return e;
             const dim3 gsplit((unsigned)room);

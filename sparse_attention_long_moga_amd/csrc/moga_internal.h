@@ -94,6 +94,7 @@ struct AttnPlan {
 constexpr int kSplitRows = 256;     // rows per split part (the largest query tile)
 constexpr int kSplitMaxParts = 8;   // key ranges per split item
 constexpr int kSplitMaxCap = 512;   // split parts held in the workspace
+constexpr int kSplitMinKeys = 2048; // shortest key range of an item worth splitting
 // split_rows: heads x query rows of the launches that use the plan when their kernel can split
 // key ranges (head_dim 128), else 0; the room for split parts is about their fp32 size
 size_t attn_plan_bytes(int32_t n_seg, int64_t max_items, int64_t split_rows);

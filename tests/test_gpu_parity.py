@@ -156,33 +156,33 @@ def test_group_attn_leaves_rows_outside_segments():
 def _split_tail(kl, n_q_tiles, heads, slots, cap):
     """The planner's key-range split, restated: items run longest key range first (ties by
     segment), head-major within a segment; the last n_items mod slots items are split when
-    they are at most half of min(slots, cap).  Returns ([(segment, head, q tile)] of the split
-    items, parts)."""
+    they are at most half of min(slots, cap) and the first of them has at least 2048 keys.
+    Returns ([(segment, head, q tile)] of the split items, parts)."""
     order = sorted(range(len(kl)), key=lambda s: (-kl[s], s))
     items = [(s, hh, t) for s in order for hh in range(heads) for t in range(n_q_tiles[s])]
     cap = min(slots, cap)
     r = len(items) % slots
-    if r == 0 or 2 * r > cap:
+    if r == 0 or 2 * r > cap or kl[items[len(items) - r][0]] < 2048:
         return [], 1
     return items[len(items) - r:], min(8, cap // r)
 
 
-@pytest.mark.parametrize("case", ["long_segments", "short_segments"])
+@pytest.mark.parametrize("case", ["mixed_segments", "many_segments"])
 def test_group_attn_split_tail(case):
     """The last items of a launch split into key ranges and merged: every row of those items
     and a sample of the others against the oracle, including a segment with queries but no
-    keys, ragged last tiles and parts that get no key tile at all."""
+    keys (every part empty), q != k lengths and ragged last query and key tiles."""
     _announce("group_attn_split_tail", case=case)
-    rng = np.random.Generator(np.random.PCG64(31 if case == "long_segments" else 37))
+    rng = np.random.Generator(np.random.PCG64(31 if case == "mixed_segments" else 37))
     hd = 128
-    if case == "long_segments":   # 8-wave items of 256 rows
+    if case == "mixed_segments":  # the tail: a 2500-key segment's items, then a keyless one's
         h = 2
         ql = np.array([20000, 9000, 3000, 1300, 300])
-        kl = np.array([20000, 9050, 3000, 1300, 0])
-    else:                         # 4-wave items of 128 rows over short segments
+        kl = np.array([20000, 9050, 3000, 2500, 0])
+    else:                         # thirty segments of 2100 rows, one head: eight parts
         h = 1
-        ql = rng.integers(257, 384, 180)
-        kl = ql + rng.integers(0, 130, 180)
+        ql = np.full(30, 2100)
+        kl = ql + rng.integers(0, 40, 30)
     cu_q, cu_k = _segments(ql), _segments(kl)
     lq, lk = int(cu_q[-1]), int(cu_k[-1])
     waves = 8 if lq // len(ql) >= 1024 else 4
