@@ -349,3 +349,17 @@ def test_fused_forward_is_bitwise_the_explicit_one(hybrid, hd):
         ref = (ref + oracle.stga_attn(qh, kh, vh, grid, "temporal", scale, rows_h, rows_t)[0]
                + oracle.stga_attn(qh, kh, vh, grid, "frame", scale, rows_h, rows_t)[0]) / 3.0
     assert_close_bf16(host(b["out"]).reshape(-1, hd), ref, f"fused hybrid={hybrid}")
+
+
+def test_fused_forward_is_bitwise_the_explicit_one_with_split_tail():
+    """At the 5 s size the last 24 items are split into key ranges: the fused forward (rows
+    read through perm) must still equal the explicit one bit for bit, lse included."""
+    wl = workloads.WAN5S
+    _announce("fused_vs_explicit_split", name=wl.name)
+    x, w = workloads.make_x(wl, DEV), workloads.make_w(wl, DEV)
+    q, k, v = workloads.make_qkv(wl, DEV)
+    a = api.moga_forward(x, w, q, k, v, wl.n_groups, alpha=wl.alpha, with_lse=True)
+    b = api.moga_forward_fused(x, w, q, k, v, wl.n_groups, alpha=wl.alpha, with_lse=True)
+    torch.cuda.synchronize()
+    for key in ("out", "lse", "perm", "cu_seqlens", "p_sel"):
+        assert torch.equal(a[key], b[key]), key
