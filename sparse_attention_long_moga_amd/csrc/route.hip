@@ -799,11 +799,11 @@ hipError_t launch_stage(const RouteLaunch &a, size_t lds, hipStream_t s) {
             return e;
         attr_set = true;
     }
-    // one block of NW waves per CU, at least two tiles (32 tokens) per wave, and no more waves
-    // than rows of partial statistics
+    // one block of NW waves per CU, at least one tile (16 tokens) per wave (short inputs still
+    // spread over every CU), and no more waves than rows of partial statistics
     const int64_t n_tiles = (a.n + 15) / 16;
     const int64_t n_waves = std::max<int64_t>(
-        1, std::min<int64_t>({(int64_t)cus * NW, (n_tiles + 1) / 2, route_partials(a.n)}));
+        1, std::min<int64_t>({(int64_t)cus * NW, n_tiles, route_partials(a.n)}));
     hipLaunchKernelGGL((route_stage_kernel<NW, NH, UB>), dim3((unsigned)((n_waves + NW - 1) / NW)),
                        dim3(64 * NW), smem, s, a, (int)n_waves);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -848,9 +848,9 @@ hipError_t launch_mfma(const RouteLaunch &a, hipStream_t s) {
 int64_t route_blocks(int64_t n) { return (n + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock; }
 
 int64_t route_partials(int64_t n) {
-    // per-block rows of kMaxGroups (fp32 x) or per-item rows of m <= kMaxGroups (bf16 x, items of
-    // at least 32 tokens)
-    return std::max<int64_t>(route_blocks(n), (n + 31) / 32);
+    // per-block rows of kMaxGroups (fp32 x) or per-wave / per-item rows of m <= kMaxGroups (bf16
+    // x: waves of at least one 16-token tile, items of 64 tokens)
+    return std::max<int64_t>(route_blocks(n), (n + 15) / 16);
 }
 
 size_t route_split_bytes(int d, int m) {
