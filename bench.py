@@ -242,7 +242,7 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
     stages["permute_frac_of_hbm"] = stages["permute_gbs"] / HBM_PEAK_GBS
     stages["unpermute_frac_of_hbm"] = stages["unpermute_gbs"] / HBM_PEAK_GBS
     stages["roofline"] = {
-        "bound": "mfma", "kernel": "attn_kernel_direct<8> (group_attn stage)",
+        "bound": "mfma", "kernel": "attn_kernel_direct<8, false, false> (group_attn stage)",
         "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
         "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": attn_traffic_bytes(),
         "algorithmic_flops_per_launch": attn_flops,
