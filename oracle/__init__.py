@@ -82,6 +82,9 @@ def _load():
     lib.oracle_moga_dq_rows.argtypes = [_f32p, _f32p, _f32p, _f32p, c_i64, c_int, _i32p, c_int,
                                         _f64p, c_dbl, c_i64, _i32p, _i64p, _f64p, _f64p, _f64p]
     lib.oracle_moga_dq_rows.restype = c_int
+    lib.oracle_moga_dkdv_rows.argtypes = [_f32p, _f32p, _f32p, _f32p, c_i64, c_int, _i32p, c_int,
+                                          _f64p, c_dbl, c_i64, _i32p, _i64p, _f64p, _f64p]
+    lib.oracle_moga_dkdv_rows.restype = c_int
     lib.oracle_router_bwd_rows.argtypes = [_f32p, _f32p, c_i64, c_int, c_int, _i32p, _f64p,
                                            _i64p, c_i64, c_dbl, c_dbl, _f64p, _f64p]
     lib.oracle_router_bwd_rows.restype = c_int
@@ -221,6 +224,23 @@ def moga_dq_rows(q, k, v, d_out, group_id, m: int, p_sel, scale: float, rows_h, 
     if rc != 0:
         raise ValueError(f"oracle_moga_dq_rows failed ({rc})")
     return dq, D, lse
+
+
+def moga_dkdv_rows(q, k, v, d_out, group_id, m: int, p_sel, scale: float, rows_h, rows_t):
+    """dk and dv of selected (head, key token) rows, same definitions as moga_backward (each
+    needs the softmax rows of every query of the key's group).  Returns (dk, dv), each
+    [rows][hd]."""
+    q, k, v, go = _f32(q), _f32(k), _f32(v), _f32(d_out)
+    _, n, hd = q.shape
+    g = np.ascontiguousarray(group_id, dtype=np.int32)
+    ps = np.ascontiguousarray(p_sel, dtype=np.float64)
+    rh, rt = _rows(rows_h, rows_t)
+    dk, dv = np.empty((rh.shape[0], hd)), np.empty((rh.shape[0], hd))
+    rc = _load().oracle_moga_dkdv_rows(q, k, v, go, n, hd, g, m, ps, float(scale), rh.shape[0],
+                                       rh, rt, dk, dv)
+    if rc != 0:
+        raise ValueError(f"oracle_moga_dkdv_rows failed ({rc})")
+    return dk, dv
 
 
 def router_backward_rows(x_rows, w, group_rows, dp_rows, counts, n: int, d_loss: float,

@@ -589,3 +589,84 @@ int oracle_router_bwd_rows(const float *x_rows, const float *w, int64_t n_rows, 
     free(p); free(F);
     return 0;
 }
+
+/* dk and dv of selected KEY rows only: row r is head rows_h[r] (an index into the heads of
+ * q/k/v/d_out), key token rows_t[r].  Same definitions as oracle_moga_backward: for a key u of
+ * group G, dv_u = sum over the queries t of G of P_tu dO'_t and
+ * dk_u = scale sum_t P_tu (dP_tu - D_t) q_t, with dO'_t = p_t d_out_t, dP_tu = <dO'_t, v_u>,
+ * and P_tu, D_t = <dO'_t, O'_t> from each query's whole softmax row over G.  Every query of G
+ * is needed, so the work per (head, group) is |G|^2 hd whatever the number of sampled keys. */
+int oracle_moga_dkdv_rows(const float *q, const float *k, const float *v, const float *d_out,
+                          int64_t n, int hd, const int32_t *group_id, int m,
+                          const double *p_sel, double scale, int64_t n_rows,
+                          const int32_t *rows_h, const int64_t *rows_t, double *dk, double *dv)
+{
+    if (n < 1 || hd < 1 || m < 1 || n_rows < 0) return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows_t[r] < 0 || rows_t[r] >= n || group_id[rows_t[r]] < 0 || group_id[rows_t[r]] >= m)
+            return -3;
+    int64_t *cnt = (int64_t *)calloc((size_t)m + 1, sizeof(int64_t));
+    int64_t *members = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    if (!cnt || !members) { free(cnt); free(members); return -2; }
+    group_members(group_id, n, m, cnt, members);
+    for (int64_t r = 0; r < n_rows * hd; ++r) { dk[r] = 0.0; dv[r] = 0.0; }
+    int rc = 0;
+    /* one (head, group) pair at a time: the softmax statistics of all its queries, then the
+     * sampled keys of that pair */
+    for (int64_t r0 = 0; r0 < n_rows && rc == 0; ++r0) {
+        const int h = rows_h[r0], g = group_id[rows_t[r0]];
+        int first = 1;
+        for (int64_t r1 = 0; r1 < r0; ++r1)
+            if (rows_h[r1] == h && group_id[rows_t[r1]] == g) { first = 0; break; }
+        if (!first) continue;
+        const int64_t nk = cnt[g + 1] - cnt[g];
+        const int64_t *keys = members + cnt[g];
+        const int64_t hoff = (int64_t)h * n * hd;
+        double *lse = (double *)malloc(sizeof(double) * (size_t)nk);
+        double *D = (double *)malloc(sizeof(double) * (size_t)nk);
+        if (!lse || !D) { free(lse); free(D); rc = -2; break; }
+#pragma omp parallel
+        {
+            double *P = (double *)malloc(sizeof(double) * (size_t)nk);
+            double *o = (double *)malloc(sizeof(double) * (size_t)hd);
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t a = 0; a < nk; ++a) {
+                const int64_t t = keys[a];
+                lse[a] = softmax_row(q + hoff + t * hd, k + hoff, v + hoff, hd, keys, nk, scale, P,
+                                     o);
+                double Dt = 0.0;
+                for (int c = 0; c < hd; ++c)
+                    Dt += p_sel[t] * (double)d_out[hoff + t * hd + c] * o[c];
+                D[a] = Dt;
+            }
+            free(P);
+            free(o);
+        }
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = r0; r < n_rows; ++r) {
+            if (rows_h[r] != h || group_id[rows_t[r]] != g) continue;
+            const int64_t u = rows_t[r];
+            const float *ku = k + hoff + u * hd, *vu = v + hoff + u * hd;
+            for (int64_t a = 0; a < nk; ++a) {
+                const int64_t t = keys[a];
+                const float *qt = q + hoff + t * hd, *gt = d_out + hoff + t * hd;
+                double s = 0.0, dP = 0.0;
+                for (int c = 0; c < hd; ++c) {
+                    s += (double)qt[c] * (double)ku[c];
+                    dP += p_sel[t] * (double)gt[c] * (double)vu[c];
+                }
+                const double P = exp(scale * s - lse[a]);
+                const double dS = P * (dP - D[a]);
+                for (int c = 0; c < hd; ++c) {
+                    dv[r * hd + c] += P * p_sel[t] * (double)gt[c];
+                    dk[r * hd + c] += scale * dS * (double)qt[c];
+                }
+            }
+        }
+        free(lse);
+        free(D);
+    }
+    free(cnt);
+    free(members);
+    return rc;
+}

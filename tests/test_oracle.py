@@ -477,3 +477,24 @@ def test_backward_dq_rows_match_full():
     dq, D, lse = oracle.moga_dq_rows(q, k, v, go, g, 3, p_sel, 0.3, rows_h, rows_t)
     np.testing.assert_allclose(dq, ref["dq"][rows_h, rows_t], rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(lse, ref["lse"][rows_h, rows_t], rtol=1e-12)
+
+
+def test_backward_dkdv_rows_match_full():
+    """dk and dv of sampled key rows equal the full backward's rows (which autograd and finite
+    differences pin above), including a key of a one-token group and keys of two heads."""
+    x, w, q, k, v, go = _bwd_case(n=90, m=4, seed=38)
+    g = bf.router(x, w)[2].copy()
+    g[17] = 3
+    g[g == 3] = 2
+    g[17] = 3                                   # group 3 holds one token
+    _, p, _ = bf.router(x, w)
+    p_sel = p[np.arange(len(g)), g]
+    ref = oracle.moga_backward(x, w, q, k, v, g, go, 0.7, 0.1, 0.3)
+    rows_h = np.array([0, 1, 1, 0, 1, 0], np.int32)
+    rows_t = np.array([0, 5, 89, 40, 17, 17], np.int64)
+    dk, dv = oracle.moga_dkdv_rows(q, k, v, go, g, 4, p_sel, 0.3, rows_h, rows_t)
+    np.testing.assert_allclose(dk, ref["dk"][rows_h, rows_t], rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dv, ref["dv"][rows_h, rows_t], rtol=1e-11, atol=1e-14)
+    # a one-token group: P = 1, so dv = p * d_out and dk = 0
+    np.testing.assert_allclose(dv[4], p_sel[17] * go[1][17], rtol=1e-12)
+    np.testing.assert_allclose(dk[4], 0.0, atol=1e-14)
