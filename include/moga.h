@@ -121,7 +121,7 @@ size_t moga_workspace_bytes(const moga_dims *dims, const stga_layout *stga);
 
 /* Workspace bytes needed by moga_group_attn with n_seg segments and len_q query rows.
  * With head_dim 128 this includes room for the key-range split of a launch's last items
- * (fp32 partial rows: at most 512 parts of 256 rows, and no more rows than H * len_q). */
+ * (fp32 partial rows: at most 256 parts of 256 rows, and no more rows than H * len_q). */
 size_t moga_group_attn_workspace_bytes(const moga_dims *dims, int32_t n_seg, int64_t len_q);
 
 /* Router (design 1; blog §2.3): r = x W in fp32 (no bias), p = softmax(r),

@@ -807,7 +807,7 @@ int64_t attn_max_items(int n_heads, int64_t len_q, int32_t n_seg) {
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// split parts the workspace holds: no more rows than the launch's queries, at most 512 parts
+// split parts the workspace holds: no more rows than the launch's queries, at most kSplitMaxCap
 static int64_t split_cap(int64_t split_rows) {
     return std::min<int64_t>(kSplitMaxCap, std::max<int64_t>(split_rows, 0) / kSplitRows);
 }

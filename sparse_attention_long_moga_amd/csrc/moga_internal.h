@@ -93,7 +93,9 @@ struct AttnPlan {
 };
 constexpr int kSplitRows = 256;     // rows per split part (the largest query tile)
 constexpr int kSplitMaxParts = 8;   // key ranges per split item
-constexpr int kSplitMaxCap = 512;   // split parts held in the workspace
+// split parts held in the workspace: the planner uses at most one part per block of the
+// persistent grid (one 8-wave block per CU, 256 on gfx950), so more room would never be used
+constexpr int kSplitMaxCap = 256;
 constexpr int kSplitMinKeys = 2048; // shortest key range of an item worth splitting
 // split_rows: heads x query rows of the launches that use the plan when their kernel can split
 // key ranges (head_dim 128), else 0; the room for split parts is about their fp32 size
