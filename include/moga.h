@@ -164,6 +164,21 @@ moga_status moga_group_attn(const void *q, const void *k, const void *v, int64_t
                             const int32_t *cu_k, const float *row_scale, const moga_dims *dims,
                             void *o, void *ws, size_t ws_bytes, void *stream);
 
+/* moga_group_attn without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The arguments and results are those of moga_group_attn (bitwise the same outputs); the
+ * attention plan lives in a static array of 40 MiB that the library holds on every device it
+ * runs on until the process ends.  Sizes whose plan exceeds it (moga_group_attn_workspace_bytes
+ * above 40 MiB: H * len_q beyond about 60 M query rows) return MOGA_ERR_WORKSPACE before any
+ * launch.  Every call on one device shares that device's array: calls that overlap in time on
+ * one device (different streams, or several host threads without ordering) race and must not
+ * be issued.  The call allocates nothing and needs no initialised memory (the planning kernel
+ * writes every counter the attention kernels read). */
+moga_status moga_group_attn_noalloc(const void *q, const void *k, const void *v, int64_t len_q,
+                                    int64_t len_k, int32_t n_seg, const int32_t *cu_q,
+                                    const int32_t *cu_k, const float *row_scale,
+                                    const moga_dims *dims, void *o, void *stream);
+
 /* STGA (design 4): temporal-window groups with boundary-frame K/V augmentation,
  * written to o_temporal, and per-frame groups, written to o_frame, both bf16
  * [H][N][head_dim] in token order and unscaled.  Either output may be NULL to

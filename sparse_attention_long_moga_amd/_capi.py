@@ -15,7 +15,7 @@ STATUS_NAMES = {0: "MOGA_OK", 1: "MOGA_ERR_ARG", 2: "MOGA_ERR_UNSUPPORTED",
 EXPORTS = ["moga_last_error", "moga_workspace_bytes", "moga_group_attn_workspace_bytes",
            "moga_route", "moga_permute", "moga_group_attn", "stga_group_attn",
            "moga_balance_loss", "moga_forward", "moga_forward_fused",
-           "moga_backward_workspace_bytes", "moga_backward"]
+           "moga_backward_workspace_bytes", "moga_backward", "moga_group_attn_noalloc"]
 
 
 class MogaDims(ctypes.Structure):
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH):
     lib.moga_permute.restype = st
     lib.moga_group_attn.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, pdims, vp, vp, sz, vp]
     lib.moga_group_attn.restype = st
+    lib.moga_group_attn_noalloc.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, pdims, vp, vp]
+    lib.moga_group_attn_noalloc.restype = st
     lib.stga_group_attn.argtypes = [vp, vp, vp, pdims, pstga, vp, vp, vp, sz, vp]
     lib.stga_group_attn.restype = st
     lib.moga_balance_loss.argtypes = [vp, vp, pdims, vp, vp, vp, vp]

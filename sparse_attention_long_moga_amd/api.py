@@ -16,7 +16,8 @@ from . import _capi
 from ._capi import MogaDims, MogaGrads, MogaInputs, MogaOutputs, MogaSaved, StgaLayout, check
 
 __all__ = ["make_dims", "make_stga_layout", "moga_workspace_bytes", "workspace", "moga_route",
-           "moga_permute", "moga_unpermute", "moga_group_attn", "stga_group_attn",
+           "moga_permute", "moga_unpermute", "moga_group_attn", "moga_group_attn_noalloc",
+           "stga_group_attn",
            "moga_balance_loss", "moga_forward", "moga_forward_fused", "moga_backward"]
 
 
@@ -169,23 +170,17 @@ def moga_unpermute(perm: torch.Tensor, tensors: Sequence[torch.Tensor], n_groups
     return outs
 
 
-def moga_group_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_q: torch.Tensor,
-                    cu_k: torch.Tensor, row_scale: Optional[torch.Tensor] = None,
-                    softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
-                    ws: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Varlen group attention: q [H, Lq, hd], k/v [H, Lk, hd] bf16; cu_q/cu_k int32 [S+1]."""
+def _group_attn_args(q, k, v, cu_q, cu_k, row_scale, out):
     _need(q, "q", torch.bfloat16, 3)
     h, lq, hd = q.shape
     _need(k, "k", torch.bfloat16, 3, q.device)
     _need(v, "v", torch.bfloat16, 3, q.device)
-    lk = k.shape[1]
     if k.shape != v.shape or k.shape[0] != h or k.shape[2] != hd:
         raise ValueError("k and v must be [H, Lk, head_dim] matching q")
     _need(cu_q, "cu_q", torch.int32, 1, q.device)
     _need(cu_k, "cu_k", torch.int32, 1, q.device)
     if cu_q.shape != cu_k.shape:
         raise ValueError("cu_q and cu_k must have the same length")
-    n_seg = cu_q.shape[0] - 1
     if row_scale is not None:
         _need(row_scale, "row_scale", torch.float32, 1, q.device)
         if row_scale.shape[0] != lq:
@@ -194,6 +189,17 @@ def moga_group_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_q: tor
         out = torch.empty_like(q)
     else:
         _need(out, "out", torch.bfloat16, 3, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    return h, lq, hd, k.shape[1], cu_q.shape[0] - 1, out
+
+
+def moga_group_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_q: torch.Tensor,
+                    cu_k: torch.Tensor, row_scale: Optional[torch.Tensor] = None,
+                    softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Varlen group attention: q [H, Lq, hd], k/v [H, Lk, hd] bf16; cu_q/cu_k int32 [S+1]."""
+    h, lq, hd, lk, n_seg, out = _group_attn_args(q, k, v, cu_q, cu_k, row_scale, out)
     dims = make_dims(max(lq, 1), 1, h, hd, 1, softmax_scale=softmax_scale)
     nb = _lib().moga_group_attn_workspace_bytes(ctypes.byref(dims), n_seg, lq)
     if nb == 0:
@@ -202,6 +208,20 @@ def moga_group_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_q: tor
     check(_lib().moga_group_attn(_ptr(q), _ptr(k), _ptr(v), lq, lk, n_seg, _ptr(cu_q), _ptr(cu_k),
                                  _ptr(row_scale), ctypes.byref(dims), _ptr(out), _ptr(ws),
                                  ws.numel(), _stream()))
+    return out
+
+
+def moga_group_attn_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            cu_q: torch.Tensor, cu_k: torch.Tensor,
+                            row_scale: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moga_group_attn with the library's static scratch instead of a workspace (pass `out`
+    to allocate nothing at all).  Calls that overlap on one device race."""
+    h, lq, hd, lk, n_seg, out = _group_attn_args(q, k, v, cu_q, cu_k, row_scale, out)
+    dims = make_dims(max(lq, 1), 1, h, hd, 1, softmax_scale=softmax_scale)
+    check(_lib().moga_group_attn_noalloc(_ptr(q), _ptr(k), _ptr(v), lq, lk, n_seg, _ptr(cu_q),
+                                         _ptr(cu_k), _ptr(row_scale), ctypes.byref(dims),
+                                         _ptr(out), _stream()))
     return out
 
 

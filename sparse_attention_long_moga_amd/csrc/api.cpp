@@ -332,6 +332,72 @@ moga_status run_stga(const void *q, const void *k, const void *v, const moga_dim
     return MOGA_OK;
 }
 
+moga_status check_group_attn(const void *q, const void *k, const void *v, int64_t len_q,
+                             int64_t len_k, int32_t n_seg, const int32_t *cu_q,
+                             const int32_t *cu_k, const moga_dims *dims, const void *o,
+                             size_t *need) {
+    moga_status st = check_dims(dims);
+    if (st != MOGA_OK) return st;
+    if (!q || !k || !v || !o || !cu_q || !cu_k) return fail(MOGA_ERR_ARG, "a required pointer is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(MOGA_ERR_ARG, "q, k, v and o must be 16-byte aligned");
+    if (len_q < 0 || len_q >= (int64_t(1) << 31) || len_k < 0 || len_k >= (int64_t(1) << 31))
+        return fail(MOGA_ERR_ARG, "len_q/len_k outside [0, 2^31)");
+    if (n_seg < 1) return fail(MOGA_ERR_ARG, "n_seg %d < 1", n_seg);
+    const int64_t items = attn_max_items(dims->n_heads, len_q, n_seg);
+    if (items >= (int64_t(1) << 31)) return fail(MOGA_ERR_ARG, "too many work items");
+    *need = attn_plan_bytes(n_seg, items, split_rows(dims, len_q));
+    return MOGA_OK;
+}
+
+// The launch of moga_group_attn on a validated call; plan_mem holds attn_plan_bytes of room.
+moga_status run_group_attn(const void *q, const void *k, const void *v, int64_t len_q,
+                           int64_t len_k, int32_t n_seg, const int32_t *cu_q, const int32_t *cu_k,
+                           const float *row_scale, const moga_dims *dims, void *o,
+                           void *plan_mem, hipStream_t s) {
+    const int64_t items = attn_max_items(dims->n_heads, len_q, n_seg);
+    // long segments on average: 256-row query tiles; short ones: 128
+    const int waves = len_q / n_seg >= 1024 ? 8 : 4;
+    return run_attn(q, k, v, o, cu_q, cu_k, n_seg, nullptr, nullptr, row_scale, len_q, len_k, len_q,
+                    len_k, len_q, dims, plan_mem, n_seg, items, waves, s);
+}
+
+// ---------------------------------------------------------------- library-owned scratch
+// moga_group_attn_noalloc keeps its attention plan (segment tables, work list, dispatch
+// counters and the split parts' rows) in this array instead of a caller workspace.  Every
+// device the library runs on holds its own copy until the process ends, and every call on a
+// device shares it.  On the host the array's name denotes a host-side stand-in, so host code
+// only ever uses the device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(40) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[64];
+
+// Device address of the current device's copy of `scratch`, looked up once per device with
+// that device current.
+moga_status scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(MOGA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] {
+        void *p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess) slot.ptr = p;
+    });
+    if (slot.err != hipSuccess) return hip_fail(slot.err, "hipGetSymbolAddress(scratch)");
+    if (!slot.ptr || (reinterpret_cast<uintptr_t>(slot.ptr) & 255u) != 0)
+        return fail(MOGA_ERR_HIP, "static scratch has no 256-byte aligned device address");
+    *out = slot.ptr;
+    return MOGA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -397,23 +463,32 @@ moga_status moga_group_attn(const void *q, const void *k, const void *v, int64_t
                             int64_t len_k, int32_t n_seg, const int32_t *cu_q,
                             const int32_t *cu_k, const float *row_scale, const moga_dims *dims,
                             void *o, void *ws, size_t ws_bytes, void *stream) {
-    moga_status st = check_dims(dims);
+    size_t need = 0;
+    moga_status st = check_group_attn(q, k, v, len_q, len_k, n_seg, cu_q, cu_k, dims, o, &need);
     if (st != MOGA_OK) return st;
-    if (!q || !k || !v || !o || !cu_q || !cu_k) return fail(MOGA_ERR_ARG, "a required pointer is NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-        return fail(MOGA_ERR_ARG, "q, k, v and o must be 16-byte aligned");
-    if (len_q < 0 || len_q >= (int64_t(1) << 31) || len_k < 0 || len_k >= (int64_t(1) << 31))
-        return fail(MOGA_ERR_ARG, "len_q/len_k outside [0, 2^31)");
-    if (n_seg < 1) return fail(MOGA_ERR_ARG, "n_seg %d < 1", n_seg);
-    const int64_t items = attn_max_items(dims->n_heads, len_q, n_seg);
-    if (items >= (int64_t(1) << 31)) return fail(MOGA_ERR_ARG, "too many work items");
-    const size_t need = attn_plan_bytes(n_seg, items, split_rows(dims, len_q));
     if ((st = check_ws(ws, ws_bytes, need)) != MOGA_OK) return st;
     if ((st = check_device()) != MOGA_OK) return st;
-    // long segments on average: 256-row query tiles; short ones: 128
-    const int waves = len_q / n_seg >= 1024 ? 8 : 4;
-    return run_attn(q, k, v, o, cu_q, cu_k, n_seg, nullptr, nullptr, row_scale, len_q, len_k, len_q,
-                    len_k, len_q, dims, ws, n_seg, items, waves, static_cast<hipStream_t>(stream));
+    return run_group_attn(q, k, v, len_q, len_k, n_seg, cu_q, cu_k, row_scale, dims, o, ws,
+                          static_cast<hipStream_t>(stream));
+}
+
+moga_status moga_group_attn_noalloc(const void *q, const void *k, const void *v, int64_t len_q,
+                                    int64_t len_k, int32_t n_seg, const int32_t *cu_q,
+                                    const int32_t *cu_k, const float *row_scale,
+                                    const moga_dims *dims, void *o, void *stream) {
+    size_t need = 0;
+    moga_status st = check_group_attn(q, k, v, len_q, len_k, n_seg, cu_q, cu_k, dims, o, &need);
+    if (st != MOGA_OK) return st;
+    if (need > kNoAllocScratchBytes)
+        return fail(MOGA_ERR_WORKSPACE,
+                    "moga_group_attn_noalloc: the attention plan needs %zu bytes and the "
+                    "library's static scratch holds %zu (use moga_group_attn with a workspace)",
+                    need, kNoAllocScratchBytes);
+    if ((st = check_device()) != MOGA_OK) return st;
+    void *scratch_dev = nullptr;
+    if ((st = scratch_address(&scratch_dev)) != MOGA_OK) return st;
+    return run_group_attn(q, k, v, len_q, len_k, n_seg, cu_q, cu_k, row_scale, dims, o,
+                          scratch_dev, static_cast<hipStream_t>(stream));
 }
 
 moga_status stga_group_attn(const void *q, const void *k, const void *v, const moga_dims *dims,
