@@ -21,6 +21,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -780,7 +781,7 @@ __global__ __launch_bounds__(256) void attn_split_combine(AttnLaunch a, int bq) 
         make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
 }
 
-int g_num_cus[64];  // per device
+std::atomic<int> g_num_cus[kMaxDevices];  // per device; 0 until first queried
 
 }  // namespace
 
@@ -788,15 +789,16 @@ hipError_t device_cus(int *out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (g_num_cus[dev] == 0) {
-        int n = 0;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int n = g_num_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        // concurrent first calls may both query; they store the same value
         if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) !=
             hipSuccess)
             return e;
-        g_num_cus[dev] = n;
+        g_num_cus[dev].store(n, std::memory_order_relaxed);
     }
-    *out = g_num_cus[dev];
+    *out = n;
     return hipSuccess;
 }
 

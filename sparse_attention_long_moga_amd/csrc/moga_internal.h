@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace moga {
 
 typedef __bf16 bf16;
@@ -23,8 +25,29 @@ constexpr int kPlanSortMax = 4096; // segments sorted by key length up to this c
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Compute units of the current device (cached per device).
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device (cached per device; thread-safe).
 hipError_t device_cus(int *n);
+
+// A set-up step run once per device, with that device current, the first time any thread asks
+// for it there; later calls return the first call's status.  Thread-safe.
+class DeviceOnce {
+  public:
+    template <typename F>
+    hipError_t run(F &&f) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+        std::call_once(flag_[dev], [&] { status_[dev] = f(); });
+        return status_[dev];
+    }
+
+  private:
+    std::once_flag flag_[kMaxDevices];
+    hipError_t status_[kMaxDevices] = {};
+};
 
 // ---------------------------------------------------------------- router
 struct RouteLaunch {

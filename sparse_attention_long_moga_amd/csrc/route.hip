@@ -18,13 +18,16 @@
 // them by W^T staged once per block in LDS, and reduces the per-lane partial logits across
 // the wave.  Group statistics are kept per lane (lane i owns group i).
 #include <algorithm>
+#include <atomic>
 
 #include "moga_internal.h"
 
 namespace moga {
 namespace {
 
-constexpr int kRouteLdsBytes = 64 * 1024;
+// dynamic LDS of the vector router (W^T, or a chunk of its columns): with the kernel's 3 KiB of
+// static reduction arrays the block stays within 64 KiB
+constexpr int kRouteLdsBytes = 60 * 1024;
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -791,14 +794,14 @@ hipError_t launch_stage(const RouteLaunch &a, size_t lds, hipStream_t s) {
     hipError_t e = device_cus(&cus);
     if (e != hipSuccess) return e;
     const size_t smem = ((lds + 1023) & ~(size_t)1023) + (size_t)NW * 16 * UB;
-    static bool attr_set = false;  // the largest image: kRouteLdsW + NW x 16 UB
-    if (!attr_set) {
-        if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&route_stage_kernel<NW, NH, UB>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     kRouteLdsW + NW * 16 * UB)) != hipSuccess)
-            return e;
-        attr_set = true;
-    }
+    // once per device (and thread-safe): allow the largest image, kRouteLdsW + NW x 16 UB
+    static DeviceOnce attr;
+    if ((e = attr.run([] {
+             return hipFuncSetAttribute(
+                 reinterpret_cast<const void *>(&route_stage_kernel<NW, NH, UB>),
+                 hipFuncAttributeMaxDynamicSharedMemorySize, kRouteLdsW + NW * 16 * UB);
+         })) != hipSuccess)
+        return e;
     // one block of NW waves per CU, at least one tile (16 tokens) per wave (short inputs still
     // spread over every CU), and no more waves than rows of partial statistics
     const int64_t n_tiles = (a.n + 15) / 16;
@@ -814,18 +817,23 @@ hipError_t launch_stage(const RouteLaunch &a, size_t lds, hipStream_t s) {
 
 template <int MT, int T, int U>
 hipError_t launch_mfma(const RouteLaunch &a, hipStream_t s) {
-    static int blocks_per_cu = 0;  // occupancy of this instantiation (same on every gfx950)
+    // occupancy of this instantiation, queried once per device (thread-safe)
+    static DeviceOnce occ;
+    static std::atomic<int> occ_blocks[kMaxDevices];
     int cus = 0;
     hipError_t e = device_cus(&cus);
     if (e != hipSuccess) return e;
-    if (blocks_per_cu == 0) {
-        int b = 0;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                 &b, reinterpret_cast<const void *>(&route_mfma_kernel<MT, T, U>), 256, 0)) !=
-            hipSuccess)
-            return e;
-        blocks_per_cu = b > 0 ? b : 1;
-    }
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = occ.run([dev] {
+             int b = 0;
+             const hipError_t r = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                 &b, reinterpret_cast<const void *>(&route_mfma_kernel<MT, T, U>), 256, 0);
+             occ_blocks[dev].store(b > 0 ? b : 1);
+             return r;
+         })) != hipSuccess)
+        return e;
+    const int blocks_per_cu = occ_blocks[dev].load();
     const int steps = (a.d + 31) / 32;
     const int64_t frags = (int64_t)MT * steps * 64;
     int *queue = reinterpret_cast<int *>(a.wsplit);
