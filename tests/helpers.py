@@ -27,5 +27,23 @@ def assert_close_bf16(out, ref, what="", max_abs=MAX_ABS, rrms=REL_RMS):
     return err, r
 
 
+def assert_close_per_group(out, ref, keys, what="", rrms=REL_RMS, min_rows=1):
+    """Relative RMS per label of `keys` (one label per row, e.g. (head, group) pairs encoded
+    as integers): the outputs of a large group are small (a softmax over many keys averages
+    the values down), so a global figure can hide an error confined to one group."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    keys = np.asarray(keys)
+    worst = 0.0
+    for key in np.unique(keys):
+        sel = keys == key
+        if sel.sum() < min_rows:
+            continue
+        r = rel_rms(out[sel], ref[sel])
+        worst = max(worst, r)
+        assert r <= rrms, f"{what}: relative RMS {r:.3e} > {rrms} for label {key}"
+    return worst
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy() if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()

@@ -195,6 +195,21 @@ def test_full_size_backward(wl):
     assert_grad_close(host(grads["dx"][torch.from_numpy(t).to(DEV)]), dx_ref,
                       f"{wl.name} dx rows")
 
+    # dk and dv of sampled key rows of the two smallest groups, last head (the oracle needs the
+    # softmax row of every query of a key's group: |G|^2 hd per (head, group))
+    sizes = np.bincount(g, minlength=m)
+    smallest = [int(i) for i in np.argsort(sizes, kind="stable") if sizes[i] > 0][:2]
+    krows_t = np.concatenate([rng.choice(np.flatnonzero(g == gi), size=min(6, int(sizes[gi])),
+                                         replace=False) for gi in smallest]).astype(np.int64)
+    hl = nh - 1
+    qh, kh, vh, gh = (host(t[hl:hl + 1]) for t in (q, k, v, dout))
+    dk_ref, dv_ref = oracle.moga_dkdv_rows(qh, kh, vh, gh, g, m, r["p_sel"], scale,
+                                           np.zeros(krows_t.size, np.int32), krows_t)
+    del qh, kh, vh, gh
+    kt = torch.from_numpy(krows_t).to(DEV)
+    assert_grad_close(host(grads["dk"][hl][kt]), dk_ref, f"{wl.name} dk rows (groups {smallest})")
+    assert_grad_close(host(grads["dv"][hl][kt]), dv_ref, f"{wl.name} dv rows (groups {smallest})")
+
     # group sums at full size, two heads
     gd = torch.from_numpy(g.astype(np.int64)).to(DEV)
     psel = fwd["p_sel"]

@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 from sparse_attention_long_moga_amd import api
-from tests.helpers import assert_close_bf16, host
+from tests.helpers import assert_close_bf16, assert_close_per_group, host
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -59,6 +59,7 @@ def test_full_size_forward(wl):
         lay = api.make_stga_layout(**grid)
     got = api.moga_forward(x, w, q, k, v, m, alpha=wl.alpha, pin=pin, stga=lay)
     torch.cuda.synchronize()
+    x_all = x if wl.hybrid else None  # the hybrid check runs the MoGA-only forward again
     del x
 
     # routing, groups, loss: every token
@@ -78,13 +79,29 @@ def test_full_size_forward(wl):
     kh = np.stack([host(k[i]) for i in heads])
     vh = np.stack([host(v[i]) for i in heads])
     scale = 1.0 / math.sqrt(hd)
-    want, _ = oracle.moga_attn(qh, kh, vh, ref["group_id"], m, ref["p_sel"], scale, rows_h, rows_t)
+    want_m, _ = oracle.moga_attn(qh, kh, vh, ref["group_id"], m, ref["p_sel"], scale, rows_h,
+                                 rows_t)
+    want = want_m
     if wl.hybrid:
         wt, _ = oracle.stga_attn(qh, kh, vh, grid, "temporal", scale, rows_h, rows_t)
         wf, _ = oracle.stga_attn(qh, kh, vh, grid, "frame", scale, rows_h, rows_t)
-        want = (want + wt + wf) / 3.0
-    out = got["out"]
+        want = (want_m + wt + wf) / 3.0
     gh = torch.tensor([heads[i] for i in rows_h], device=DEV)
     gt = torch.from_numpy(rows_t).to(DEV)
-    have = host(out[gh, gt])
-    assert_close_bf16(have, want, f"{wl.name} sampled rows ({rows_t.size // len(heads)} tokens x 2 heads)")
+    what = f"{wl.name} sampled rows ({rows_t.size // len(heads)} tokens x 2 heads)"
+    assert_close_bf16(host(got["out"][gh, gt]), want, what)
+    # the MoGA rows per (head, group): in the hybrid mean the larger STGA rows would hide an
+    # error confined to the MoGA branch, so there the MoGA-only forward of the same inputs and
+    # the two STGA branches are checked on their own
+    label = rows_h * m + ref["group_id"][rows_t]
+    if wl.hybrid:
+        del got
+        moga = api.moga_forward(x_all, w, q, k, v, m, alpha=wl.alpha, pin=pin)["out"]
+        o_t, o_f = api.stga_group_attn(q, k, v, lay)
+        torch.cuda.synchronize()
+        assert_close_per_group(host(moga[gh, gt]), want_m, label, what + " MoGA branch")
+        del moga
+        assert_close_bf16(host(o_t[gh, gt]), wt, what + " temporal branch")
+        assert_close_bf16(host(o_f[gh, gt]), wf, what + " per-frame branch")
+    else:
+        assert_close_per_group(host(got["out"][gh, gt]), want_m, label, what)

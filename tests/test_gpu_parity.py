@@ -9,7 +9,7 @@ import torch
 import oracle
 import workloads
 from sparse_attention_long_moga_amd import api
-from tests.helpers import assert_close_bf16, host
+from tests.helpers import assert_close_bf16, assert_close_per_group, host
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -42,6 +42,22 @@ def _router_case(n, d, m, seed, x_dtype="bf16", dirichlet=None):
     (70000, 1536, 5, "bf16", 12),    # many waves, each over a range of 16-token tiles
     (3000, 512, 16, "bf16", 13),     # sixteen groups: every lane of the row-contiguous kernel
     (500, 768, 1, "bf16", 14),       # one group in bf16: p == 1
+    # bf16 x whose three-term W image exceeds the LDS budget with M <= 16: W streamed from L2
+    # in fragments (the Wan2.1-14B width, 5120, with the pages' M = 5, and M = 16)
+    (3000, 5120, 5, "bf16", 21),
+    (2000, 5120, 16, "bf16", 22),
+    # f32 x at every group-count instantiation of the vector router
+    (2500, 256, 5, "f32", 23),
+    (2500, 256, 8, "f32", 24),
+    (1500, 512, 16, "f32", 25),
+    (1500, 300, 20, "f32", 26),
+    (1000, 256, 32, "f32", 27),
+    (700, 128, 64, "f32", 28),
+    # f32 x with W^T larger than the LDS budget: W staged in chunks of columns (a partial last
+    # chunk for d = 4100)
+    (600, 5120, 5, "f32", 29),
+    (500, 4100, 20, "f32", 30),
+    (400, 1024, 64, "f32", 31),
 ])
 def test_route_parity(n, d, m, x_dtype, seed):
     _announce("route", n=n, d=d, m=m, x_dtype=x_dtype)
@@ -278,13 +294,19 @@ def test_forward_parity(hybrid, hd):
     h = q.shape[0]
     rows_h, rows_t = np.repeat(np.arange(h), n), np.tile(np.arange(n), h)
     qh, kh, vh = host(q), host(k), host(v)
-    ref, _ = oracle.moga_attn(qh, kh, vh, ref_r["group_id"], m, ref_r["p_sel"], scale, rows_h,
-                              rows_t)
+    ref_m, _ = oracle.moga_attn(qh, kh, vh, ref_r["group_id"], m, ref_r["p_sel"], scale, rows_h,
+                                rows_t)
+    ref = ref_m
     if hybrid:
         rt, _ = oracle.stga_attn(qh, kh, vh, grid, "temporal", scale, rows_h, rows_t)
         rf, _ = oracle.stga_attn(qh, kh, vh, grid, "frame", scale, rows_h, rows_t)
-        ref = (ref + rt + rf) / 3.0
+        ref = (ref_m + rt + rf) / 3.0
     assert_close_bf16(host(got["out"]).reshape(-1, hd), ref, f"forward hybrid={hybrid}")
+    # per (head, group), on the MoGA output alone (in the hybrid mean the STGA rows dominate)
+    moga = got["out"] if not hybrid else api.moga_forward(x, w, q, k, v, m, alpha=0.1, pin=pin)["out"]
+    torch.cuda.synchronize()
+    assert_close_per_group(host(moga).reshape(-1, hd), ref_m, rows_h * m + ref_r["group_id"][rows_t],
+                           f"forward hybrid={hybrid} MoGA rows per (head, group)")
 
 
 def test_forward_collapse_and_single_group():
