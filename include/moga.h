@@ -109,7 +109,8 @@ typedef struct {
     float *lse;           /* optional [H][N] fp32, token order: natural log of the softmax
                              normaliser of the token's MoGA attention row,
                              log sum_u exp(scale q.k_u) over its group's keys; the state
-                             moga_backward needs besides out */
+                             moga_backward needs besides out.  MoGA only: with a STGA
+                             layout the call returns MOGA_ERR_UNSUPPORTED if lse is set */
 } moga_outputs;
 
 const char *moga_last_error(void);

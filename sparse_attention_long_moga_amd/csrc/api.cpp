@@ -534,6 +534,10 @@ static moga_status forward_impl(const moga_inputs *in, const moga_dims *dims, co
         return fail(MOGA_ERR_ARG, "q, k, v and out must be 16-byte aligned");
     StgaGeom g;
     if (stga && (st = check_stga(dims, stga, &g)) != MOGA_OK) return st;
+    if (stga && out->lse)
+        return fail(MOGA_ERR_UNSUPPORTED,
+                    "lse is the MoGA branch's softmax normaliser, which moga_backward pairs with a "
+                    "MoGA-only out; it is not returned beside a hybrid (STGA) out");
     const Layout L = make_layout(dims, stga ? &g : nullptr);
     if ((st = check_ws(ws, ws_bytes, L.total)) != MOGA_OK) return st;
     if ((st = check_device()) != MOGA_OK) return st;

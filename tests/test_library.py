@@ -158,3 +158,20 @@ def test_backward_argument_checks(lib):
     assert call(d128, w=16) == _capi.MOGA_ERR_WORKSPACE
     assert call(d128, wsp=None) == _capi.MOGA_ERR_WORKSPACE
     assert lib.moga_backward_workspace_bytes(ctypes.byref(_dims(n_groups=0))) == 0
+
+
+def test_hybrid_forward_refuses_lse(lib):
+    """lse belongs to a MoGA-only out (moga_backward pairs the two), so a hybrid forward that
+    asks for it is refused before any launch."""
+    from sparse_attention_long_moga_amd._capi import MogaInputs, MogaOutputs
+    n = 4 * 6 * 8
+    d = _dims(n_tokens=n)
+    lay = make_stga_layout(4, 6, 8, [0, 2, 4], 3, 4, 2, 2)
+    p = 256
+    ins = MogaInputs(p, 1, p, p, p, p, None)
+    outs = MogaOutputs(p, p, None, None, None, None, None, None, p)
+    for fn in (lib.moga_forward, lib.moga_forward_fused):
+        st = fn(ctypes.byref(ins), ctypes.byref(d), lay.ref(), ctypes.byref(outs),
+                ctypes.c_void_p(256), 1 << 40, None)
+        assert st == _capi.MOGA_ERR_UNSUPPORTED
+        assert "lse" in lib.moga_last_error().decode()
