@@ -188,7 +188,8 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
 
     n, h, hd, m = wl.n_tokens, wl.n_heads, wl.head_dim, wl.n_groups
     stream = torch.cuda.current_stream()
-    names = ["route", "permute", "group_attn", "unpermute", "loss"] + (["stga"] if lay else [])
+    names = ["route", "histogram", "permute", "group_attn", "unpermute", "loss"] + (
+        ["stga"] if lay else [])
     acc = {s: [] for s in names}
     log(f"stage breakdown over {args.steps} passes")
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=x.device)
@@ -200,6 +201,8 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
     torch.cuda.synchronize()
     calls = {
         "route": (lambda: api.moga_route(x, w, m, ws=ws), STAGE_REPS),
+        # the index build alone (histogram, scan, stable scatter of perm): no tensors moved
+        "histogram": (lambda: api.moga_permute(r["group_id"], [], m, ws=ws), STAGE_REPS),
         "permute": (lambda: api.moga_permute(r["group_id"], [q, k, v], m, p_sel=r["p_sel"], ws=ws),
                     STAGE_REPS),
         "group_attn": (lambda: api.moga_group_attn(qp, kp, vp, cu, cu, row_scale=pp, ws=ws), 1),
@@ -229,16 +232,19 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
     route_bytes = x_bytes + wl.d_model * m * 4 + n * 8
     permute_bytes = 6 * e_bytes + n * 4 * 2 + n * 8
     unpermute_bytes = 2 * e_bytes + n * 4
+    histogram_bytes = n * 4 + n * 4 + (m + 1) * 4  # group ids read, perm and cu_seqlens written
     attn_tflops = attn_flops / (ms["group_attn"] / 1e3) / 1e12
     stages = {
         "stage_ms": ms,
         "attn_tflops": attn_tflops,
         "attn_frac_of_bf16_peak": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
         "route_gbs": route_bytes / (ms["route"] / 1e3) / 1e9,
+        "histogram_gbs": histogram_bytes / (ms["histogram"] / 1e3) / 1e9,
         "permute_gbs": permute_bytes / (ms["permute"] / 1e3) / 1e9,
         "unpermute_gbs": unpermute_bytes / (ms["unpermute"] / 1e3) / 1e9,
     }
     stages["route_frac_of_hbm"] = stages["route_gbs"] / HBM_PEAK_GBS
+    stages["histogram_frac_of_hbm"] = stages["histogram_gbs"] / HBM_PEAK_GBS
     stages["permute_frac_of_hbm"] = stages["permute_gbs"] / HBM_PEAK_GBS
     stages["unpermute_frac_of_hbm"] = stages["unpermute_gbs"] / HBM_PEAK_GBS
     stages["roofline"] = {
@@ -422,6 +428,19 @@ def stga_pairs_closed_form(g):
     return pairs + g["frames"] * hw * hw
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(wl, x, w, q, k, v, target_s):
     """Oracle rate on a bounded sample: routing, groups and loss on every token, MoGA
     attention on seeded (head, token) rows, extrapolated by row count."""
@@ -467,7 +486,8 @@ def cpu_baseline(wl, x, w, q, k, v, target_s):
     per_row = used / timed_rows
     total = t_route + per_row * h * n
     return {
-        "value": n / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "value": n / total, "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(),
+        "kind": "oracle",
         "sample": (f"route + groups + loss on all {n} tokens ({t_route:.1f} s); MoGA attention "
                    f"on {timed_rows} seeded (head, token) rows of {h * n} ({used:.1f} s), "
                    f"extrapolated by row count to {total:.0f} s for the whole forward"),
