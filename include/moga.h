@@ -197,17 +197,18 @@ moga_status moga_balance_loss(const int32_t *counts, const double *prob_sum,
                               const moga_dims *dims, double *loss, double *F, double *P,
                               void *stream);
 
-/* The whole forward: route -> permute -> group attention scaled by p(g|x) ->
- * inverse permute, plus the balance loss; with stga non-NULL, out is the mean of
- * the MoGA output and the two STGA outputs (computed in fp32, rounded once).
- * ws: moga_workspace_bytes(dims, stga). */
+/* The whole forward: route -> permute -> group attention scaled by p(g|x), whose epilogue
+ * writes every row straight back to its token (the inverse permute), plus the balance loss.
+ * With stga non-NULL the two STGA branches run first (each rounded to bf16 as it is stored in
+ * the workspace) and out is the mean of the three rows, taken in fp32 in the MoGA epilogue
+ * from the unrounded MoGA row and rounded to bf16 once.  ws: moga_workspace_bytes(dims, stga). */
 moga_status moga_forward(const moga_inputs *in, const moga_dims *dims, const stga_layout *stga,
                          const moga_outputs *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Permute-free variant of moga_forward, for the same inputs and outputs: the attention
  * kernel reads the query, key and value rows of each group through perm and writes every
- * output row straight back to its token, so the permuted copies of Q, K, V and O and the
- * two row gathers are skipped.  Keys are visited in the same order, so every output is
+ * output row straight back to its token (as moga_forward's epilogue does too), so the
+ * permuted copies of Q, K and V and their gather are skipped.  Keys are visited in the same order, so every output is
  * bitwise identical to moga_forward's.  perm and cu_seqlens are still computed (and
  * returned if requested).  ws: moga_workspace_bytes(dims, stga). */
 moga_status moga_forward_fused(const moga_inputs *in, const moga_dims *dims,

@@ -137,7 +137,7 @@ struct Carver {
 struct Layout {
     // MoGA
     size_t part_p, part_c, wsplit, gid, psel, counts, probsum, cu, perm, table, base_rel, totals, pperm;
-    size_t qp, kp, vp, op, lsep, plan;
+    size_t qp, kp, vp, plan;
     // STGA
     size_t shot_info, cu_tq, cu_tk, cu_f, q_idx, kv_idx, ot, of;
     int32_t plan_seg;
@@ -168,8 +168,6 @@ Layout make_layout(const moga_dims *d, const StgaGeom *g) {
     L.qp = c.take(tensor);
     L.kp = c.take(tensor);
     L.vp = c.take(tensor);
-    L.op = c.take(tensor);
-    L.lsep = c.take(sizeof(float) * d->n_heads * n);
     int32_t seg = m;
     int64_t items = attn_max_items(d->n_heads, n, m);
     if (g) {
@@ -284,12 +282,20 @@ moga_status run_gather(int inverse, const int32_t *perm, const moga_dims *d,
     return MOGA_OK;
 }
 
+// Optional parts of an attention launch's epilogue: output rows through a map, the log-sum-exp,
+// and the mean with two other branches' rows.
+struct AttnEpilogue {
+    const int32_t *o_idx = nullptr;
+    float *lse = nullptr;
+    const void *mean_a = nullptr, *mean_b = nullptr;
+};
+
 moga_status run_attn(const void *q, const void *k, const void *v, void *o, const int32_t *cu_q,
                      const int32_t *cu_k, int32_t n_seg, const int32_t *q_idx,
                      const int32_t *kv_idx, const float *row_scale, int64_t len_q, int64_t len_k,
                      int64_t q_rows, int64_t kv_rows, int64_t o_rows, const moga_dims *d,
                      void *plan_mem, int32_t plan_seg, int64_t plan_items, int waves,
-                     hipStream_t s, float *lse = nullptr) {
+                     hipStream_t s, const AttnEpilogue &ep = AttnEpilogue()) {
     AttnLaunch a{};
     a.q = static_cast<const bf16 *>(q); a.k = static_cast<const bf16 *>(k);
     a.v = static_cast<const bf16 *>(v); a.o = static_cast<bf16 *>(o);
@@ -299,7 +305,10 @@ moga_status run_attn(const void *q, const void *k, const void *v, void *o, const
     a.n_heads = d->n_heads; a.head_dim = d->head_dim; a.scale = scale_of(d);
     a.max_items = attn_max_items(d->n_heads, len_q, n_seg);
     a.waves = waves;
-    a.lse = lse;
+    a.lse = ep.lse;
+    a.o_idx = ep.o_idx;
+    a.mean_a = static_cast<const bf16 *>(ep.mean_a);
+    a.mean_b = static_cast<const bf16 *>(ep.mean_b);
     if (a.max_items > plan_items || n_seg > plan_seg)
         return fail(MOGA_ERR_WORKSPACE, "attention plan larger than its workspace region");
     attn_plan_carve(a.plan, plan_mem, n_seg, a.max_items, split_rows(d, len_q));
@@ -557,45 +566,39 @@ static moga_status forward_impl(const moga_inputs *in, const moga_dims *dims, co
                         L, s)) != MOGA_OK)
         return st;
     if ((st = run_perm_index(gid, dims, cu, perm, ws, L, s)) != MOGA_OK) return st;
-    if (fused) {
-        // 3-5 in one pass: rows are read through perm and written back in token order
-        if ((st = run_attn(in->q, in->k, in->v, out->out, cu, cu, dims->n_groups, perm, perm, psel,
-                           n, n, n, n, n, dims, plan, L.plan_seg, L.plan_items, 8, s,
-                           out->lse)) != MOGA_OK)
-            return st;
-    } else {
-        // 3 gather Q, K, V and p by perm  4 varlen group attention scaled by p(g|x)
-        // 5 back to token order
-        float *pperm = at<float>(ws, L.pperm);
-        void *qp = at<char>(ws, L.qp), *kp = at<char>(ws, L.kp), *vp = at<char>(ws, L.vp);
-        void *op = at<char>(ws, L.op);
-        const void *src[3] = {in->q, in->k, in->v};
-        void *dst[3] = {qp, kp, vp};
-        if ((st = run_gather(0, perm, dims, src, dst, 3, psel, pperm, s)) != MOGA_OK) return st;
-        float *lsep = out->lse ? at<float>(ws, L.lsep) : nullptr;
-        if ((st = run_attn(qp, kp, vp, op, cu, cu, dims->n_groups, nullptr, nullptr, pperm, n, n, n,
-                           n, n, dims, plan, L.plan_seg, L.plan_items, 8, s, lsep)) != MOGA_OK)
-            return st;
-        const void *osrc[1] = {op};
-        void *odst[1] = {out->out};
-        if ((st = run_gather(1, perm, dims, osrc, odst, 1, nullptr, nullptr, s)) != MOGA_OK)
-            return st;
-        if (lsep)
-            HIP_TRY(launch_bwd_gather_f32(lsep, perm, n, dims->n_heads, 1.0f, 1, out->lse, s),
-                    "lse scatter launch");
-    }
-    // 6 group-balancing loss
+    // 3 group-balancing loss
     HIP_TRY(launch_balance_loss(counts, probsum, n, dims->n_groups, dims->alpha, out->loss, nullptr,
                                 nullptr, s),
             "loss launch");
-    if (!stga) return MOGA_OK;
-    // 7 STGA branches and the mean of the three outputs
-    void *ot = at<char>(ws, L.ot), *of = at<char>(ws, L.of);
-    if ((st = run_stga(in->q, in->k, in->v, dims, g, ot, of, ws, L, s)) != MOGA_OK) return st;
-    HIP_TRY(launch_combine3(static_cast<const bf16 *>(out->out), static_cast<const bf16 *>(ot),
-                            static_cast<const bf16 *>(of), static_cast<bf16 *>(out->out),
-                            (int64_t)dims->n_heads * n * dims->head_dim, s),
-            "combine launch");
+    // 4 with a STGA layout: the two static branches first, in token order; the MoGA epilogue
+    // then stores the mean of the three rows (in fp32, one rounding)
+    AttnEpilogue ep;
+    if (stga) {
+        void *ot = at<char>(ws, L.ot), *of = at<char>(ws, L.of);
+        if ((st = run_stga(in->q, in->k, in->v, dims, g, ot, of, ws, L, s)) != MOGA_OK) return st;
+        ep.mean_a = ot;
+        ep.mean_b = of;
+    }
+    ep.lse = out->lse;
+    if (fused) {
+        // 5 rows are read through perm and written back in token order
+        if ((st = run_attn(in->q, in->k, in->v, out->out, cu, cu, dims->n_groups, perm, perm, psel,
+                           n, n, n, n, n, dims, plan, L.plan_seg, L.plan_items, 8, s, ep)) !=
+            MOGA_OK)
+            return st;
+    } else {
+        // 5 gather Q, K, V and p by perm, then the varlen group attention scaled by p(g|x),
+        // whose epilogue writes each row straight to its token (no separate inverse permute)
+        float *pperm = at<float>(ws, L.pperm);
+        void *qp = at<char>(ws, L.qp), *kp = at<char>(ws, L.kp), *vp = at<char>(ws, L.vp);
+        const void *src[3] = {in->q, in->k, in->v};
+        void *dst[3] = {qp, kp, vp};
+        if ((st = run_gather(0, perm, dims, src, dst, 3, psel, pperm, s)) != MOGA_OK) return st;
+        ep.o_idx = perm;
+        if ((st = run_attn(qp, kp, vp, out->out, cu, cu, dims->n_groups, nullptr, nullptr, pperm, n,
+                           n, n, n, n, dims, plan, L.plan_seg, L.plan_items, 8, s, ep)) != MOGA_OK)
+            return st;
+    }
     return MOGA_OK;
 }
 

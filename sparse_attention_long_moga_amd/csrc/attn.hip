@@ -413,22 +413,24 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel(AttnLaunch 
 
         // ---- epilogue: 1/l, optional per-row scale, bf16, 8-byte stores of 4 head channels
         const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-        if (a.lse && qvalid && hh == 0)  // log(sum exp(scale q.k)) = scale*m + ln(l)
-            a.lse[(int64_t)h * a.o_rows + qphys] =
-                l_tot > 0.0f ? (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
         if (qvalid) {
+            const int64_t orow = out_row(a, qrow, qphys);
+            if (a.lse && hh == 0)  // log(sum exp(scale q.k)) = scale*m + ln(l)
+                a.lse[(int64_t)h * a.o_rows + orow] =
+                    l_tot > 0.0f ? (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
             float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
             if (a.row_scale) inv *= a.row_scale[qphys];
-            bf16 *op = a.o + (int64_t)h * a.o_rows * HD + qphys * HD + 4 * hh;
+            const int64_t off = (int64_t)h * a.o_rows * HD + orow * HD + 4 * hh;
 #pragma unroll
-            for (int ti = 0; ti < T::NT; ++ti)
+            for (int ti = 0; ti < T::NT; ++ti) {
 #pragma unroll
-                for (int kq = 0; kq < 4; ++kq) {
-                    const uint2 w = make_uint2(
-                        pack_bf16x2(o[ti][kq * 4 + 0] * inv, o[ti][kq * 4 + 1] * inv),
-                        pack_bf16x2(o[ti][kq * 4 + 2] * inv, o[ti][kq * 4 + 3] * inv));
-                    *reinterpret_cast<uint2 *>(op + 32 * ti + 8 * kq) = w;
-                }
+                for (int kq = 0; kq < 4; ++kq)
+                    store4(a, off + 32 * ti + 8 * kq, o[ti][kq * 4 + 0] * inv,
+                           o[ti][kq * 4 + 1] * inv, o[ti][kq * 4 + 2] * inv,
+                           o[ti][kq * 4 + 3] * inv);
+                // one block of 32 columns at a time: the mean rows' loads are not all hoisted
+                asm volatile("" ::: "memory");
+            }
         }
     }
 }
@@ -569,6 +571,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) o[ti] = f32x16{};
 
+        uint4 pf_u[4];  // the tile's probabilities, bf16, in the B-operand layout
         auto tile = [&](auto bufc, auto maskc, int t) {
             constexpr int buf = decltype(bufc)::value;
             constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
@@ -579,16 +582,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
             const unsigned char *kt = lds[buf][0];
             const unsigned char *vt_ = lds[buf][1];
 
+            // S^T for the two 32-key sub-blocks, one accumulation chain each, sub-block 0 first
+            // so that its probabilities can be formed while sub-block 1's products run
             f32x16 sacc[2];
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) sacc[sb] = f32x16{};
+            for (int sb = 0; sb < 2; ++sb) {
+                sacc[sb] = f32x16{};
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
+                for (int s = 0; s < NS; ++s) {
                     const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kt + sb * 32 * ROWB + koff[s]);
                     sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sb], 0, 0, 0);
                 }
+            }
             if constexpr (MASK) {
                 const int key0 = t * KT;
 #pragma unroll
@@ -599,35 +604,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                         if (key >= klen) sacc[sb][v] = -INFINITY;
                     }
             }
-            // row maximum: four max3 chains over 8 scores each, then across the two lane halves
-            // that hold the same query (a VALU lane swap, no LDS round trip)
-            float pm[4];
+            // this lane's largest score of each sub-block (16 keys each)
+            float pm[2];
 #pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const f32x16 &sv = sacc[qd >> 1];
-                const int v0 = 8 * (qd & 1);
-                float m = fmaxf(fmaxf(sv[v0], sv[v0 + 1]), sv[v0 + 2]);
-                m = fmaxf(fmaxf(m, sv[v0 + 3]), sv[v0 + 4]);
-                m = fmaxf(fmaxf(m, sv[v0 + 5]), sv[v0 + 6]);
-                pm[qd] = fmaxf(m, sv[v0 + 7]);
+            for (int sb = 0; sb < 2; ++sb) {
+                const f32x16 &sv = sacc[sb];
+                float m0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+                m0 = fmaxf(fmaxf(m0, sv[3]), sv[4]);
+                m0 = fmaxf(fmaxf(m0, sv[5]), sv[6]);
+                float m1 = fmaxf(fmaxf(sv[8], sv[9]), sv[10]);
+                m1 = fmaxf(fmaxf(m1, sv[11]), sv[12]);
+                m1 = fmaxf(fmaxf(m1, sv[13]), sv[14]);
+                pm[sb] = fmaxf(fmaxf(m0, sv[7]), fmaxf(m1, sv[15]));
             }
-            float tmax = fmaxf(fmaxf(fmaxf(pm[0], pm[1]), pm[2]), pm[3]);
-            tmax = max_across_halves(tmax);
-            const bool up = tmax > m_run + thr;
-            if (__ballot(up)) {
-                const float m_new = up ? tmax : m_run;
-                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int ti = 0; ti < NT; ++ti)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) o[ti][v] *= alpha;
-            }
-            const float mc = m_run * c;
-            bf16x8 pf[4];
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
+            // probabilities of sub-block sb against the running maximum
+            auto probs = [&](int sb, float mc) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     float pv[8];
@@ -636,23 +627,71 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                         pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][half * 8 + e], c, -mc));
                     const uint4 packed = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                                                     pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
-                    // the row sum adds the bf16 probabilities the MFMA multiplies V with,
-                    // two per dot2 instruction
-                    l_run = sum_bf16x2(packed.x, l_run);
-                    l_run = sum_bf16x2(packed.y, l_run);
-                    l_run = sum_bf16x2(packed.z, l_run);
-                    l_run = sum_bf16x2(packed.w, l_run);
-                    pf[sb * 2 + half] = __builtin_bit_cast(bf16x8, packed);
+                    pf_u[sb * 2 + half] = packed;
                 }
+            };
+            // Speculatively, sub-block 0's probabilities are formed against the running maximum
+            // before sub-block 1's scores are known.  They stand unless some score of the tile
+            // exceeds the running maximum by more than the lazy threshold; only then (the first
+            // tile of an item, or a large jump) is the row maximum over the whole tile taken, the
+            // running output rescaled and the probabilities formed again, exactly as a kernel
+            // that always took the maximum first would have done.
+            float mc = m_run * c;
+            probs(0, mc);
+            // keep them here: without this the compiler moves them below the branch, after
+            // sub-block 1's products, which is the serialisation this order avoids
+            asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pf_u[0])),
+                         "v"(__builtin_bit_cast(u32x4, pf_u[1])));
+            const bool up_lane = fmaxf(pm[0], pm[1]) > m_run + thr;
+            // order for the scheduler: sub-block 0's eight K reads, each of its products followed
+            // by one of sub-block 1's reads, then sub-block 1's products each followed by vector
+            // work (sub-block 0's probabilities), so the products never wait on a read just issued
+            // and the exponentials run while the matrix core is busy
+            __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);  // LDS reads
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch)
+            for (int i = 0; i < NS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            }
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+            }
+            if (__ballot(up_lane)) {
+                float tmax = max_across_halves(fmaxf(pm[0], pm[1]));
+                const bool up = tmax > m_run + thr;
+                const float m_new = up ? tmax : m_run;
+                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[ti][v] *= alpha;
+                mc = m_run * c;
+                probs(0, mc);
+            }
+            probs(1, mc);
+            // the row sum adds the bf16 probabilities the MFMA multiplies V with, two per dot2
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                l_run = sum_bf16x2(pf_u[ch].x, l_run);
+                l_run = sum_bf16x2(pf_u[ch].y, l_run);
+                l_run = sum_bf16x2(pf_u[ch].z, l_run);
+                l_run = sum_bf16x2(pf_u[ch].w, l_run);
+            }
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const bf16x8 pfc = __builtin_bit_cast(bf16x8, pf_u[ch]);
 #pragma unroll
                 for (int ti = 0; ti < NT; ++ti) {
                     const unsigned char *vp = vt_ + ch * 16 * ROWB + voff[ti];
                     const uint2 ulo = lds_read_tr16(vp), uhi = lds_read_tr16(vp + 8 * ROWB);
                     const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
-                    o[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ch], o[ti], 0, 0, 0);
+                    o[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfc, o[ti], 0, 0, 0);
                 }
+            }
             // the next tile's direct loads must have landed before anyone reads them
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
             __syncthreads();
@@ -700,22 +739,32 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                 *reinterpret_cast<float2 *>(a.plan.split_ml + 2 * row) = make_float2(m_run, l_tot);
             continue;
         }
-        if (a.lse && qvalid && hh == 0)  // log(sum exp(scale q.k)) = scale*m + ln(l)
-            a.lse[(int64_t)h * a.o_rows + qphys] =
-                l_tot > 0.0f ? (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
         if (qvalid) {
+            // the 8-wave (MoGA) launches may write through an output map, with the log-sum-exp
+            // and the mean of three branches; the 4-wave (short-segment) launches store plainly
+            constexpr bool FULL_EPI = WAVES == 8;
+            const int64_t orow = FULL_EPI ? out_row(a, qrow, qphys) : qphys;
+            if (FULL_EPI && a.lse && hh == 0)  // log(sum exp(scale q.k)) = scale*m + ln(l)
+                a.lse[(int64_t)h * a.o_rows + orow] =
+                    l_tot > 0.0f ? (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
             float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
             if (a.row_scale) inv *= a.row_scale[qphys];
-            bf16 *op = a.o + (int64_t)h * a.o_rows * HD + qphys * HD + 4 * hh;
+            const int64_t off = (int64_t)h * a.o_rows * HD + orow * HD + 4 * hh;
 #pragma unroll
-            for (int ti = 0; ti < NT; ++ti)
+            for (int ti = 0; ti < NT; ++ti) {
 #pragma unroll
                 for (int kq = 0; kq < 4; ++kq) {
-                    const uint2 w = make_uint2(
-                        pack_bf16x2(o[ti][kq * 4 + 0] * inv, o[ti][kq * 4 + 1] * inv),
-                        pack_bf16x2(o[ti][kq * 4 + 2] * inv, o[ti][kq * 4 + 3] * inv));
-                    *reinterpret_cast<uint2 *>(op + 32 * ti + 8 * kq) = w;
+                    const float v0 = o[ti][kq * 4 + 0] * inv, v1 = o[ti][kq * 4 + 1] * inv,
+                                v2 = o[ti][kq * 4 + 2] * inv, v3 = o[ti][kq * 4 + 3] * inv;
+                    if constexpr (FULL_EPI)
+                        store4(a, off + 32 * ti + 8 * kq, v0, v1, v2, v3);
+                    else
+                        *reinterpret_cast<uint2 *>(a.o + off + 32 * ti + 8 * kq) =
+                            make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
                 }
+                // one block of 32 columns at a time: the mean rows' loads are not all hoisted
+                if constexpr (FULL_EPI) asm volatile("" ::: "memory");
+            }
         }
     }
 }
@@ -772,13 +821,14 @@ __global__ __launch_bounds__(256) void attn_split_combine(AttnLaunch a, int bq) 
     }
     const int64_t qphys =
         a.q_idx ? min(max((int64_t)a.q_idx[qrow], (int64_t)0), a.q_rows - 1) : qrow;
+    const int64_t orow = out_row(a, qrow, qphys);
     if (a.lse && col == 0)
-        a.lse[(int64_t)h * a.o_rows + qphys] =
+        a.lse[(int64_t)h * a.o_rows + orow] =
             l > 0.0f ? (m * c + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
     float inv = l > 0.0f ? 1.0f / l : 0.0f;
     if (a.row_scale) inv *= a.row_scale[qphys];
-    *reinterpret_cast<uint2 *>(a.o + (int64_t)h * a.o_rows * HD + qphys * HD + col) =
-        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+    store4(a, (int64_t)h * a.o_rows * HD + orow * HD + col, acc.x * inv, acc.y * inv,
+           acc.z * inv, acc.w * inv);
 }
 
 std::atomic<int> g_num_cus[kMaxDevices];  // per device; 0 until first queried
@@ -857,6 +907,9 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     const bool indexed = a.kv_idx || a.q_idx;
     const bool direct = a.head_dim == 128 && a.kv_rows * 256 < (int64_t(1) << 31);
     const int waves = a.waves == 4 ? 4 : 8;
+    // an output map, the log-sum-exp and the three-branch mean are epilogue features of the
+    // 8-wave launches only
+    if (direct && waves == 4 && (a.o_idx || a.lse || a.mean_a)) return hipErrorInvalidValue;
     const int bq = direct ? 32 * waves : (indexed ? 128 : 256);
     int cus = 0;
     hipError_t e = device_cus(&cus);

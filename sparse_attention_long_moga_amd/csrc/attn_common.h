@@ -121,5 +121,29 @@ __device__ __forceinline__ int t_read_off(int lane, int ti) {
 __device__ __forceinline__ int a_dma_chunk(int r, int s16) { return (s16 ^ (r & 15)) << 4; }
 __device__ __forceinline__ int t_dma_chunk(int r, int s16) { return (s16 ^ (4 * (r & 3))) << 4; }
 
+// Physical output row of logical query row qrow whose query is physical row qphys: the query
+// row itself unless an output map is given (clamped to the head so a bad map cannot address
+// outside it).
+__device__ __forceinline__ int64_t out_row(const AttnLaunch &a, int64_t qrow, int64_t qphys) {
+    return a.o_idx ? min(max((int64_t)a.o_idx[qrow], (int64_t)0), a.o_rows - 1) : qphys;
+}
+
+// Stores four consecutive output channels of one row from their fp32 values: rounded to bf16
+// once, after the mean with the two other branches' rows when the launch asks for it
+// (out = (v + a + b) / 3 in fp32).  off: element offset of the first of the four in o.
+__device__ __forceinline__ void store4(const AttnLaunch &a, int64_t off, float v0, float v1,
+                                       float v2, float v3) {
+    if (a.mean_a) {
+        const uint2 ua = *reinterpret_cast<const uint2 *>(a.mean_a + off);
+        const uint2 ub = *reinterpret_cast<const uint2 *>(a.mean_b + off);
+        constexpr float third = 1.0f / 3.0f;
+        v0 = (v0 + __uint_as_float(ua.x << 16) + __uint_as_float(ub.x << 16)) * third;
+        v1 = (v1 + __uint_as_float(ua.x & 0xffff0000u) + __uint_as_float(ub.x & 0xffff0000u)) * third;
+        v2 = (v2 + __uint_as_float(ua.y << 16) + __uint_as_float(ub.y << 16)) * third;
+        v3 = (v3 + __uint_as_float(ua.y & 0xffff0000u) + __uint_as_float(ub.y & 0xffff0000u)) * third;
+    }
+    *reinterpret_cast<uint2 *>(a.o + off) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+}
+
 }  // namespace
 }  // namespace moga

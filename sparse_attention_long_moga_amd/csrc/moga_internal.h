@@ -135,6 +135,9 @@ struct AttnLaunch {
     const int32_t *q_idx;    // NULL or logical q row -> physical row of q, o and row_scale
     const int32_t *kv_idx;   // NULL or logical kv row -> physical row of k, v
     const float *row_scale;  // NULL or [physical q rows]
+    const int32_t *o_idx;    // NULL: output rows are the physical q rows; else logical q row ->
+                             // physical output row (of o, lse and the mean rows)
+    const bf16 *mean_a, *mean_b;  // NULL, or [H][o_rows][hd] rows stored as (o + a + b) / 3
     int64_t len_q, len_k;    // logical rows
     int64_t q_rows, kv_rows, o_rows;  // physical rows per head
     int n_heads, head_dim;
@@ -210,8 +213,6 @@ int32_t stga_n_groups(const StgaGeom &g);
 int64_t stga_extra_rows(const StgaGeom &g);
 hipError_t launch_stga_index(const StgaGeom &g, const StgaBuffers &b, hipStream_t s);
 
-hipError_t launch_combine3(const bf16 *a, const bf16 *b, const bf16 *c, bf16 *out, int64_t n_elem,
-                           hipStream_t s);
 
 // ---------------------------------------------------------------- loss
 hipError_t launch_balance_loss(const int32_t *counts, const double *prob_sum, int64_t n, int m,

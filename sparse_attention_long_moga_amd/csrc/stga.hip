@@ -1,12 +1,12 @@
-// Spatial-temporal group attention (STGA) index maps, the 3-way mean, and the
-// group-balancing loss.
+// Spatial-temporal group attention (STGA) index maps and the group-balancing loss.
 //
 // STGA (papernotes.org MoGA note, 关键设计 4; jxzklqfsx.com translation, 時空分組注意力;
 // xugj520.cn MoGA blog §3.2 and §9): the latent video is cut into fixed spatial windows,
 // frames are grouped along time inside each shot, and the keys/values (not the queries)
 // of a group that touches a shot boundary also take two latent frames of the adjacent
 // shot.  A second static grouping is the whole frame.  Each token receives one dynamic
-// (MoGA) and two static outputs and takes their mean.
+// (MoGA) and two static outputs and takes their mean (formed in the MoGA attention's
+// epilogue).
 //
 // Temporal groups are enumerated (shot, chunk, window) and every offset has a closed
 // form, so instead of gathering Q/K/V the attention kernel reads rows through two index
@@ -126,32 +126,6 @@ __global__ __launch_bounds__(256) void stga_index_kernel(StgaGeom g, StgaBuffers
     }
 }
 
-__global__ __launch_bounds__(256) void combine3_kernel(const bf16 *a, const bf16 *b,
-                                                        const bf16 *c, bf16 *out, int64_t n8) {
-    const float third = 1.0f / 3.0f;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8;
-         i += (int64_t)gridDim.x * 256) {
-        const uint4 ua = reinterpret_cast<const uint4 *>(a)[i];
-        const uint4 ub = reinterpret_cast<const uint4 *>(b)[i];
-        const uint4 uc = reinterpret_cast<const uint4 *>(c)[i];
-        const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w},
-                       wc[4] = {uc.x, uc.y, uc.z, uc.w};
-        uint32_t wo[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float lo = (__uint_as_float(wa[q] << 16) + __uint_as_float(wb[q] << 16) +
-                              __uint_as_float(wc[q] << 16)) * third;
-            const float hi = (__uint_as_float(wa[q] & 0xffff0000u) +
-                              __uint_as_float(wb[q] & 0xffff0000u) +
-                              __uint_as_float(wc[q] & 0xffff0000u)) * third;
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            bf16x2 r = {(__bf16)lo, (__bf16)hi};
-            wo[q] = __builtin_bit_cast(uint32_t, r);
-        }
-        reinterpret_cast<uint4 *>(out)[i] = make_uint4(wo[0], wo[1], wo[2], wo[3]);
-    }
-}
-
 // Group-balancing loss (papernotes.org MoGA note, 关键设计 3): F_i = n_i / N,
 // P_i = (sum over tokens of p(i|x)) / N, L = alpha * M * sum_i F_i P_i, in fp64.
 __global__ void balance_loss_kernel(const int32_t *counts, const double *prob_sum, int64_t n,
@@ -197,15 +171,6 @@ hipError_t launch_stga_index(const StgaGeom &g, const StgaBuffers &b, hipStream_
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)g.frames * g.height * g.width;
     hipLaunchKernelGGL(stga_index_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g, b);
-    return hipGetLastError();
-}
-
-hipError_t launch_combine3(const bf16 *a, const bf16 *b, const bf16 *c, bf16 *out, int64_t n_elem,
-                           hipStream_t s) {
-    const int64_t n8 = n_elem / 8;
-    int64_t blocks = (n8 + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(combine3_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, b, c, out, n8);
     return hipGetLastError();
 }
 

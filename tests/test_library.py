@@ -121,7 +121,7 @@ def test_stga_work_list_bound(lib):
 def test_workspace_sizes_scale_with_problem(lib):
     small = moga_workspace_bytes(_dims())
     big = moga_workspace_bytes(_dims(n_tokens=8192))
-    assert big > small > 4 * 4 * 4096 * 64 * 2  # at least the permuted Q/K/V/O
+    assert big > small > 3 * 4 * 4096 * 64 * 2  # at least the permuted Q/K/V
 
 
 def test_no_device_reported_as_unsupported(lib):
