@@ -85,6 +85,14 @@ def _load():
     lib.oracle_moga_dkdv_rows.argtypes = [_f32p, _f32p, _f32p, _f32p, c_i64, c_int, _i32p, c_int,
                                           _f64p, c_dbl, c_i64, _i32p, _i64p, _f64p, _f64p]
     lib.oracle_moga_dkdv_rows.restype = c_int
+    lib.oracle_stga_backward.argtypes = [_f32p, _f32p, _f32p, _f32p, c_int, c_int, c_int, c_int,
+                                         c_int, c_int, _i32p, c_int, c_int, c_int, c_int, c_int,
+                                         c_dbl, _f64p, _f64p, _f64p, _f64p]
+    lib.oracle_stga_backward.restype = c_int
+    lib.oracle_stga_bwd_rows.argtypes = [_f32p, _f32p, _f32p, _f32p, c_int, c_int, c_int, c_int,
+                                         c_int, _i32p, c_int, c_int, c_int, c_int, c_int, c_dbl,
+                                         c_i64, _i32p, _i64p, _f64p, _f64p, _f64p, _f64p]
+    lib.oracle_stga_bwd_rows.restype = c_int
     lib.oracle_router_bwd_rows.argtypes = [_f32p, _f32p, c_i64, c_int, c_int, _i32p, _f64p,
                                            _i64p, c_i64, c_dbl, c_dbl, _f64p, _f64p]
     lib.oracle_router_bwd_rows.restype = c_int
@@ -301,6 +309,60 @@ def stga_attn(q, k, v, grid: dict, mode: str, scale: float, rows_h, rows_t):
     if pairs < 0:
         raise ValueError("oracle_stga_attn failed (bad geometry)")
     return out, int(pairs)
+
+
+def stga_backward(q, k, v, d_out, grid: dict, mode: str, scale: float) -> dict:
+    """Gradients of sum <d_out, O> for one STGA branch ('temporal' or 'frame') on whole tensors
+    [H][N][hd]: dq, dk, dv (dk, dv add over every query whose key set holds the key) and lse."""
+    q, k, v, go = _f32(q), _f32(k), _f32(v), _f32(d_out)
+    h, n, hd = q.shape
+    f, hh, ww, ns, ss, wh, wws, tg, aug = _grid_args(grid)
+    out = {name: np.empty((h, n, hd)) for name in ("dq", "dk", "dv")}
+    out["lse"] = np.empty((h, n))
+    rc = _load().oracle_stga_backward(q, k, v, go, h, hd, f, hh, ww, ns, ss, wh, wws, tg, aug,
+                                      {"temporal": 0, "frame": 1}[mode], float(scale),
+                                      out["dq"], out["dk"], out["dv"], out["lse"])
+    if rc != 0:
+        raise ValueError(f"oracle_stga_backward failed ({rc})")
+    return out
+
+
+def stga_bwd_rows(q, k, v, d_out, grid: dict, mode: str, scale: float, rows_h, rows_t):
+    """stga_backward's dq and lse (the token as a query) and dk, dv (as a key) of selected
+    (head, token) rows.  Returns (dq, dk, dv, lse)."""
+    q, k, v, go = _f32(q), _f32(k), _f32(v), _f32(d_out)
+    hd = q.shape[2]
+    rh, rt = _rows(rows_h, rows_t)
+    f, hh, ww, ns, ss, wh, wws, tg, aug = _grid_args(grid)
+    r = rh.shape[0]
+    dq, dk, dv, lse = np.empty((r, hd)), np.empty((r, hd)), np.empty((r, hd)), np.empty(r)
+    rc = _load().oracle_stga_bwd_rows(q, k, v, go, hd, f, hh, ww, ns, ss, wh, wws, tg, aug,
+                                      {"temporal": 0, "frame": 1}[mode], float(scale), r, rh, rt,
+                                      dq, dk, dv, lse)
+    if rc != 0:
+        raise ValueError(f"oracle_stga_bwd_rows failed ({rc})")
+    return dq, dk, dv, lse
+
+
+def hybrid_backward(x, w, q, k, v, group_id, grid: dict, d_out, d_loss: float, alpha: float,
+                    scale: float) -> dict:
+    """Gradients of <d_out, out> + d_loss * L_gb for the hybrid layer out = (O_moga + O_temporal
+    + O_frame) / 3 (papernotes.org MoGA note, 关键设计 4: each token takes the mean of its three
+    outputs), routing held fixed: each branch receives d_out / 3, the MoGA branch's gradients
+    (router included) come from moga_backward, and dq, dk, dv add over the three branches."""
+    # every gradient is linear in d_out, and the loss term does not depend on it: the
+    # d_out / 3 share is formed by dividing gradients in fp64 (d_out itself stays exact)
+    att = moga_backward(x, w, q, k, v, group_id, d_out, 0.0, alpha, scale)
+    los = moga_backward(x, w, q, k, v, group_id, np.zeros_like(_f32(d_out)), d_loss, alpha,
+                        scale)
+    out = {name: att[name] / 3.0 + los[name] for name in ("dq", "dk", "dv", "dx", "dw", "dp")}
+    out["lse"] = att["lse"]
+    for mode in ("temporal", "frame"):
+        st = stga_backward(q, k, v, d_out, grid, mode, scale)
+        for name in ("dq", "dk", "dv"):
+            out[name] = out[name] + st[name] / 3.0
+        out["lse_" + mode] = st["lse"]
+    return out
 
 
 def stga_pairs(grid: dict, mode: str) -> int:

@@ -670,3 +670,134 @@ int oracle_moga_dkdv_rows(const float *q, const float *k, const float *v, const 
     free(members);
     return rc;
 }
+
+/* ========================================================================= */
+/* Backward of one STGA branch ([N] key design 4; the branches enter the      */
+/* layer output through the mean, so their upstream gradient is the mean's).  */
+/* For O_t = softmax_u(scale <q_t, k_u>) v_u over the branch's key set of t  */
+/* and J = sum_t <G_t, O_t> (G = d_out, per head):                            */
+/*   P_tu = softmax over set(t);  D_t = <G_t, O_t>;  dP_tu = <G_t, v_u>;      */
+/*   dS_tu = P_tu (dP_tu - D_t);  dq_t = scale sum_{u in set(t)} dS_tu k_u;   */
+/*   dk_u = scale sum_{t : u in set(t)} dS_tu q_t;  dv_u = sum_t P_tu G_t.    */
+/* A key can sit in several key sets (a boundary frame is borrowed by the     */
+/* neighbouring shot's chunk), so dk, dv add over every query that uses it.   */
+/* mode 0 = temporal groups, 1 = per-frame groups; tensors [n_heads][n][hd];  */
+/* lse [n_heads][n] gets each query's log-normaliser.  Plain loops in fp64.   */
+/* ========================================================================= */
+int oracle_stga_backward(const float *q, const float *k, const float *v, const float *d_out,
+                         int n_heads, int hd, int frames, int height, int width, int n_shots,
+                         const int32_t *shot_start, int win_h, int win_w, int t_group, int aug,
+                         int mode, double scale, double *dq, double *dk, double *dv, double *lse)
+{
+    oracle_grid G = {frames, height, width, n_shots, win_h, win_w, t_group, aug, shot_start};
+    if (!grid_ok(&G) || hd < 1 || n_heads < 1) return -1;
+    const int64_t n = (int64_t)frames * height * width;
+    const int64_t max_keys = (int64_t)height * width * (t_group + 2 * aug) + (int64_t)height * width;
+    const size_t E = (size_t)n_heads * n * hd;
+    memset(dq, 0, sizeof(double) * E);
+    memset(dk, 0, sizeof(double) * E);
+    memset(dv, 0, sizeof(double) * E);
+    /* one head per thread: keys of several queries meet in dk, dv */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < n_heads; ++h) {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)max_keys);
+        double *P = (double *)malloc(sizeof(double) * (size_t)max_keys);
+        double *o = (double *)malloc(sizeof(double) * (size_t)hd);
+        const int64_t hoff = (int64_t)h * n * hd;
+        const float *qh = q + hoff, *kh = k + hoff, *vh = v + hoff, *gh = d_out + hoff;
+        for (int64_t t = 0; t < n; ++t) {
+            const int64_t nk = stga_keys(&G, mode, t, keys);
+            const double l = softmax_row(qh + t * hd, kh, vh, hd, keys, nk, scale, P, o);
+            if (lse) lse[(int64_t)h * n + t] = l;
+            double Dt = 0.0;
+            for (int c = 0; c < hd; ++c) Dt += (double)gh[t * hd + c] * o[c];
+            for (int64_t b = 0; b < nk; ++b) {
+                const int64_t u = keys[b];
+                double dP = 0.0;
+                for (int c = 0; c < hd; ++c) dP += (double)gh[t * hd + c] * (double)vh[u * hd + c];
+                const double dS = P[b] * (dP - Dt);
+                for (int c = 0; c < hd; ++c) {
+                    dq[hoff + t * hd + c] += scale * dS * (double)kh[u * hd + c];
+                    dk[hoff + u * hd + c] += scale * dS * (double)qh[t * hd + c];
+                    dv[hoff + u * hd + c] += P[b] * (double)gh[t * hd + c];
+                }
+            }
+        }
+        free(keys); free(P); free(o);
+    }
+    return 0;
+}
+
+/* The same gradients for selected rows only (full-size tests): row r is head rows_h[r] (an
+ * index into the heads of q/k/v/d_out), token rows_t[r]; dq and lse are that token's as a
+ * query, dk and dv as a key.  The queries whose key set can hold key u lie in u's spatial
+ * window (per-frame: u's frame) within t_group + aug frames of u; each candidate's key set is
+ * built and searched for u, so the sum runs over exactly the queries that use u. */
+int oracle_stga_bwd_rows(const float *q, const float *k, const float *v, const float *d_out,
+                         int hd, int frames, int height, int width, int n_shots,
+                         const int32_t *shot_start, int win_h, int win_w, int t_group, int aug,
+                         int mode, double scale, int64_t n_rows, const int32_t *rows_h,
+                         const int64_t *rows_t, double *dq, double *dk, double *dv, double *lse)
+{
+    oracle_grid G = {frames, height, width, n_shots, win_h, win_w, t_group, aug, shot_start};
+    if (!grid_ok(&G) || hd < 1) return -1;
+    const int64_t n = (int64_t)frames * height * width, hw = (int64_t)height * width;
+    const int64_t max_keys = (int64_t)height * width * (t_group + 2 * aug) + (int64_t)height * width;
+    int rc = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)max_keys);
+        double *P = (double *)malloc(sizeof(double) * (size_t)max_keys);
+        double *o = (double *)malloc(sizeof(double) * (size_t)hd);
+        const int64_t hoff = (int64_t)rows_h[r] * n * hd;
+        const float *qh = q + hoff, *kh = k + hoff, *vh = v + hoff, *gh = d_out + hoff;
+        const int64_t u = rows_t[r];
+        double *dqr = dq + r * hd, *dkr = dk + r * hd, *dvr = dv + r * hd;
+        for (int c = 0; c < hd; ++c) { dqr[c] = 0.0; dkr[c] = 0.0; dvr[c] = 0.0; }
+        /* as a query */
+        {
+            const int64_t nk = stga_keys(&G, mode, u, keys);
+            const double l = softmax_row(qh + u * hd, kh, vh, hd, keys, nk, scale, P, o);
+            if (lse) lse[r] = l;
+            double Dt = 0.0;
+            for (int c = 0; c < hd; ++c) Dt += (double)gh[u * hd + c] * o[c];
+            for (int64_t b = 0; b < nk; ++b) {
+                double dP = 0.0;
+                for (int c = 0; c < hd; ++c) dP += (double)gh[u * hd + c] * (double)vh[keys[b] * hd + c];
+                const double dS = P[b] * (dP - Dt);
+                for (int c = 0; c < hd; ++c) dqr[c] += scale * dS * (double)kh[keys[b] * hd + c];
+            }
+        }
+        /* as a key: every query t whose key set holds u */
+        const int fu = (int)(u / hw);
+        const int yu = (int)((u % hw) / width), xu = (int)(u % width);
+        const int span = mode == 1 ? 0 : t_group + aug;
+        const int f_lo = fu - span < 0 ? 0 : fu - span;
+        const int f_hi = fu + span >= frames ? frames - 1 : fu + span;
+        const int y0 = mode == 1 ? 0 : (yu / win_h) * win_h, y1 = mode == 1 ? height : y0 + win_h;
+        const int x0 = mode == 1 ? 0 : (xu / win_w) * win_w, x1 = mode == 1 ? width : x0 + win_w;
+        for (int f = f_lo; f <= f_hi; ++f)
+            for (int y = y0; y < y1; ++y)
+                for (int x = x0; x < x1; ++x) {
+                    const int64_t t = (int64_t)f * hw + (int64_t)y * width + x;
+                    const int64_t nk = stga_keys(&G, mode, t, keys);
+                    int64_t bu = -1;
+                    for (int64_t b = 0; b < nk; ++b)
+                        if (keys[b] == u) { bu = b; break; }
+                    if (bu < 0) continue;
+                    softmax_row(qh + t * hd, kh, vh, hd, keys, nk, scale, P, o);
+                    double Dt = 0.0, dP = 0.0;
+                    for (int c = 0; c < hd; ++c) {
+                        Dt += (double)gh[t * hd + c] * o[c];
+                        dP += (double)gh[t * hd + c] * (double)vh[u * hd + c];
+                    }
+                    const double dS = P[bu] * (dP - Dt);
+                    for (int c = 0; c < hd; ++c) {
+                        dkr[c] += scale * dS * (double)qh[t * hd + c];
+                        dvr[c] += P[bu] * (double)gh[t * hd + c];
+                    }
+                }
+        free(keys); free(P); free(o);
+    }
+    return rc;
+}

@@ -498,3 +498,91 @@ def test_backward_dkdv_rows_match_full():
     # a one-token group: P = 1, so dv = p * d_out and dk = 0
     np.testing.assert_allclose(dv[4], p_sel[17] * go[1][17], rtol=1e-12)
     np.testing.assert_allclose(dk[4], 0.0, atol=1e-14)
+
+
+# ------------------------------------------------------------------ STGA and hybrid backward
+STGA_BWD_GRID = dict(frames=7, height=4, width=6, shot_start=[0, 3, 4, 7], win_h=2, win_w=3,
+                     t_group=2, aug_frames=2)
+
+
+def _stga_case(grid, h=2, hd=8, seed=41):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = grid["frames"] * grid["height"] * grid["width"]
+    return tuple(rng.standard_normal((h, n, hd)).astype(np.float32) for _ in range(4))
+
+
+@pytest.mark.parametrize("mode", ["temporal", "frame"])
+def test_stga_backward_matches_autograd(mode):
+    """Gradients of one STGA branch equal torch autograd of the dense masked formulation (a
+    one-frame shot whose frames are borrowed by both neighbours, clipped borrowing, a short
+    last chunk)."""
+    q, k, v, go = _stga_case(STGA_BWD_GRID)
+    scale = 0.4
+    mask = torch.from_numpy(bf.stga_mask(STGA_BWD_GRID, mode))
+    leaf = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    Q, K, V = leaf(q), leaf(k), leaf(v)
+    s = (scale * Q @ K.transpose(1, 2)).masked_fill(~mask, float("-inf"))
+    out = torch.softmax(s, dim=-1) @ V
+    J = (torch.from_numpy(go.astype(np.float64)) * out).sum()
+    dQ, dK, dV = torch.autograd.grad(J, [Q, K, V])
+    ref = oracle.stga_backward(q, k, v, go, STGA_BWD_GRID, mode, scale)
+    for name, gr in (("dq", dQ), ("dk", dK), ("dv", dV)):
+        np.testing.assert_allclose(ref[name], gr.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+    lse = torch.logsumexp(s, dim=-1).detach().numpy()
+    np.testing.assert_allclose(ref["lse"], lse, rtol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["temporal", "frame"])
+def test_stga_bwd_rows_match_full(mode):
+    """Sampled rows (a token of the one-frame shot, borrowed twice; shot-boundary tokens; an
+    interior token) equal the full backward's rows."""
+    q, k, v, go = _stga_case(STGA_BWD_GRID, seed=42)
+    ref = oracle.stga_backward(q, k, v, go, STGA_BWD_GRID, mode, 0.3)
+    hw = 24
+    rows_t = np.array([3 * hw + 5, 2 * hw + 0, 4 * hw + 23, 6 * hw + 7, 0, 3 * hw + 17], np.int64)
+    rows_h = np.array([0, 1, 1, 0, 1, 0], np.int32)
+    dq, dk, dv, lse = oracle.stga_bwd_rows(q, k, v, go, STGA_BWD_GRID, mode, 0.3, rows_h, rows_t)
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        np.testing.assert_allclose(got, ref[name][rows_h, rows_t], rtol=1e-11, atol=1e-13,
+                                   err_msg=name)
+    np.testing.assert_allclose(lse, ref["lse"][rows_h, rows_t], rtol=1e-12)
+
+
+def test_stga_backward_sums():
+    """Rows of P sum to one, so over the keys dv sums to sum_t G_t (each query's weights add up
+    to one) and dk sums to zero (each row of dS sums to zero)."""
+    q, k, v, go = _stga_case(STGA_BWD_GRID, seed=43)
+    for mode in ("temporal", "frame"):
+        ref = oracle.stga_backward(q, k, v, go, STGA_BWD_GRID, mode, 0.5)
+        np.testing.assert_allclose(ref["dv"].sum(1), go.astype(np.float64).sum(1), atol=1e-11)
+        np.testing.assert_allclose(ref["dk"].sum(1), 0.0, atol=1e-11)
+
+
+def test_hybrid_backward_matches_autograd():
+    """The hybrid layer (mean of the MoGA output and both STGA branches) and the balance loss:
+    every gradient equals torch autograd of the dense formulation, routing fixed."""
+    grid = STGA_BWD_GRID
+    n = grid["frames"] * grid["height"] * grid["width"]
+    x, w, q, k, v, go = _bwd_case(n=n, d=10, m=3, h=2, hd=8, seed=44)
+    scale, alpha, d_loss = 0.35, 0.1, 0.6
+    g = bf.router(x, w)[2]
+    m = w.shape[1]
+    leaf = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    X, W, Q, K, V = leaf(x), leaf(w), leaf(q), leaf(k), leaf(v)
+    p = torch.softmax(X @ W, dim=1)
+    gi = torch.from_numpy(g.astype(np.int64))
+    p_sel = p[torch.arange(n), gi]
+
+    def att(mask):
+        s = (scale * Q @ K.transpose(1, 2)).masked_fill(~mask, float("-inf"))
+        return torch.softmax(s, dim=-1) @ V
+
+    out = (p_sel[None, :, None] * att(gi[:, None] == gi[None, :])
+           + att(torch.from_numpy(bf.stga_mask(grid, "temporal")))
+           + att(torch.from_numpy(bf.stga_mask(grid, "frame")))) / 3.0
+    F = torch.bincount(gi, minlength=m).double() / n
+    J = (torch.from_numpy(go.astype(np.float64)) * out).sum() + d_loss * alpha * m * (F * p.mean(0)).sum()
+    grads = torch.autograd.grad(J, [X, W, Q, K, V])
+    ref = oracle.hybrid_backward(x, w, q, k, v, g, grid, go, d_loss, alpha, scale)
+    for name, gr in zip(["dx", "dw", "dq", "dk", "dv"], grads):
+        np.testing.assert_allclose(ref[name], gr.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
