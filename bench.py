@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the MoGA forward on one MI355X.
 
-A step is one whole forward (route -> histogram/scan/permute -> varlen group attention
-scaled by p(g|x) -> inverse permute -> balance loss; plus STGA and the 3-way mean for the
-hybrid workloads) over one synthetic batch already resident in HBM.  The default
+A step is one whole forward (route -> histogram/scan/permute -> balance loss -> varlen group
+attention scaled by p(g|x), whose epilogue writes each row back to its token; for the hybrid
+workloads the two STGA branches run before it and its epilogue stores the 3-way mean) over one
+synthetic batch already resident in HBM.  The default
 workload is the 30 s, 282,360-token, M = 5 layer with Dirichlet(0.5)-skewed routing.
 
 Prints one JSON line: tokens/s of the whole forward (value), the group-attention
@@ -59,8 +60,8 @@ def parse():
                    help="only run the group-count sweep (M = 1, 2, 4, 8, 16 at the 10 s shape) "
                         "and print one JSON line per M")
     p.add_argument("--backward", action="store_true",
-                   help="only time moga_backward (after one forward that saves lse) on the "
-                        "workload and print one JSON line")
+                   help="only time moga_backward (moga_hybrid_backward on a STGA workload) "
+                        "after one forward that saves its state, and print one JSON line")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates the HBM byte "
                         "counters against a known size) and exit")
@@ -188,8 +189,8 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
 
     n, h, hd, m = wl.n_tokens, wl.n_heads, wl.head_dim, wl.n_groups
     stream = torch.cuda.current_stream()
-    names = ["route", "histogram", "permute", "group_attn", "unpermute", "loss"] + (
-        ["stga"] if lay else [])
+    # (no inverse-permute stage: the attention epilogue of moga_forward writes token order)
+    names = ["route", "histogram", "permute", "group_attn", "loss"] + (["stga"] if lay else [])
     acc = {s: [] for s in names}
     log(f"stage breakdown over {args.steps} passes")
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=x.device)
@@ -206,7 +207,6 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
         "permute": (lambda: api.moga_permute(r["group_id"], [q, k, v], m, p_sel=r["p_sel"], ws=ws),
                     STAGE_REPS),
         "group_attn": (lambda: api.moga_group_attn(qp, kp, vp, cu, cu, row_scale=pp, ws=ws), 1),
-        "unpermute": (lambda: api.moga_unpermute(perm, [op], m, ws=ws), STAGE_REPS),
         "loss": (lambda: api.moga_balance_loss(r["counts"], r["prob_sum"], n, wl.alpha), STAGE_REPS),
     }
     if lay:
@@ -231,7 +231,6 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
     x_bytes = n * wl.d_model * (2 if wl.x_dtype == "bf16" else 4)
     route_bytes = x_bytes + wl.d_model * m * 4 + n * 8
     permute_bytes = 6 * e_bytes + n * 4 * 2 + n * 8
-    unpermute_bytes = 2 * e_bytes + n * 4
     histogram_bytes = n * 4 + n * 4 + (m + 1) * 4  # group ids read, perm and cu_seqlens written
     attn_tflops = attn_flops / (ms["group_attn"] / 1e3) / 1e12
     stages = {
@@ -241,12 +240,10 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
         "route_gbs": route_bytes / (ms["route"] / 1e3) / 1e9,
         "histogram_gbs": histogram_bytes / (ms["histogram"] / 1e3) / 1e9,
         "permute_gbs": permute_bytes / (ms["permute"] / 1e3) / 1e9,
-        "unpermute_gbs": unpermute_bytes / (ms["unpermute"] / 1e3) / 1e9,
     }
     stages["route_frac_of_hbm"] = stages["route_gbs"] / HBM_PEAK_GBS
     stages["histogram_frac_of_hbm"] = stages["histogram_gbs"] / HBM_PEAK_GBS
     stages["permute_frac_of_hbm"] = stages["permute_gbs"] / HBM_PEAK_GBS
-    stages["unpermute_frac_of_hbm"] = stages["unpermute_gbs"] / HBM_PEAK_GBS
     stages["roofline"] = {
         "bound": "mfma", "kernel": "attn_kernel_direct<8, false, false> (group_attn stage)",
         "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -277,9 +274,11 @@ WAN13B_LAYERS, WAN13B_PARAMS = 30, 1.3e9
 def backward(args):
     """Time moga_backward: D and dp, the row gathers, the dQ and dK/dV attention kernels, the
     inverse gathers and the router backward, with inputs and the forward's saved state
-    resident in HBM.  Attention FLOPs are counted two ways: the five products of the
-    standard attention backward (S recomputed, dP, dV, dQ, dK: 10 hd per query-key pair and
-    head) and what the two kernels execute (both compute S and dP: 14 hd)."""
+    resident in HBM.  On a STGA workload, moga_hybrid_backward: the same plus the per-frame
+    and temporal branches' backward and the per-token sum of the three.  Attention FLOPs are
+    counted two ways: the five products of the standard attention backward (S recomputed,
+    dP, dV, dQ, dK: 10 hd per query-key pair and head) and what the two kernels execute (both
+    compute S and dP: 14 hd)."""
     import numpy as np
     import torch
 
@@ -287,8 +286,6 @@ def backward(args):
     from sparse_attention_long_moga_amd import api, metrics
 
     wl = workloads.BY_NAME[args.workload]
-    if wl.hybrid:
-        raise SystemExit("the backward covers MoGA only; pick a workload without STGA")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     n, h, hd, m = wl.n_tokens, wl.n_heads, wl.head_dim, wl.n_groups
@@ -296,11 +293,20 @@ def backward(args):
     x, w = workloads.make_x(wl, dev), workloads.make_w(wl, dev)
     q, k, v = workloads.make_qkv(wl, dev)
     dout = workloads.make_dout(wl, dev)
-    saved = api.moga_forward(x, w, q, k, v, m, alpha=wl.alpha, fused=True, with_lse=True)
+    lay = None
+    if wl.hybrid:
+        lay = api.make_stga_layout(wl.frames, wl.height, wl.width, wl.shot_start, wl.win_h,
+                                   wl.win_w, wl.t_group, wl.aug_frames)
+    saved = api.moga_forward(x, w, q, k, v, m, alpha=wl.alpha, fused=True, with_lse=True,
+                             stga=lay)
     dims = api.make_dims(n, wl.d_model, h, hd, m, alpha=wl.alpha)
     import ctypes
     from sparse_attention_long_moga_amd import _capi
-    ws = api.workspace(_capi.load().moga_backward_workspace_bytes(ctypes.byref(dims)), dev)
+    if lay:
+        nb = _capi.load().moga_hybrid_backward_workspace_bytes(ctypes.byref(dims), lay.ref())
+    else:
+        nb = _capi.load().moga_backward_workspace_bytes(ctypes.byref(dims))
+    ws = api.workspace(nb, dev)
     grads = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                  dx=torch.empty(n, wl.d_model, dtype=torch.float32, device=dev),
                  dw=torch.empty(wl.d_model, m, dtype=torch.float32, device=dev),
@@ -308,8 +314,12 @@ def backward(args):
     torch.cuda.synchronize()
 
     def step():
-        api.moga_backward(x, w, q, k, v, saved, dout, d_loss=1.0, alpha=wl.alpha, ws=ws,
-                          grads=grads)
+        if lay:
+            api.moga_hybrid_backward(x, w, q, k, v, saved, dout, lay, d_loss=1.0, alpha=wl.alpha,
+                                     ws=ws, grads=grads)
+        else:
+            api.moga_backward(x, w, q, k, v, saved, dout, d_loss=1.0, alpha=wl.alpha, ws=ws,
+                              grads=grads)
 
     for _ in range(args.warmup):
         step()
@@ -325,10 +335,15 @@ def backward(args):
     ms = e0.elapsed_time(e1) / args.steps
     counts = saved["counts"].cpu().numpy().astype(np.int64)
     pairs = metrics.moga_pairs(counts)
+    if lay:  # plus the temporal and per-frame branches' (query, key) pairs
+        pairs += stga_pairs_closed_form(dict(
+            frames=wl.frames, height=wl.height, width=wl.width, shot_start=list(wl.shot_start),
+            win_h=wl.win_h, win_w=wl.win_w, t_group=wl.t_group, aug_frames=wl.aug_frames))
     fwd_flops = metrics.attention_flops(pairs, h, hd)  # 4 hd per pair and head
     algo, executed = 2.5 * fwd_flops, 3.5 * fwd_flops
     line = {
-        "mode": "backward", "workload": wl.name, "n_tokens": n, "n_groups": m,
+        "mode": "hybrid_backward" if lay else "backward", "workload": wl.name, "n_tokens": n,
+        "n_groups": m,
         "group_sizes": counts.tolist(), "steps": args.steps, "warmup": args.warmup,
         "backward_ms": ms, "tokens_per_s": n / (ms / 1e3),
         "attn_bwd_tflop_algorithmic": algo / 1e12, "attn_bwd_tflop_executed": executed / 1e12,

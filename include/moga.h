@@ -109,8 +109,14 @@ typedef struct {
     float *lse;           /* optional [H][N] fp32, token order: natural log of the softmax
                              normaliser of the token's MoGA attention row,
                              log sum_u exp(scale q.k_u) over its group's keys; the state
-                             moga_backward needs besides out.  MoGA only: with a STGA
-                             layout the call returns MOGA_ERR_UNSUPPORTED if lse is set */
+                             moga_backward needs besides out.  With a STGA layout: [3][H][N],
+                             the MoGA, temporal and per-frame normalisers (planes in that
+                             order), allowed only together with o_branches (else the call
+                             returns MOGA_ERR_UNSUPPORTED) */
+    void *o_branches;     /* optional, STGA layout only: bf16 [3][H][N][head_dim], token order:
+                             each branch's row before the mean (the MoGA row scaled by
+                             p(g|x), the temporal row, the per-frame row), each rounded to
+                             bf16 once; with lse, the state moga_hybrid_backward needs */
 } moga_outputs;
 
 const char *moga_last_error(void);
@@ -225,7 +231,7 @@ moga_status moga_forward_fused(const moga_inputs *in, const moga_dims *dims,
  *   attention backward of each group with dO' = p_t G (dQ, dK, dV; softmax recomputed from lse)
  *   a_ti = [i = g_t] dp_t + d_loss alpha M F_i / N,  dr_t = p_t (a_t - <a_t, p_t>)  (p_t: all M
  *   probabilities, recomputed from x W in fp32),  dx = dr W^T,  dW = x^T dr.
- * MoGA only: the STGA branches have no backward here. */
+ * moga_hybrid_backward below covers the mean with the two STGA branches. */
 
 /* What moga_backward reads from the forward; all DEVICE, as written by moga_forward or
  * moga_forward_fused called with stga NULL on the same inputs. */
@@ -257,6 +263,24 @@ size_t moga_backward_workspace_bytes(const moga_dims *dims);
 moga_status moga_backward(const moga_inputs *in, const moga_saved *saved, const void *d_out,
                           double d_loss, const moga_dims *dims, const moga_grads *grads,
                           void *ws, size_t ws_bytes, void *stream);
+
+/* Gradients of the hybrid forward out = (O_m + O_t + O_f) / 3 (design 4 beside design 1:
+ * every token takes the mean of its MoGA row O_m = p O, its temporal-window row O_t and its
+ * per-frame row O_f), with the routing held fixed as above.  Each branch receives G / 3:
+ *   MoGA: as moga_backward with G / 3 (dp_t = sum_h <G, O_m> / (3 p_t)); the loss term as is;
+ *   per-frame: attention backward of each frame with dO = G / 3;
+ *   temporal: attention backward of each temporal group with dO = G / 3; a key row that a
+ *   group borrows from the adjacent shot passes its dK, dV back to the token it was taken
+ *   from, so a token's dK and dV sum over every group whose key set holds it.
+ * The three branches' dQ, dK, dV are added per token in fp32 and rounded to bf16 once.
+ * saved: as moga_forward wrote it with this stga layout, with out = o_branches
+ * ([3][H][N][head_dim]) and lse = the [3][H][N] normalisers; the other fields as for
+ * moga_backward.  Needs head_dim 128.  ws: moga_hybrid_backward_workspace_bytes. */
+size_t moga_hybrid_backward_workspace_bytes(const moga_dims *dims, const stga_layout *stga);
+moga_status moga_hybrid_backward(const moga_inputs *in, const moga_saved *saved,
+                                 const stga_layout *stga, const void *d_out, double d_loss,
+                                 const moga_dims *dims, const moga_grads *grads, void *ws,
+                                 size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

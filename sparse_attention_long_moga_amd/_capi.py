@@ -15,7 +15,8 @@ STATUS_NAMES = {0: "MOGA_OK", 1: "MOGA_ERR_ARG", 2: "MOGA_ERR_UNSUPPORTED",
 EXPORTS = ["moga_last_error", "moga_workspace_bytes", "moga_group_attn_workspace_bytes",
            "moga_route", "moga_permute", "moga_group_attn", "stga_group_attn",
            "moga_balance_loss", "moga_forward", "moga_forward_fused",
-           "moga_backward_workspace_bytes", "moga_backward", "moga_group_attn_noalloc"]
+           "moga_backward_workspace_bytes", "moga_backward", "moga_group_attn_noalloc",
+           "moga_hybrid_backward_workspace_bytes", "moga_hybrid_backward"]
 
 
 class MogaDims(ctypes.Structure):
@@ -44,7 +45,7 @@ class MogaOutputs(ctypes.Structure):
                 ("group_id", ctypes.c_void_p), ("p_sel", ctypes.c_void_p),
                 ("cu_seqlens", ctypes.c_void_p), ("perm", ctypes.c_void_p),
                 ("counts", ctypes.c_void_p), ("prob_sum", ctypes.c_void_p),
-                ("lse", ctypes.c_void_p)]
+                ("lse", ctypes.c_void_p), ("o_branches", ctypes.c_void_p)]
 
 
 class MogaSaved(ctypes.Structure):
@@ -105,6 +106,12 @@ def load(path: str = LIB_PATH):
     lib.moga_backward.argtypes = [ctypes.POINTER(MogaInputs), ctypes.POINTER(MogaSaved), vp,
                                   ctypes.c_double, pdims, ctypes.POINTER(MogaGrads), vp, sz, vp]
     lib.moga_backward.restype = st
+    lib.moga_hybrid_backward_workspace_bytes.argtypes = [pdims, pstga]
+    lib.moga_hybrid_backward_workspace_bytes.restype = sz
+    lib.moga_hybrid_backward.argtypes = [ctypes.POINTER(MogaInputs), ctypes.POINTER(MogaSaved),
+                                         pstga, vp, ctypes.c_double, pdims,
+                                         ctypes.POINTER(MogaGrads), vp, sz, vp]
+    lib.moga_hybrid_backward.restype = st
     _lib = lib
     return lib
 

@@ -262,10 +262,12 @@ def moga_forward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Ten
                  out: Optional[dict] = None, fused: bool = False, with_lse: bool = False) -> dict:
     """Whole forward.  Returns a dict with out, loss and the routing tensors
     (group_id, p_sel, cu_seqlens, perm, counts, prob_sum), plus lse ([H, N] f32, what
-    moga_backward needs) when with_lse is set.  Pass `out` (a dict of preallocated
-    tensors with those keys) and `ws` to run without allocating.  fused=True calls
-    moga_forward_fused (rows read through perm inside the attention kernel; bitwise
-    identical results)."""
+    moga_backward needs) when with_lse is set; with a STGA layout with_lse returns the
+    three branches' state moga_hybrid_backward needs instead: lse [3, H, N] and o_branches
+    [3, H, N, head_dim] (MoGA row scaled by p, temporal row, per-frame row).  Pass `out` (a
+    dict of preallocated tensors with those keys) and `ws` to run without allocating.
+    fused=True calls moga_forward_fused (rows read through perm inside the attention kernel;
+    bitwise identical results)."""
     _need(x, "x", ndim=2)
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("x must be float32 or bfloat16")
@@ -286,7 +288,10 @@ def moga_forward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Ten
                    perm=torch.empty(n, dtype=torch.int32, device=dev),
                    counts=torch.empty(n_groups, dtype=torch.int32, device=dev),
                    prob_sum=torch.empty(n_groups, dtype=torch.float64, device=dev))
-        if with_lse:
+        if with_lse and stga is not None:
+            out["lse"] = torch.empty(3, h, n, dtype=torch.float32, device=dev)
+            out["o_branches"] = torch.empty((3,) + tuple(q.shape), dtype=q.dtype, device=dev)
+        elif with_lse:
             out["lse"] = torch.empty(h, n, dtype=torch.float32, device=dev)
     ws = _ws(ws, moga_workspace_bytes(dims, stga), dev)
     ins = MogaInputs(x.data_ptr(), _capi.MOGA_BF16 if x.dtype == torch.bfloat16 else _capi.MOGA_F32,
@@ -294,7 +299,7 @@ def moga_forward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Ten
                      pin.data_ptr() if pin is not None else None)
     g = lambda key: out[key].data_ptr() if out.get(key) is not None else None
     outs = MogaOutputs(g("out"), g("loss"), g("group_id"), g("p_sel"), g("cu_seqlens"), g("perm"),
-                       g("counts"), g("prob_sum"), g("lse"))
+                       g("counts"), g("prob_sum"), g("lse"), g("o_branches"))
     fn = _lib().moga_forward_fused if fused else _lib().moga_forward
     check(fn(ctypes.byref(ins), ctypes.byref(dims), stga.ref() if stga else None,
              ctypes.byref(outs), _ptr(ws), ws.numel(), _stream()))
@@ -306,28 +311,26 @@ def moga_forward_fused(*args, **kwargs) -> dict:
     return moga_forward(*args, fused=True, **kwargs)
 
 
-def moga_backward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
-                  v: torch.Tensor, saved: dict, d_out: torch.Tensor, d_loss: float = 0.0,
-                  alpha: float = 0.1, softmax_scale: float = 0.0,
-                  ws: Optional[torch.Tensor] = None, grads: Optional[dict] = None) -> dict:
-    """Gradients of moga_forward (stga None, routing held fixed).  saved: the dict
-    moga_forward returned with with_lse=True; d_out: bf16 [H, N, head_dim], the gradient
-    with respect to out; d_loss: the gradient with respect to the balance loss.  Returns
-    dq, dk, dv (bf16, like q), dx ([N, d] f32), dw ([d, M] f32) and dp ([N] f32)."""
+def _backward(x, w, q, k, v, saved, d_out, d_loss, alpha, softmax_scale, ws, grads, stga):
     _need(x, "x", ndim=2)
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("x must be float32 or bfloat16")
     n, d = x.shape
     _need(w, "w", torch.float32, 2, x.device)
     m = w.shape[1]
-    h, nn, hd = _heads_shape([q, k, v, d_out, saved["out"]])
+    h, nn, hd = _heads_shape([q, k, v, d_out])
     if nn != n or w.shape[0] != d:
         raise ValueError("shape mismatch between x, w and q/k/v")
+    hybrid = stga is not None
+    out_key = "o_branches" if hybrid else "out"
+    lse_shape = (3, h, n) if hybrid else (h, n)
     for key, dt, shape in (("group_id", torch.int32, (n,)), ("p_sel", torch.float32, (n,)),
                            ("counts", torch.int32, (m,)), ("cu_seqlens", torch.int32, (m + 1,)),
-                           ("perm", torch.int32, (n,)), ("lse", torch.float32, (h, n))):
+                           ("perm", torch.int32, (n,)), ("lse", torch.float32, lse_shape),
+                           (out_key, q.dtype, ((3,) if hybrid else ()) + tuple(q.shape))):
         if saved.get(key) is None:
-            raise ValueError(f"saved['{key}'] is missing (run moga_forward with with_lse=True)")
+            raise ValueError(f"saved['{key}'] is missing (run moga_forward with with_lse=True"
+                             + (" and this stga layout)" if hybrid else ")"))
         _need(saved[key], f"saved['{key}']", dt, len(shape), x.device)
         if tuple(saved[key].shape) != shape:
             raise ValueError(f"saved['{key}'] must be {shape}")
@@ -338,7 +341,10 @@ def moga_backward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Te
                      dx=torch.empty(n, d, dtype=torch.float32, device=dev),
                      dw=torch.empty(d, m, dtype=torch.float32, device=dev),
                      dp=torch.empty(n, dtype=torch.float32, device=dev))
-    nb = _lib().moga_backward_workspace_bytes(ctypes.byref(dims))
+    if hybrid:
+        nb = _lib().moga_hybrid_backward_workspace_bytes(ctypes.byref(dims), stga.ref())
+    else:
+        nb = _lib().moga_backward_workspace_bytes(ctypes.byref(dims))
     if nb == 0:
         check(_capi.MOGA_ERR_ARG)
     ws = _ws(ws, nb, dev)
@@ -346,10 +352,39 @@ def moga_backward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Te
                      w.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), None)
     sv = lambda key: saved[key].data_ptr()
     sav = MogaSaved(sv("group_id"), sv("p_sel"), sv("counts"), sv("cu_seqlens"), sv("perm"),
-                    sv("out"), sv("lse"))
+                    sv(out_key), sv("lse"))
     g = lambda key: grads[key].data_ptr() if grads.get(key) is not None else None
     gr = MogaGrads(g("dq"), g("dk"), g("dv"), g("dx"), g("dw"), g("dp"))
-    check(_lib().moga_backward(ctypes.byref(ins), ctypes.byref(sav), _ptr(d_out), float(d_loss),
-                               ctypes.byref(dims), ctypes.byref(gr), _ptr(ws), ws.numel(),
-                               _stream()))
+    if hybrid:
+        check(_lib().moga_hybrid_backward(ctypes.byref(ins), ctypes.byref(sav), stga.ref(),
+                                          _ptr(d_out), float(d_loss), ctypes.byref(dims),
+                                          ctypes.byref(gr), _ptr(ws), ws.numel(), _stream()))
+    else:
+        check(_lib().moga_backward(ctypes.byref(ins), ctypes.byref(sav), _ptr(d_out),
+                                   float(d_loss), ctypes.byref(dims), ctypes.byref(gr), _ptr(ws),
+                                   ws.numel(), _stream()))
     return grads
+
+
+def moga_backward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                  v: torch.Tensor, saved: dict, d_out: torch.Tensor, d_loss: float = 0.0,
+                  alpha: float = 0.1, softmax_scale: float = 0.0,
+                  ws: Optional[torch.Tensor] = None, grads: Optional[dict] = None) -> dict:
+    """Gradients of moga_forward (stga None, routing held fixed).  saved: the dict
+    moga_forward returned with with_lse=True; d_out: bf16 [H, N, head_dim], the gradient
+    with respect to out; d_loss: the gradient with respect to the balance loss.  Returns
+    dq, dk, dv (bf16, like q), dx ([N, d] f32), dw ([d, M] f32) and dp ([N] f32)."""
+    return _backward(x, w, q, k, v, saved, d_out, d_loss, alpha, softmax_scale, ws, grads, None)
+
+
+def moga_hybrid_backward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                         v: torch.Tensor, saved: dict, d_out: torch.Tensor, stga: _Layout,
+                         d_loss: float = 0.0, alpha: float = 0.1, softmax_scale: float = 0.0,
+                         ws: Optional[torch.Tensor] = None, grads: Optional[dict] = None) -> dict:
+    """Gradients of the hybrid forward (moga_forward with this stga layout, routing held
+    fixed): out is the mean of the MoGA, temporal and per-frame rows.  saved: the dict
+    moga_forward returned with with_lse=True and stga (o_branches and the [3, H, N] lse);
+    otherwise as moga_backward."""
+    if stga is None:
+        raise ValueError("moga_hybrid_backward needs the forward's stga layout")
+    return _backward(x, w, q, k, v, saved, d_out, d_loss, alpha, softmax_scale, ws, grads, stga)

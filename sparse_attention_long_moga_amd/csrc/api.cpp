@@ -193,34 +193,57 @@ Layout make_layout(const moga_dims *d, const StgaGeom *g) {
 }
 
 // backward: token-order D and dp, group-order copies of everything the attention backward
-// reads and writes, the router's dr and dW partials, and the attention plan
+// reads and writes, the router's dr and dW partials, and the attention plan.  With a STGA
+// layout (hybrid backward) the copies of K and V also hold the borrowed key rows of the
+// temporal groups, and the temporal branch's dQ, dK, dV (position order), its index maps and
+// each token's positions in them come on top; the per-frame branch reuses the MoGA copies.
 struct BwdLayout {
-    size_t D, dp, Dp, lse2p, qp, kp, vp, dov, dqp, dkp, dvp, dr, dw_part, plan;
+    size_t D, dp, Dp, lse2p, qp, kp, vp, dov, dqp, dkp, dvp, dr, dw_part;
+    size_t shot_info, cu_tq, cu_tk, cu_f, q_idx, kv_idx, tpos, dqt, dkt, dvt, plan;
+    int32_t plan_seg;
     int64_t plan_items;
     size_t total;
 };
 
-BwdLayout make_bwd_layout(const moga_dims *d) {
+BwdLayout make_bwd_layout(const moga_dims *d, const StgaGeom *g = nullptr) {
     BwdLayout B{};
     Carver c;
     const int64_t n = d->n_tokens;
+    const int64_t nk = g ? n + stga_extra_rows(*g) : n;  // key rows of the widest launch
     const size_t rows = sizeof(float) * d->n_heads * n;
-    const size_t tensor = (size_t)d->n_heads * n * d->head_dim * sizeof(uint16_t);
+    const size_t row_bytes = (size_t)d->n_heads * d->head_dim * sizeof(uint16_t);
+    const size_t tensor = row_bytes * n, ktensor = row_bytes * nk;
     B.D = c.take(rows);
     B.dp = c.take(sizeof(float) * n);
     B.Dp = c.take(rows);
     B.lse2p = c.take(rows);
     B.qp = c.take(tensor);
-    B.kp = c.take(tensor);
-    B.vp = c.take(tensor);
+    B.kp = c.take(ktensor);
+    B.vp = c.take(ktensor);
     B.dov = c.take(tensor);
     B.dqp = c.take(tensor);
     B.dkp = c.take(tensor);
     B.dvp = c.take(tensor);
     B.dr = c.take(sizeof(float) * n * d->n_groups);
     B.dw_part = c.take(sizeof(float) * bwd_dw_chunks(n) * d->d_model * d->n_groups);
-    B.plan_items = attn_max_items(d->n_heads, n, d->n_groups);
-    B.plan = c.take(attn_plan_bytes(d->n_groups, B.plan_items, 0));
+    B.plan_seg = d->n_groups;
+    if (g) {
+        const int32_t ng = stga_n_groups(*g);
+        B.shot_info = c.take(sizeof(int32_t) * 6 * g->n_shots);
+        B.cu_tq = c.take(sizeof(int32_t) * (ng + 1));
+        B.cu_tk = c.take(sizeof(int32_t) * (ng + 1));
+        B.cu_f = c.take(sizeof(int32_t) * (g->frames + 1));
+        B.q_idx = c.take(sizeof(int32_t) * n);
+        B.kv_idx = c.take(sizeof(int32_t) * nk);
+        B.tpos = c.take(sizeof(int32_t) * 4 * n);
+        B.dqt = c.take(tensor);
+        B.dkt = c.take(ktensor);
+        B.dvt = c.take(ktensor);
+        B.plan_seg = std::max(B.plan_seg, std::max(ng, g->frames));
+    }
+    // the dK/dV kernel's items run over key tiles, of which the temporal groups have more
+    B.plan_items = attn_max_items(d->n_heads, nk, B.plan_seg);
+    B.plan = c.take(attn_plan_bytes(B.plan_seg, B.plan_items, 0));
     B.total = c.off;
     return B;
 }
@@ -283,11 +306,12 @@ moga_status run_gather(int inverse, const int32_t *perm, const moga_dims *d,
 }
 
 // Optional parts of an attention launch's epilogue: output rows through a map, the log-sum-exp,
-// and the mean with two other branches' rows.
+// and the mean with two other branches' rows (and the row before the mean).
 struct AttnEpilogue {
     const int32_t *o_idx = nullptr;
     float *lse = nullptr;
     const void *mean_a = nullptr, *mean_b = nullptr;
+    void *o_raw = nullptr;
 };
 
 moga_status run_attn(const void *q, const void *k, const void *v, void *o, const int32_t *cu_q,
@@ -309,6 +333,7 @@ moga_status run_attn(const void *q, const void *k, const void *v, void *o, const
     a.o_idx = ep.o_idx;
     a.mean_a = static_cast<const bf16 *>(ep.mean_a);
     a.mean_b = static_cast<const bf16 *>(ep.mean_b);
+    a.o_raw = static_cast<bf16 *>(ep.o_raw);
     if (a.max_items > plan_items || n_seg > plan_seg)
         return fail(MOGA_ERR_WORKSPACE, "attention plan larger than its workspace region");
     attn_plan_carve(a.plan, plan_mem, n_seg, a.max_items, split_rows(d, len_q));
@@ -316,9 +341,10 @@ moga_status run_attn(const void *q, const void *k, const void *v, void *o, const
     return MOGA_OK;
 }
 
+// The two STGA branches (token order); lse_t, lse_f: NULL or [H][N] normalisers of each.
 moga_status run_stga(const void *q, const void *k, const void *v, const moga_dims *d,
                      const StgaGeom &g, void *o_t, void *o_f, void *ws, const Layout &L,
-                     hipStream_t s) {
+                     hipStream_t s, float *lse_t = nullptr, float *lse_f = nullptr) {
     StgaBuffers b{};
     b.shot_info = at<int32_t>(ws, L.shot_info); b.cu_tq = at<int32_t>(ws, L.cu_tq);
     b.cu_tk = at<int32_t>(ws, L.cu_tk); b.cu_f = at<int32_t>(ws, L.cu_f);
@@ -328,14 +354,18 @@ moga_status run_stga(const void *q, const void *k, const void *v, const moga_dim
     void *plan = at<char>(ws, L.plan);
     if (o_t) {
         const int32_t ng = stga_n_groups(g);
+        AttnEpilogue ep;
+        ep.lse = lse_t;
         moga_status st = run_attn(q, k, v, o_t, b.cu_tq, b.cu_tk, ng, b.q_idx, b.kv_idx, nullptr, n,
                                   n + stga_extra_rows(g), n, n, n, d, plan, L.plan_seg,
-                                  L.plan_items, 4, s);
+                                  L.plan_items, 4, s, ep);
         if (st != MOGA_OK) return st;
     }
     if (o_f) {
+        AttnEpilogue ep;
+        ep.lse = lse_f;
         moga_status st = run_attn(q, k, v, o_f, b.cu_f, b.cu_f, g.frames, nullptr, nullptr, nullptr,
-                                  n, n, n, n, n, d, plan, L.plan_seg, L.plan_items, 4, s);
+                                  n, n, n, n, n, d, plan, L.plan_seg, L.plan_items, 4, s, ep);
         if (st != MOGA_OK) return st;
     }
     return MOGA_OK;
@@ -369,6 +399,99 @@ moga_status run_group_attn(const void *q, const void *k, const void *v, int64_t 
     const int waves = len_q / n_seg >= 1024 ? 8 : 4;
     return run_attn(q, k, v, o, cu_q, cu_k, n_seg, nullptr, nullptr, row_scale, len_q, len_k, len_q,
                     len_k, len_q, dims, plan_mem, n_seg, items, waves, s);
+}
+
+moga_status check_bwd_args(const moga_inputs *in, const moga_saved *saved, const void *d_out,
+                           double d_loss, const moga_dims *dims, const moga_grads *grads) {
+    moga_status st = check_dims(dims);
+    if (st != MOGA_OK) return st;
+    if (dims->head_dim != 128)
+        return fail(MOGA_ERR_UNSUPPORTED, "backward needs head_dim 128, got %d", dims->head_dim);
+    if (!in || !saved || !grads) return fail(MOGA_ERR_ARG, "inputs, saved or grads is NULL");
+    if ((st = check_route_args(in->x, in->x_dtype, in->w, dims)) != MOGA_OK) return st;
+    if (!in->q || !in->k || !in->v || !d_out) return fail(MOGA_ERR_ARG, "q, k, v or d_out is NULL");
+    if (!saved->group_id || !saved->p_sel || !saved->counts || !saved->cu_seqlens ||
+        !saved->perm || !saved->out || !saved->lse)
+        return fail(MOGA_ERR_ARG, "a saved forward tensor is NULL");
+    if (!grads->dq || !grads->dk || !grads->dv) return fail(MOGA_ERR_ARG, "dq, dk or dv is NULL");
+    const void *vec[8] = {in->q, in->k, in->v, d_out, saved->out, grads->dq, grads->dk, grads->dv};
+    for (const void *p : vec)
+        if (!aligned16(p)) return fail(MOGA_ERR_ARG, "q, k, v, d_out, out, dq, dk, dv must be 16-byte aligned");
+    if ((grads->dx && !aligned16(grads->dx)) || (grads->dw && !aligned16(grads->dw)))
+        return fail(MOGA_ERR_ARG, "dx and dw must be 16-byte aligned");
+    if (!std::isfinite(d_loss)) return fail(MOGA_ERR_ARG, "d_loss is not finite");
+    return MOGA_OK;
+}
+
+// The MoGA backward on a validated call: out_m and lse_m are the MoGA branch's rows (p-scaled)
+// and normalisers, dp_scale the factor of the branch in the objective's output (1, or 1/3 under
+// the hybrid mean), applied to dp only: dQ, dK, dV come out for the unscaled G.
+moga_status run_moga_bwd(const moga_inputs *in, const moga_saved *saved, const void *out_m,
+                         const float *lse_m, const void *d_out, double d_loss, float dp_scale,
+                         const moga_dims *dims, const moga_grads *grads, void *ws,
+                         const BwdLayout &B, hipStream_t s) {
+    moga_status st;
+    const int64_t n = dims->n_tokens;
+    const int nh = dims->n_heads, m = dims->n_groups;
+    const int32_t *perm = saved->perm;
+
+    // D = <G, out> per (head, token) row; dp = dp_scale * sum over heads of D / p
+    float *D = at<float>(ws, B.D);
+    float *dp = grads->dp ? grads->dp : at<float>(ws, B.dp);
+    HIP_TRY(launch_bwd_rowdot(static_cast<const bf16 *>(d_out), static_cast<const bf16 *>(out_m),
+                              (int64_t)nh * n, D, s),
+            "row dot launch");
+    HIP_TRY(launch_bwd_dp(D, saved->p_sel, n, nh, dp_scale, dp, s), "dp launch");
+    // group order: Q, K, V; dO' = p * G; D; lse in base 2
+    void *qp = at<char>(ws, B.qp), *kp = at<char>(ws, B.kp), *vp = at<char>(ws, B.vp);
+    void *dov = at<char>(ws, B.dov);
+    const void *src[3] = {in->q, in->k, in->v};
+    void *dst[3] = {qp, kp, vp};
+    if ((st = run_gather(0, perm, dims, src, dst, 3, nullptr, nullptr, s)) != MOGA_OK) return st;
+    {
+        GatherLaunch g{};
+        g.src[0] = d_out; g.dst[0] = dov; g.n_tensors = 1; g.perm = perm; g.n = n;
+        g.n_heads = nh; g.head_dim = dims->head_dim; g.inverse = 0; g.src_scale = saved->p_sel;
+        HIP_TRY(launch_gather(g, s), "scaled gather launch");
+    }
+    float *Dp = at<float>(ws, B.Dp), *lse2p = at<float>(ws, B.lse2p);
+    HIP_TRY(launch_bwd_gather_f32(D, perm, n, nh, 1.0f, 0, Dp, s), "D gather launch");
+    HIP_TRY(launch_bwd_gather_f32(lse_m, perm, n, nh, 1.4426950408889634f, 0, lse2p, s),
+            "lse gather launch");
+    // attention backward per group
+    void *dqp = at<char>(ws, B.dqp), *dkp = at<char>(ws, B.dkp), *dvp = at<char>(ws, B.dvp);
+    {
+        AttnBwdLaunch a{};
+        a.q = static_cast<const bf16 *>(qp); a.k = static_cast<const bf16 *>(kp);
+        a.v = static_cast<const bf16 *>(vp); a.dov = static_cast<const bf16 *>(dov);
+        a.lse2 = lse2p; a.D = Dp;
+        a.dq = static_cast<bf16 *>(dqp); a.dk = static_cast<bf16 *>(dkp);
+        a.dv = static_cast<bf16 *>(dvp);
+        a.cu_q = a.cu_k = saved->cu_seqlens; a.n_seg = m; a.len_q = a.len_k = n; a.n_heads = nh;
+        a.scale = scale_of(dims);
+        a.max_items = B.plan_items;
+        attn_plan_carve(a.plan, at<char>(ws, B.plan), B.plan_seg, B.plan_items, 0);
+        HIP_TRY(launch_attention_bwd(a, s), "attention backward launch");
+    }
+    // back to token order
+    {
+        const void *gsrc[3] = {dqp, dkp, dvp};
+        void *gdst[3] = {grads->dq, grads->dk, grads->dv};
+        if ((st = run_gather(1, perm, dims, gsrc, gdst, 3, nullptr, nullptr, s)) != MOGA_OK)
+            return st;
+    }
+    // router: softmax backward, dx, dW
+    if (grads->dx || grads->dw) {
+        BwdRouterLaunch r{};
+        r.x = in->x; r.x_is_bf16 = in->x_dtype == MOGA_BF16; r.w = in->w; r.n = n;
+        r.d = dims->d_model; r.m = m; r.group_id = saved->group_id; r.counts = saved->counts;
+        r.dp = dp;
+        r.loss_coef = (float)(d_loss * dims->alpha * m / ((double)n * (double)n));
+        r.dr = at<float>(ws, B.dr); r.dx = grads->dx; r.dw = grads->dw;
+        r.dw_part = at<float>(ws, B.dw_part);
+        HIP_TRY(launch_router_bwd(r, s), "router backward launch");
+    }
+    return MOGA_OK;
 }
 
 // ---------------------------------------------------------------- library-owned scratch
@@ -543,10 +666,13 @@ static moga_status forward_impl(const moga_inputs *in, const moga_dims *dims, co
         return fail(MOGA_ERR_ARG, "q, k, v and out must be 16-byte aligned");
     StgaGeom g;
     if (stga && (st = check_stga(dims, stga, &g)) != MOGA_OK) return st;
-    if (stga && out->lse)
+    if (out->o_branches && !stga) return fail(MOGA_ERR_ARG, "o_branches needs a STGA layout");
+    if (out->o_branches && !aligned16(out->o_branches))
+        return fail(MOGA_ERR_ARG, "o_branches is not 16-byte aligned");
+    if (stga && out->lse && !out->o_branches)
         return fail(MOGA_ERR_UNSUPPORTED,
-                    "lse is the MoGA branch's softmax normaliser, which moga_backward pairs with a "
-                    "MoGA-only out; it is not returned beside a hybrid (STGA) out");
+                    "with a STGA layout lse holds the three branches' normalisers, which are "
+                    "returned only together with o_branches (the rows the backward pairs them with)");
     const Layout L = make_layout(dims, stga ? &g : nullptr);
     if ((st = check_ws(ws, ws_bytes, L.total)) != MOGA_OK) return st;
     if ((st = check_device()) != MOGA_OK) return st;
@@ -573,13 +699,21 @@ static moga_status forward_impl(const moga_inputs *in, const moga_dims *dims, co
     // 4 with a STGA layout: the two static branches first, in token order; the MoGA epilogue
     // then stores the mean of the three rows (in fp32, one rounding)
     AttnEpilogue ep;
+    ep.lse = out->lse;
     if (stga) {
-        void *ot = at<char>(ws, L.ot), *of = at<char>(ws, L.of);
-        if ((st = run_stga(in->q, in->k, in->v, dims, g, ot, of, ws, L, s)) != MOGA_OK) return st;
+        // o_branches given: the branch rows are stored there (MoGA row, temporal, per-frame),
+        // and lse holds the three normalisers in the same plane order
+        const size_t plane = (size_t)dims->n_heads * n * dims->head_dim * sizeof(uint16_t);
+        char *ob = static_cast<char *>(out->o_branches);
+        void *ot = ob ? ob + plane : at<char>(ws, L.ot), *of = ob ? ob + 2 * plane : at<char>(ws, L.of);
+        float *lse_t = out->lse ? out->lse + (size_t)dims->n_heads * n : nullptr;
+        float *lse_f = out->lse ? out->lse + 2 * (size_t)dims->n_heads * n : nullptr;
+        if ((st = run_stga(in->q, in->k, in->v, dims, g, ot, of, ws, L, s, lse_t, lse_f)) != MOGA_OK)
+            return st;
         ep.mean_a = ot;
         ep.mean_b = of;
+        ep.o_raw = ob;
     }
-    ep.lse = out->lse;
     if (fused) {
         // 5 rows are read through perm and written back in token order
         if ((st = run_attn(in->q, in->k, in->v, out->out, cu, cu, dims->n_groups, perm, perm, psel,
@@ -618,89 +752,105 @@ size_t moga_backward_workspace_bytes(const moga_dims *dims) {
     return make_bwd_layout(dims).total;
 }
 
+size_t moga_hybrid_backward_workspace_bytes(const moga_dims *dims, const stga_layout *stga) {
+    if (check_dims(dims) != MOGA_OK || dims->head_dim != 128) return 0;
+    StgaGeom g;
+    if (check_stga(dims, stga, &g) != MOGA_OK) return 0;
+    return make_bwd_layout(dims, &g).total;
+}
+
 moga_status moga_backward(const moga_inputs *in, const moga_saved *saved, const void *d_out,
                           double d_loss, const moga_dims *dims, const moga_grads *grads,
                           void *ws, size_t ws_bytes, void *stream) {
-    moga_status st = check_dims(dims);
+    moga_status st = check_bwd_args(in, saved, d_out, d_loss, dims, grads);
     if (st != MOGA_OK) return st;
-    if (dims->head_dim != 128)
-        return fail(MOGA_ERR_UNSUPPORTED, "backward needs head_dim 128, got %d", dims->head_dim);
-    if (!in || !saved || !grads) return fail(MOGA_ERR_ARG, "inputs, saved or grads is NULL");
-    if ((st = check_route_args(in->x, in->x_dtype, in->w, dims)) != MOGA_OK) return st;
-    if (!in->q || !in->k || !in->v || !d_out) return fail(MOGA_ERR_ARG, "q, k, v or d_out is NULL");
-    if (!saved->group_id || !saved->p_sel || !saved->counts || !saved->cu_seqlens ||
-        !saved->perm || !saved->out || !saved->lse)
-        return fail(MOGA_ERR_ARG, "a saved forward tensor is NULL");
-    if (!grads->dq || !grads->dk || !grads->dv) return fail(MOGA_ERR_ARG, "dq, dk or dv is NULL");
-    const void *vec[8] = {in->q, in->k, in->v, d_out, saved->out, grads->dq, grads->dk, grads->dv};
-    for (const void *p : vec)
-        if (!aligned16(p)) return fail(MOGA_ERR_ARG, "q, k, v, d_out, out, dq, dk, dv must be 16-byte aligned");
-    if ((grads->dx && !aligned16(grads->dx)) || (grads->dw && !aligned16(grads->dw)))
-        return fail(MOGA_ERR_ARG, "dx and dw must be 16-byte aligned");
-    if (!std::isfinite(d_loss)) return fail(MOGA_ERR_ARG, "d_loss is not finite");
     const BwdLayout B = make_bwd_layout(dims);
     if ((st = check_ws(ws, ws_bytes, B.total)) != MOGA_OK) return st;
     if ((st = check_device()) != MOGA_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t n = dims->n_tokens;
-    const int nh = dims->n_heads, m = dims->n_groups;
-    const int32_t *perm = saved->perm;
+    return run_moga_bwd(in, saved, saved->out, saved->lse, d_out, d_loss, 1.0f, dims, grads, ws, B,
+                        static_cast<hipStream_t>(stream));
+}
 
-    // D = <G, out> per (head, token) row; dp = sum over heads of D / p
-    float *D = at<float>(ws, B.D);
-    float *dp = grads->dp ? grads->dp : at<float>(ws, B.dp);
-    HIP_TRY(launch_bwd_rowdot(static_cast<const bf16 *>(d_out), static_cast<const bf16 *>(saved->out),
-                              (int64_t)nh * n, D, s),
-            "row dot launch");
-    HIP_TRY(launch_bwd_dp(D, saved->p_sel, n, nh, dp, s), "dp launch");
-    // group order: Q, K, V; dO' = p * G; D; lse in base 2
-    void *qp = at<char>(ws, B.qp), *kp = at<char>(ws, B.kp), *vp = at<char>(ws, B.vp);
-    void *dov = at<char>(ws, B.dov);
-    const void *src[3] = {in->q, in->k, in->v};
-    void *dst[3] = {qp, kp, vp};
-    if ((st = run_gather(0, perm, dims, src, dst, 3, nullptr, nullptr, s)) != MOGA_OK) return st;
+moga_status moga_hybrid_backward(const moga_inputs *in, const moga_saved *saved,
+                                 const stga_layout *stga, const void *d_out, double d_loss,
+                                 const moga_dims *dims, const moga_grads *grads, void *ws,
+                                 size_t ws_bytes, void *stream) {
+    moga_status st = check_bwd_args(in, saved, d_out, d_loss, dims, grads);
+    if (st != MOGA_OK) return st;
+    StgaGeom g;
+    if ((st = check_stga(dims, stga, &g)) != MOGA_OK) return st;
+    const BwdLayout B = make_bwd_layout(dims, &g);
+    if ((st = check_ws(ws, ws_bytes, B.total)) != MOGA_OK) return st;
+    if ((st = check_device()) != MOGA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = dims->n_tokens, nk = n + stga_extra_rows(g);
+    const int nh = dims->n_heads;
+    const size_t plane = (size_t)nh * n * dims->head_dim;  // elements of one branch's rows
+    const bf16 *o_br = static_cast<const bf16 *>(saved->out);
+    const float *lse_br = saved->lse;
+    const float third = 1.0f / 3.0f;
+    const float log2e = 1.4426950408889634f;
+
+    // 1 the MoGA branch with G (dQ, dK, dV unscaled, to token order in grads); the router sees
+    //   dp with the 1/3 of the mean and the loss term as is
+    if ((st = run_moga_bwd(in, saved, o_br, lse_br, d_out, d_loss, third, dims, grads, ws, B, s)) !=
+        MOGA_OK)
+        return st;
+    // 2 the STGA index maps and each token's positions in them
+    StgaBuffers sb{};
+    sb.shot_info = at<int32_t>(ws, B.shot_info); sb.cu_tq = at<int32_t>(ws, B.cu_tq);
+    sb.cu_tk = at<int32_t>(ws, B.cu_tk); sb.cu_f = at<int32_t>(ws, B.cu_f);
+    sb.q_idx = at<int32_t>(ws, B.q_idx); sb.kv_idx = at<int32_t>(ws, B.kv_idx);
+    sb.tpos = at<int32_t>(ws, B.tpos);
+    HIP_TRY(launch_stga_index(g, sb, s), "stga index launch");
+    const bf16 *G = static_cast<const bf16 *>(d_out);
+    float *D = at<float>(ws, B.D), *Dp = at<float>(ws, B.Dp), *lse2p = at<float>(ws, B.lse2p);
+    AttnBwdLaunch a{};
+    a.n_heads = nh;
+    a.scale = scale_of(dims);
+    a.max_items = B.plan_items;
+    attn_plan_carve(a.plan, at<char>(ws, B.plan), B.plan_seg, B.plan_items, 0);
+    // 3 per-frame branch, in token order in place (segments cu_f), with G; results in the MoGA
+    //   copies' dQ, dK, dV regions
+    bf16 *dqf = at<bf16>(ws, B.dqp), *dkf = at<bf16>(ws, B.dkp), *dvf = at<bf16>(ws, B.dvp);
+    HIP_TRY(launch_bwd_rowdot(G, o_br + 2 * plane, (int64_t)nh * n, D, s), "row dot launch");
+    HIP_TRY(launch_bwd_gather_f32(lse_br + 2 * (size_t)nh * n, nullptr, n, nh, log2e, 0, lse2p, s),
+            "lse scale launch");
+    a.q = static_cast<const bf16 *>(in->q); a.k = static_cast<const bf16 *>(in->k);
+    a.v = static_cast<const bf16 *>(in->v); a.dov = G; a.lse2 = lse2p; a.D = D;
+    a.dq = dqf; a.dk = dkf; a.dv = dvf;
+    a.cu_q = a.cu_k = sb.cu_f; a.n_seg = g.frames; a.len_q = a.len_k = n;
+    HIP_TRY(launch_attention_bwd(a, s), "per-frame attention backward launch");
+    // 4 temporal branch: Q, dO, D, lse to query positions, K and V to key positions (own rows
+    //   and borrowed frames), the backward over the groups, results in position order
+    bf16 *qt = at<bf16>(ws, B.qp), *kt = at<bf16>(ws, B.kp), *vt = at<bf16>(ws, B.vp);
+    bf16 *dot = at<bf16>(ws, B.dov);
     {
-        GatherLaunch g{};
-        g.src[0] = d_out; g.dst[0] = dov; g.n_tensors = 1; g.perm = perm; g.n = n;
-        g.n_heads = nh; g.head_dim = dims->head_dim; g.inverse = 0; g.src_scale = saved->p_sel;
-        HIP_TRY(launch_gather(g, s), "scaled gather launch");
+        GatherLaunch gq{};
+        gq.src[0] = in->q; gq.dst[0] = qt; gq.src[1] = d_out; gq.dst[1] = dot; gq.n_tensors = 2;
+        gq.perm = sb.q_idx; gq.n = n; gq.n_heads = nh; gq.head_dim = dims->head_dim;
+        HIP_TRY(launch_gather(gq, s), "temporal query gather launch");
+        GatherLaunch gk{};
+        gk.src[0] = in->k; gk.dst[0] = kt; gk.src[1] = in->v; gk.dst[1] = vt; gk.n_tensors = 2;
+        gk.perm = sb.kv_idx; gk.n = nk; gk.src_rows = n; gk.n_heads = nh;
+        gk.head_dim = dims->head_dim;
+        HIP_TRY(launch_gather(gk, s), "temporal key gather launch");
     }
-    float *Dp = at<float>(ws, B.Dp), *lse2p = at<float>(ws, B.lse2p);
-    HIP_TRY(launch_bwd_gather_f32(D, perm, n, nh, 1.0f, 0, Dp, s), "D gather launch");
-    HIP_TRY(launch_bwd_gather_f32(saved->lse, perm, n, nh, 1.4426950408889634f, 0, lse2p, s),
+    HIP_TRY(launch_bwd_rowdot(G, o_br + plane, (int64_t)nh * n, D, s), "row dot launch");
+    HIP_TRY(launch_bwd_gather_f32(D, sb.q_idx, n, nh, 1.0f, 0, Dp, s), "D gather launch");
+    HIP_TRY(launch_bwd_gather_f32(lse_br + (size_t)nh * n, sb.q_idx, n, nh, log2e, 0, lse2p, s),
             "lse gather launch");
-    // attention backward per group
-    void *dqp = at<char>(ws, B.dqp), *dkp = at<char>(ws, B.dkp), *dvp = at<char>(ws, B.dvp);
-    {
-        AttnBwdLaunch a{};
-        a.q = static_cast<const bf16 *>(qp); a.k = static_cast<const bf16 *>(kp);
-        a.v = static_cast<const bf16 *>(vp); a.dov = static_cast<const bf16 *>(dov);
-        a.lse2 = lse2p; a.D = Dp;
-        a.dq = static_cast<bf16 *>(dqp); a.dk = static_cast<bf16 *>(dkp);
-        a.dv = static_cast<bf16 *>(dvp);
-        a.cu = saved->cu_seqlens; a.n_seg = m; a.len = n; a.n_heads = nh; a.scale = scale_of(dims);
-        a.max_items = B.plan_items;
-        attn_plan_carve(a.plan, at<char>(ws, B.plan), m, B.plan_items, 0);
-        HIP_TRY(launch_attention_bwd(a, s), "attention backward launch");
-    }
-    // back to token order
-    {
-        const void *gsrc[3] = {dqp, dkp, dvp};
-        void *gdst[3] = {grads->dq, grads->dk, grads->dv};
-        if ((st = run_gather(1, perm, dims, gsrc, gdst, 3, nullptr, nullptr, s)) != MOGA_OK)
-            return st;
-    }
-    // router: softmax backward, dx, dW
-    if (grads->dx || grads->dw) {
-        BwdRouterLaunch r{};
-        r.x = in->x; r.x_is_bf16 = in->x_dtype == MOGA_BF16; r.w = in->w; r.n = n;
-        r.d = dims->d_model; r.m = m; r.group_id = saved->group_id; r.counts = saved->counts;
-        r.dp = dp;
-        r.loss_coef = (float)(d_loss * dims->alpha * m / ((double)n * (double)n));
-        r.dr = at<float>(ws, B.dr); r.dx = grads->dx; r.dw = grads->dw;
-        r.dw_part = at<float>(ws, B.dw_part);
-        HIP_TRY(launch_router_bwd(r, s), "router backward launch");
-    }
+    bf16 *dqt = at<bf16>(ws, B.dqt), *dkt = at<bf16>(ws, B.dkt), *dvt = at<bf16>(ws, B.dvt);
+    a.q = qt; a.k = kt; a.v = vt; a.dov = dot; a.lse2 = lse2p; a.D = Dp;
+    a.dq = dqt; a.dk = dkt; a.dv = dvt;
+    a.cu_q = sb.cu_tq; a.cu_k = sb.cu_tk; a.n_seg = stga_n_groups(g); a.len_q = n; a.len_k = nk;
+    HIP_TRY(launch_attention_bwd(a, s), "temporal attention backward launch");
+    // 5 the mean: grad = (MoGA + per-frame + temporal at the token's positions) / 3
+    bf16 *dq = static_cast<bf16 *>(grads->dq), *dk = static_cast<bf16 *>(grads->dk),
+         *dv = static_cast<bf16 *>(grads->dv);
+    HIP_TRY(launch_grad_sum(dq, dqf, dqt, n, sb.tpos, 0, 1, n, nh, third, dq, s), "dQ sum launch");
+    HIP_TRY(launch_grad_sum(dk, dkf, dkt, nk, sb.tpos, 1, 3, n, nh, third, dk, s), "dK sum launch");
+    HIP_TRY(launch_grad_sum(dv, dvf, dvt, nk, sb.tpos, 1, 3, n, nh, third, dv, s), "dV sum launch");
     return MOGA_OK;
 }
 

@@ -31,10 +31,12 @@ namespace {
 
 // ---------------------------------------------------------------------------- planning
 // slots: blocks of the persistent grid that will run the items (0: no key-range split).
+// xcd: lay the whole items out in eight XCD-local queues (chains of one segment and head kept
+// whole, chain c in longest-first order going to queue c mod 8) instead of one list.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const int32_t *cu_k,
                                                      int n_seg, int64_t len_q, int64_t len_k,
                                                      int n_heads, int bq, int64_t max_items,
-                                                     int slots, AttnPlan p) {
+                                                     int slots, int xcd, AttnPlan p) {
     __shared__ int s_klen[kPlanSortMax];
     __shared__ int s_order[kPlanSortMax];
     __shared__ int s_scan[1024];
@@ -117,26 +119,98 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *cu_q, const i
         p.counter[3] = parts;
         p.counter[4] = 0;                           // dispatch counter of the split parts
         p.counter[5] = (n_items - first) * parts;   // split parts
+        // one queue unless the XCD-local layout below applies (it needs every item listed)
+        p.counter[6] = 0;
+        for (int x = 0; x < 8; ++x) p.counter[8 + x] = 0;
+        p.counter[16] = 0;
+        for (int x = 1; x <= 8; ++x) p.counter[16 + x] = first;
+    }
+    if (!xcd) return;
+    __syncthreads();
+    const int n_items = p.counter[1];
+    if (n_items != p.item_base[n_seg] || p.counter[5] != 0) return;  // clamped or split: one queue
+    // Chains c = r * n_heads + h (segment rank r in longest-first order, head h) of seg_ntile
+    // items each go to queue c mod 8: chain_off[c] = the items of the earlier chains of its queue
+    // (a scan with stride 8 over the chains, 1024 at a time, one carry per queue).
+    __shared__ int s_carry[8];
+    if (tid < 8) s_carry[tid] = 0;
+    __syncthreads();
+    const int64_t n_chains = (int64_t)n_seg * n_heads;
+    for (int64_t c0 = 0; c0 < n_chains; c0 += 1024) {
+        const int64_t c = c0 + tid;
+        int v = 0;
+        if (c < n_chains) {
+            const int r = (int)(c / n_heads);
+            v = p.seg_ntile[sorted ? s_order[r] : r];
+        }
+        s_scan[tid] = v;
+        __syncthreads();
+        for (int off = 8; off < 1024; off <<= 1) {
+            const int add = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += add;
+            __syncthreads();
+        }
+        if (c < n_chains) p.chain_off[c] = s_carry[tid & 7] + s_scan[tid] - v;
+        __syncthreads();
+        if (tid < 8) s_carry[tid] += s_scan[1016 + tid];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        int base = 0;
+        for (int x = 0; x < 8; ++x) {
+            p.counter[16 + x] = base;
+            base += s_carry[x];
+        }
+        p.counter[24] = base;  // == n_items
+        p.counter[6] = 1;
     }
 }
 
 // Dispatch entry i: item i before the first split item; from there, part u of split item b
 // (entry first + b parts + u) carries the item's (segment, head, q tile) and w = u + 1.
-__global__ __launch_bounds__(256) void fill_items_kernel(AttnPlan p, int n_seg) {
+__global__ __launch_bounds__(256) void fill_items_kernel(AttnPlan p, int n_seg, int n_heads,
+                                                          const int32_t *cu_q, const int32_t *cu_k,
+                                                          int64_t len_q, int64_t len_k) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= p.counter[1] + p.counter[5]) return;
     const int first = p.counter[2], parts = p.counter[3];
-    const int src = i < first ? i : first + (i - first) / parts;
-    const int part = i < first ? 0 : 1 + (i - first) % parts;
-    int lo = 0, hi = n_seg;  // item_base[lo] <= src < item_base[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.item_base[mid] <= src) lo = mid; else hi = mid;
+    int seg, head, qt, part;
+    if (p.counter[6]) {
+        // entry i of the XCD-major layout: queue x, then the chain of x that holds it
+        int x = 0;
+        while (x < 7 && p.counter[17 + x] <= i) ++x;
+        const int pos = i - p.counter[16 + x];
+        const int64_t n_chains = (int64_t)n_seg * n_heads;
+        int64_t lo = 0, hi = (n_chains - x + 7) / 8;  // chain_off[x + 8 lo] <= pos, last such
+        while (hi - lo > 1) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (p.chain_off[x + 8 * mid] <= pos) lo = mid; else hi = mid;
+        }
+        const int64_t c = x + 8 * lo;
+        seg = p.order[(int)(c / n_heads)];
+        head = (int)(c % n_heads);
+        qt = pos - p.chain_off[c];
+        part = 0;
+    } else {
+        const int src = i < first ? i : first + (i - first) / parts;
+        part = i < first ? 0 : 1 + (i - first) % parts;
+        int lo = 0, hi = n_seg;  // item_base[lo] <= src < item_base[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (p.item_base[mid] <= src) lo = mid; else hi = mid;
+        }
+        seg = p.order[lo];
+        const int local = src - p.item_base[lo];
+        const int nt = p.seg_ntile[seg];
+        head = local / nt;
+        qt = local % nt;
     }
-    const int seg = p.order[lo];
-    const int local = src - p.item_base[lo];
-    const int nt = p.seg_ntile[seg];
-    p.items[i] = make_int4(seg, local / nt, local % nt, part);
+    p.items[i] = make_int4(seg, head, qt, part);
+    // the segment's rows, clamped as the kernels use them (one load decodes an item)
+    const int64_t qb = clamp64(cu_q[seg], 0, len_q), qe = clamp64(cu_q[seg + 1], qb, len_q);
+    const int64_t kb = clamp64(cu_k[seg], 0, len_k), ke = clamp64(cu_k[seg + 1], kb, len_k);
+    p.spans[i] = make_int4((int)qb, (int)qe, (int)kb, (int)ke);
 }
 
 // ---------------------------------------------------------------------------- attention
@@ -455,7 +529,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
     constexpr int LOADS = TILEB / 16 / THREADS;  // direct 16-byte loads per thread per tile
     static_assert(LOADS * THREADS * 16 == TILEB, "tile must split into whole wave loads");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2][2][TILEB];  // [buf][K, V]
-    __shared__ int s_item;
+    __shared__ int s_item[2];
+    __shared__ int s_qbase[9];  // queue x holds entries [s_qbase[x], s_qbase[x + 1])
+    __shared__ __attribute__((aligned(16))) int4 s_desc[2][2];  // [slot]: items and spans entries
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, hh = lane >> 5;
@@ -485,20 +561,62 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         vgo[i] = t_dma_chunk(r, s16) + (IDX ? 0 : r * ROWB);
     }
 
-    for (;;) {
-        if (tid == 0) s_item = atomicAdd(a.plan.counter + (SPLIT ? 4 : 0), 1);
-        __syncthreads();
-        const int item = uniform(s_item);
-        __syncthreads();
-        if (item >= total) break;
+    // Work items come from an atomic counter.  Each block reserves its next item as soon as it
+    // starts one and hands the index to every wave after the item's first two tiles, where
+    // the next item's descriptor (head, query tile, segment rows: one entry of the plan) is
+    // loaded too; a new item then waits only for its own query rows and first key tiles.
+    // Whole items come from the plan's queues: one, or eight XCD-local ones (blocks run on XCD
+    // blockIdx.x mod 8) of which a block drains its own first and then the others in turn.  The
+    // split parts have a queue of their own.  Only thread 0 tracks the queue it draws from.
+    int *const queue = a.plan.counter + (SPLIT ? 4 : 8);
+    int qcur = SPLIT ? 0 : (int)(blockIdx.x & 7) * uniform(a.plan.counter[6]);
+    if (!SPLIT && tid < 9) s_qbase[tid] = a.plan.counter[16 + tid];  // read before the first grab
+    auto request = [&]() { return atomicAdd(queue + qcur, 1); };
+    // entry index of a drawn position (total once every queue is empty)
+    auto grab = [&](int raw) {
+        if constexpr (SPLIT) {
+            return raw;
+        } else {
+            for (int tries = 1;; ++tries) {
+                const int lo = s_qbase[qcur], hi = s_qbase[qcur + 1];
+                if (raw < hi - lo) return lo + raw;
+                if (tries == 8) return total;
+                qcur = (qcur + 1) & 7;
+                raw = request();
+            }
+        }
+    };
+    // The descriptor of entry e (its items and spans records, which the plan lays out one
+    // after the other) is fetched by two lanes of wave 0 straight into LDS slot `sl`: no
+    // registers are held for it, and the tile loop's own wait and barrier publish it.
+    const uint32_t span_off = (uint32_t)(reinterpret_cast<const char *>(a.plan.spans) -
+                                         reinterpret_cast<const char *>(a.plan.items));
+    const __amdgpu_buffer_rsrc_t rdesc = make_rsrc(
+        a.plan.items, span_off + (uint32_t)((SPLIT ? split_first + total : total) * 16));
+    auto fetch_desc = [&](int it, int sl) {
+        const uint32_t e = (uint32_t)(SPLIT ? split_first + it : it);
+        if (wave == 0 && lane < 2)
+            load_lds16(rdesc, reinterpret_cast<unsigned char *>(&s_desc[sl][0]),
+                       (int)((lane ? span_off : 0u) + 16u * e));
+    };
+    __syncthreads();  // s_qbase
+    if (tid == 0) s_item[0] = grab(request());
+    __syncthreads();
+    int item = uniform(s_item[0]);
+    int slot = 0;  // s_item[slot] and s_desc[slot] describe the current item
+    if (item < total) fetch_desc(item, 0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+    while (item < total) {
+        int next_raw = 0;
+        if (tid == 0) next_raw = request();
         // a split part (entry split_first + item, w = part + 1) takes its share of the
         // segment's key tiles and leaves its rows in split slot `item`
-        const int4 itm = a.plan.items[SPLIT ? split_first + item : item];
-        const int seg = uniform(itm.x), h = uniform(itm.y), qt = uniform(itm.z);
-        const int qb = uniform((int)clamp64(a.cu_q[seg], 0, a.len_q));
-        const int qe = uniform((int)clamp64(a.cu_q[seg + 1], qb, a.len_q));
-        int kb = uniform((int)clamp64(a.cu_k[seg], 0, a.len_k));
-        const int ke = uniform((int)clamp64(a.cu_k[seg + 1], kb, a.len_k));
+        const int4 itm = s_desc[slot][0], spn = s_desc[slot][1];
+        const int h = uniform(itm.y), qt = uniform(itm.z);
+        const int qb = uniform(spn.x), qe = uniform(spn.y);
+        int kb = uniform(spn.z);
+        const int ke = uniform(spn.w);
         int klen = ke - kb;
         if constexpr (SPLIT) {
             const int part = uniform(itm.w) - 1, nt = (klen + KT - 1) / KT;
@@ -595,14 +713,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                 }
             }
             if constexpr (MASK) {
-                const int key0 = t * KT;
+                // score v of sub-block sb is key t*KT + sb*32 + 8*(v/4) + 4*hh + v%4: compare the
+                // constant part against one per-lane limit (no per-lane key table to keep)
+                const int lim = klen - t * KT - 4 * hh;
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int key = key0 + sb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-                        if (key >= klen) sacc[sb][v] = -INFINITY;
-                    }
+                    for (int v = 0; v < 16; ++v)
+                        if (sb * 32 + 8 * (v >> 2) + (v & 3) >= lim) sacc[sb][v] = -INFINITY;
             }
             // this lane's largest score of each sub-block (16 keys each)
             float pm[2];
@@ -709,8 +827,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         using B1 = std::integral_constant<int, 1>;
         using NoMask = std::integral_constant<bool, false>;
         using Mask = std::integral_constant<bool, true>;
+        // the next item's index to every wave, and its descriptor requested into the other slot
+        int next = total;
+        auto handoff = [&]() {
+            if (tid == 0) s_item[slot ^ 1] = grab(next_raw);
+            __syncthreads();
+            next = uniform(s_item[slot ^ 1]);
+            if (next < total) fetch_desc(next, slot ^ 1);
+        };
         int t = 0;
+        // Short-segment (4-wave) items hand off early, two tiles in, when at least two more
+        // tiles follow to hide the descriptor load; the long MoGA items keep their tile loop
+        // free of it and hand off at the end.
+        constexpr bool EARLY = WAVES == 4;
+        const bool handed = EARLY && nfull >= 4;
         for (; t + 1 < nfull; t += 2) {
+            if (EARLY && t == 2) handoff();
             tile(B0{}, NoMask{}, t);
             tile(B1{}, NoMask{}, t + 1);
         }
@@ -722,6 +854,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
             if (t & 1) tile(B1{}, Mask{}, t);
             else tile(B0{}, Mask{}, t);
         }
+        if (!handed) {
+            handoff();
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the descriptor has landed
+            __syncthreads();
+        }
+        slot ^= 1;
 
         const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
         if constexpr (SPLIT) {
@@ -737,14 +875,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                                     o[ti][kq * 4 + 3]);
             if (hh == 0)
                 *reinterpret_cast<float2 *>(a.plan.split_ml + 2 * row) = make_float2(m_run, l_tot);
+            item = next;
             continue;
         }
         if (qvalid) {
-            // the 8-wave (MoGA) launches may write through an output map, with the log-sum-exp
-            // and the mean of three branches; the 4-wave (short-segment) launches store plainly
+            // the 8-wave (MoGA) launches may write through an output map and store the mean of
+            // three branches; the 4-wave (short-segment) launches store their rows plainly
             constexpr bool FULL_EPI = WAVES == 8;
             const int64_t orow = FULL_EPI ? out_row(a, qrow, qphys) : qphys;
-            if (FULL_EPI && a.lse && hh == 0)  // log(sum exp(scale q.k)) = scale*m + ln(l)
+            if (a.lse && hh == 0)  // log(sum exp(scale q.k)) = scale*m + ln(l)
                 a.lse[(int64_t)h * a.o_rows + orow] =
                     l_tot > 0.0f ? (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
             float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
@@ -766,6 +905,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                 if constexpr (FULL_EPI) asm volatile("" ::: "memory");
             }
         }
+        item = next;
     }
 }
 
@@ -867,7 +1007,8 @@ static int64_t split_cap(int64_t split_rows) {
 size_t attn_plan_bytes(int32_t n_seg, int64_t max_items, int64_t split_rows) {
     const size_t seg = align256(sizeof(int32_t) * (size_t)(n_seg + 1));
     const size_t cap = (size_t)split_cap(split_rows);
-    return 4 * seg + align256(sizeof(int4) * (size_t)(max_items + cap)) + 256 +
+    return 4 * seg + 2 * align256(sizeof(int4) * (size_t)(max_items + cap)) +
+           align256(sizeof(int32_t) * (size_t)max_items) + 256 +
            cap * kSplitRows * (128 + 2) * sizeof(float);
 }
 
@@ -882,6 +1023,10 @@ void attn_plan_carve(AttnPlan &p, void *base, int32_t n_seg, int64_t max_items,
     p.split_cap = (int32_t)split_cap(split_rows);
     p.items = reinterpret_cast<int4 *>(b);
     b += align256(sizeof(int4) * (size_t)(max_items + p.split_cap));
+    p.spans = reinterpret_cast<int4 *>(b);
+    b += align256(sizeof(int4) * (size_t)(max_items + p.split_cap));
+    p.chain_off = reinterpret_cast<int32_t *>(b);
+    b += align256(sizeof(int32_t) * (size_t)max_items);
     p.counter = reinterpret_cast<int32_t *>(b); b += 256;
     p.split_o = reinterpret_cast<float *>(b); b += (size_t)p.split_cap * kSplitRows * 128 * sizeof(float);
     p.split_ml = reinterpret_cast<float *>(b);
@@ -891,11 +1036,11 @@ hipError_t launch_attn_plan(const int32_t *cu_q, const int32_t *cu_k, int32_t n_
                             int64_t len_q, int64_t len_k, int n_heads, int bq, int64_t max_items,
                             const AttnPlan &plan, hipStream_t s) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, cu_q, cu_k, n_seg, len_q, len_k,
-                       n_heads, bq, max_items, 0, plan);
+                       n_heads, bq, max_items, 0, 0, plan);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)((max_items + plan.split_cap + 255) / 256)), dim3(256), 0,
-                       s, plan, n_seg);
+                       s, plan, n_seg, n_heads, cu_q, cu_k, len_q, len_k);
     return hipGetLastError();
 }
 
@@ -907,9 +1052,8 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     const bool indexed = a.kv_idx || a.q_idx;
     const bool direct = a.head_dim == 128 && a.kv_rows * 256 < (int64_t(1) << 31);
     const int waves = a.waves == 4 ? 4 : 8;
-    // an output map, the log-sum-exp and the three-branch mean are epilogue features of the
-    // 8-wave launches only
-    if (direct && waves == 4 && (a.o_idx || a.lse || a.mean_a)) return hipErrorInvalidValue;
+    // an output map and the three-branch mean are epilogue features of the 8-wave launches only
+    if (direct && waves == 4 && (a.o_idx || a.mean_a || a.o_raw)) return hipErrorInvalidValue;
     const int bq = direct ? 32 * waves : (indexed ? 128 : 256);
     int cus = 0;
     hipError_t e = device_cus(&cus);
@@ -918,12 +1062,16 @@ hipError_t launch_attention(const AttnLaunch &a, hipStream_t s) {
     // with 256-row items (long segments) may split the last items' key ranges over the grid
     const int slots = cus * (8 / waves);
     const bool splits = direct && waves == 8;
+    // long segments (8-wave launches) share one queue, whose tail may split; the items of short
+    // segments (4-wave launches) go to XCD-local queues, so the few items of a segment and head
+    // stream its keys and values through one L2
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.cu_q, a.cu_k, a.n_seg, a.len_q,
-                       a.len_k, a.n_heads, bq, a.max_items, splits ? slots : 0, a.plan);
+                       a.len_k, a.n_heads, bq, a.max_items, splits ? slots : 0,
+                       direct && !splits ? 1 : 0, a.plan);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t fill_blocks = (a.max_items + a.plan.split_cap + 255) / 256;
     hipLaunchKernelGGL(fill_items_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, s, a.plan,
-                       a.n_seg);
+                       a.n_seg, a.n_heads, a.cu_q, a.cu_k, a.len_q, a.len_k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 grid((unsigned)slots), blk((unsigned)(64 * waves));
     const dim3 grid4((unsigned)(cus * 2)), blk4(256u);

@@ -1,4 +1,5 @@
-// Backward of the group attention (head_dim 128, groups as contiguous row ranges), given the
+// Backward of the group attention (head_dim 128, segments as contiguous row ranges, with
+// separate query and key ranges per segment), given the
 // forward's softmax normaliser per row (lse, natural log) and D = <dO', O'> per row:
 //   P = exp(scale Q K^T - lse),  dP = dO' V^T,  dS = P * (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO'
@@ -61,13 +62,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunc
         if (item >= total) break;
         const int4 itm = a.plan.items[item];
         const int seg = uniform(itm.x), h = uniform(itm.y), qt = uniform(itm.z);
-        const int rb = uniform((int)clamp64(a.cu[seg], 0, a.len));
-        const int re = uniform((int)clamp64(a.cu[seg + 1], rb, a.len));
+        const int qb = uniform((int)clamp64(a.cu_q[seg], 0, a.len_q));
+        const int qe = uniform((int)clamp64(a.cu_q[seg + 1], qb, a.len_q));
+        const int rb = uniform((int)clamp64(a.cu_k[seg], 0, a.len_k));
+        const int re = uniform((int)clamp64(a.cu_k[seg + 1], rb, a.len_k));
         const int klen = re - rb;
-        const int qrow = rb + qt * BQ + wave * 32 + j;
-        const bool qvalid = qrow < re;
-        const int qrow_c = qvalid ? qrow : re - 1;  // re > rb for every item
-        const int64_t hrow = (int64_t)h * a.len;
+        const int qrow = qb + qt * BQ + wave * 32 + j;
+        const bool qvalid = qrow < qe;
+        const int qrow_c = qvalid ? qrow : qe - 1;  // qe > qb for every item
+        const int64_t hrow = (int64_t)h * a.len_q, hrow_k = (int64_t)h * a.len_k;
         bf16x8 qf[NS], gf[NS];
         {
             const bf16 *qp = a.q + (hrow + qrow_c) * HD + 8 * hh;
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunc
             }
         }
         const float lse2 = a.lse2[hrow + qrow_c], dd = a.D[hrow + qrow_c];
-        const bf16 *kbase = a.k + hrow * HD, *vbase = a.v + hrow * HD;
+        const bf16 *kbase = a.k + hrow_k * HD, *vbase = a.v + hrow_k * HD;
         const int ntiles = (klen + KT - 1) / KT;
 
         // key tile t -> buffer BUF; rows past the group read as zeros
@@ -252,17 +255,19 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
         if (item >= total) break;
         const int4 itm = a.plan.items[item];
         const int seg = uniform(itm.x), h = uniform(itm.y), kt = uniform(itm.z);
-        const int rb = uniform((int)clamp64(a.cu[seg], 0, a.len));
-        const int re = uniform((int)clamp64(a.cu[seg + 1], rb, a.len));
+        const int kb = uniform((int)clamp64(a.cu_k[seg], 0, a.len_k));
+        const int ke = uniform((int)clamp64(a.cu_k[seg + 1], kb, a.len_k));
+        const int rb = uniform((int)clamp64(a.cu_q[seg], 0, a.len_q));
+        const int re = uniform((int)clamp64(a.cu_q[seg + 1], rb, a.len_q));
         const int qlen = re - rb;
-        const int krow = rb + kt * BK + kw * 32 + j;
-        const bool kvalid = krow < re;
-        const int krow_c = kvalid ? krow : re - 1;
-        const int64_t hrow = (int64_t)h * a.len;
+        const int krow = kb + kt * BK + kw * 32 + j;
+        const bool kvalid = krow < ke;
+        const int krow_c = kvalid ? krow : ke - 1;  // ke > kb for every item
+        const int64_t hrow = (int64_t)h * a.len_q, hrow_k = (int64_t)h * a.len_k;
         // B operand: K^T in dV waves, V^T in dK waves
         bf16x8 bf[NS];
         {
-            const bf16 *bp = (dk_role ? a.v : a.k) + (hrow + krow_c) * HD + 8 * hh;
+            const bf16 *bp = (dk_role ? a.v : a.k) + (hrow_k + krow_c) * HD + 8 * hh;
 #pragma unroll
             for (int s = 0; s < NS; ++s) bf[s] = *reinterpret_cast<const bf16x8 *>(bp + 16 * s);
         }
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
         if (dk_role) run(std::true_type{});
         else run(std::false_type{});
         if (kvalid) {
-            bf16 *op = (dk_role ? a.dk : a.dv) + (hrow + krow) * HD + 4 * hh;
+            bf16 *op = (dk_role ? a.dk : a.dv) + (hrow_k + krow) * HD + 4 * hh;
             const float mul = dk_role ? a.scale : 1.0f;
 #pragma unroll
             for (int ti = 0; ti < NT; ++ti)
@@ -459,16 +464,16 @@ hipError_t launch_attention_bwd(const AttnBwdLaunch &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     // dQ: items of 256 query rows, inner loop over the group's keys
     constexpr int kDqWaves = 8;
-    if ((e = launch_attn_plan(a.cu, a.cu, a.n_seg, a.len, a.len, a.n_heads, 32 * kDqWaves,
-                              a.max_items, a.plan, s)) != hipSuccess)
+    if ((e = launch_attn_plan(a.cu_q, a.cu_k, a.n_seg, a.len_q, a.len_k, a.n_heads,
+                              32 * kDqWaves, a.max_items, a.plan, s)) != hipSuccess)
         return e;
     hipLaunchKernelGGL(attn_bwd_dq_kernel<kDqWaves>, dim3((unsigned)cus), dim3(64 * kDqWaves), 0, s,
                        a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // dK, dV: items of 128 key rows, inner loop over the group's queries (the plan is rebuilt
     // in place once the dQ kernel, earlier on the stream, is done with it)
-    if ((e = launch_attn_plan(a.cu, a.cu, a.n_seg, a.len, a.len, a.n_heads, 128, a.max_items,
-                              a.plan, s)) != hipSuccess)
+    if ((e = launch_attn_plan(a.cu_k, a.cu_q, a.n_seg, a.len_k, a.len_q, a.n_heads, 128,
+                              a.max_items, a.plan, s)) != hipSuccess)
         return e;
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)cus), dim3(512), 0, s, a);
     return hipGetLastError();

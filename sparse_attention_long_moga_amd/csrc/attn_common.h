@@ -130,9 +130,13 @@ __device__ __forceinline__ int64_t out_row(const AttnLaunch &a, int64_t qrow, in
 
 // Stores four consecutive output channels of one row from their fp32 values: rounded to bf16
 // once, after the mean with the two other branches' rows when the launch asks for it
-// (out = (v + a + b) / 3 in fp32).  off: element offset of the first of the four in o.
+// (out = (v + a + b) / 3 in fp32), and the row itself to o_raw when given (the state the
+// backward of the mean needs).  off: element offset of the first of the four in o.
 __device__ __forceinline__ void store4(const AttnLaunch &a, int64_t off, float v0, float v1,
                                        float v2, float v3) {
+    if (a.o_raw)
+        *reinterpret_cast<uint2 *>(a.o_raw + off) =
+            make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
     if (a.mean_a) {
         const uint2 ua = *reinterpret_cast<const uint2 *>(a.mean_a + off);
         const uint2 ub = *reinterpret_cast<const uint2 *>(a.mean_b + off);

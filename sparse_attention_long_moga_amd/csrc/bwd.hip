@@ -38,30 +38,77 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16 *d_out, cons
     if (row < rows && ch == 0) D[row] = acc;
 }
 
-// dp_t = sum over heads (in head order) of D[h][t], divided by p_t.
+// dp_t = scale * (sum over heads (in head order) of D[h][t]) / p_t.
 __global__ __launch_bounds__(256) void bwd_dp_kernel(const float *D, const float *p_sel,
-                                                      int64_t n, int n_heads, float *dp) {
+                                                      int64_t n, int n_heads, float scale,
+                                                      float *dp) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= n) return;
     float s = 0.0f;
     for (int h = 0; h < n_heads; ++h) s += D[(int64_t)h * n + t];
-    dp[t] = s / p_sel[t];
+    dp[t] = scale * s / p_sel[t];
 }
 
 // fp32 [H][N] rows by perm: dst[h][j] = mult * src[h][perm[j]], or with inverse set
-// dst[h][perm[j]] = mult * src[h][j].  perm entries outside [0, n) are skipped.
+// dst[h][perm[j]] = mult * src[h][j].  perm entries outside [0, n) are skipped; perm NULL is
+// the identity.
 __global__ __launch_bounds__(256) void bwd_gather_f32_kernel(const float *src, const int32_t *perm,
                                                               int64_t n, float mult, int inverse,
                                                               float *dst) {
     const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (j >= n) return;
     const int64_t h = blockIdx.y;
-    const int32_t pj = perm[j];
+    const int32_t pj = perm ? perm[j] : (int32_t)j;
     if (inverse) {
         if (pj >= 0 && pj < n) dst[h * n + pj] = mult * src[h * n + j];
     } else {
         dst[h * n + j] = (pj >= 0 && pj < n) ? mult * src[h * n + pj] : 0.0f;
     }
+}
+
+// Gradient of a token under the mean of the three branches (hybrid backward): the two
+// token-order gradients a and b and the position-order rows c of the token (its query position
+// for dQ; for dK and dV every key position that holds it, i.e. its own group's and those of
+// the groups that borrow its frame), summed in fp32 in that order and scaled by w.  One thread
+// per 8 channels of a head_dim-128 row; every row of out has exactly this one writer.
+__global__ __launch_bounds__(256) void grad_sum_kernel(const bf16 *a, const bf16 *b, const bf16 *c,
+                                                        int64_t c_rows, const int32_t *pos,
+                                                        int first, int npos, int64_t n, float w,
+                                                        bf16 *out) {
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16-byte chunk of row h*n + t
+    const int64_t row = gi >> 4;
+    const int h = blockIdx.y;
+    if (row >= n) return;
+    const int ch = (int)(gi & 15);
+    const int64_t off = ((int64_t)h * n + row) * 128 + ch * 8;
+    const uint4 ua = *reinterpret_cast<const uint4 *>(a + off);
+    const uint4 ub = *reinterpret_cast<const uint4 *>(b + off);
+    const uint32_t aw[4] = {ua.x, ua.y, ua.z, ua.w}, bw[4] = {ub.x, ub.y, ub.z, ub.w};
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = bf16_lo(aw[i]) + bf16_lo(bw[i]);
+        acc[2 * i + 1] = bf16_hi(aw[i]) + bf16_hi(bw[i]);
+    }
+    for (int k = 0; k < npos; ++k) {
+        const int32_t p = pos[4 * row + first + k];
+        if (p < 0 || p >= c_rows) continue;
+        const uint4 uc = *reinterpret_cast<const uint4 *>(c + ((int64_t)h * c_rows + p) * 128 + ch * 8);
+        const uint32_t cw[4] = {uc.x, uc.y, uc.z, uc.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += bf16_lo(cw[i]);
+            acc[2 * i + 1] += bf16_hi(cw[i]);
+        }
+    }
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2 v = {(__bf16)(w * acc[2 * i]), (__bf16)(w * acc[2 * i + 1])};
+        r[i] = __builtin_bit_cast(uint32_t, v);
+    }
+    *reinterpret_cast<uint4 *>(out + off) = make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 // Router backward for the tokens of one wave: logits x_t W (fp32), softmax, dr_t, dx_t.  A wave
@@ -300,10 +347,10 @@ hipError_t launch_bwd_rowdot(const bf16 *d_out, const bf16 *out, int64_t rows, f
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dp(const float *D, const float *p_sel, int64_t n, int n_heads, float *dp,
-                         hipStream_t s) {
+hipError_t launch_bwd_dp(const float *D, const float *p_sel, int64_t n, int n_heads, float scale,
+                         float *dp, hipStream_t s) {
     hipLaunchKernelGGL(bwd_dp_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, D, p_sel,
-                       n, n_heads, dp);
+                       n, n_heads, scale, dp);
     return hipGetLastError();
 }
 
@@ -311,6 +358,15 @@ hipError_t launch_bwd_gather_f32(const float *src, const int32_t *perm, int64_t 
                                  float mult, int inverse, float *dst, hipStream_t s) {
     hipLaunchKernelGGL(bwd_gather_f32_kernel, dim3((unsigned)((n + 255) / 256), (unsigned)n_heads),
                        dim3(256), 0, s, src, perm, n, mult, inverse, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_sum(const bf16 *a, const bf16 *b, const bf16 *c, int64_t c_rows,
+                           const int32_t *pos, int first, int npos, int64_t n, int n_heads,
+                           float w, bf16 *out, hipStream_t s) {
+    const int64_t chunks = n * 16;
+    hipLaunchKernelGGL(grad_sum_kernel, dim3((unsigned)((chunks + 255) / 256), (unsigned)n_heads),
+                       dim3(256), 0, s, a, b, c, c_rows, pos, first, npos, n, w, out);
     return hipGetLastError();
 }
 

@@ -96,6 +96,7 @@ struct GatherLaunch {
     const float *p_sel;  // optional gather of one fp32 value per row (inverse == 0 only)
     float *p_perm;
     const float *src_scale;  // NULL, or (inverse == 0, one tensor) dst row j = src_scale[perm[j]] * src row
+    int64_t src_rows;        // (inverse == 0) rows per head of src when != 0 (else n); perm < it
 };
 hipError_t launch_gather(const GatherLaunch &a, hipStream_t s);
 
@@ -106,7 +107,11 @@ struct AttnPlan {
     int32_t *order;      // [n_seg] segments by descending key length
     int32_t *item_base;  // [n_seg + 1]
     int4 *items;         // [max_items + split_cap] (segment, head, q tile, split part + 1 or 0)
-    // [5]: dispatch counter, dispatch count, first split item, parts per split item, item count
+    int4 *spans;         // [max_items + split_cap] the entry's segment: (qb, qe, kb, ke), clamped
+    int32_t *chain_off;  // [max_items] XCD-local queues: offset of chain (segment, head) in its queue
+    // [0..5]: dispatch counter, dispatch count, first split item, parts per split item, dispatch
+    // counter and count of the split parts; [6]: 1 if the whole items sit in XCD-local queues;
+    // [8..15]: the queues' dispatch counters; [16..24]: queue x holds entries [q[x], q[x+1])
     int32_t *counter;
     // Key-range split of the last items (forward, head_dim 128): part u of the split items
     // leaves its unnormalised rows in split_o [u][kSplitRows][128] and (row max, row sum) in
@@ -138,6 +143,7 @@ struct AttnLaunch {
     const int32_t *o_idx;    // NULL: output rows are the physical q rows; else logical q row ->
                              // physical output row (of o, lse and the mean rows)
     const bf16 *mean_a, *mean_b;  // NULL, or [H][o_rows][hd] rows stored as (o + a + b) / 3
+    bf16 *o_raw;             // NULL, or [H][o_rows][hd]: the rows before the mean, stored too
     int64_t len_q, len_k;    // logical rows
     int64_t q_rows, kv_rows, o_rows;  // physical rows per head
     int n_heads, head_dim;
@@ -156,14 +162,16 @@ hipError_t launch_attn_plan(const int32_t *cu_q, const int32_t *cu_k, int32_t n_
 
 // ---------------------------------------------------------------- attention backward
 struct AttnBwdLaunch {
-    const bf16 *q, *k, *v;   // group order [H][len][hd]
-    const bf16 *dov;         // dO' = p(g|x) * d_out, group order [H][len][hd]
-    const float *lse2;       // [H][len]: log2(sum_u exp2(c q.k_u)), c = scale * log2(e)
-    const float *D;          // [H][len]: <dO', O'>
-    bf16 *dq, *dk, *dv;      // group order [H][len][hd]
-    const int32_t *cu;       // [n_seg + 1]: group u's rows are [cu[u], cu[u+1]) for q and k
+    const bf16 *q, *k, *v;   // segment order: q [H][len_q][hd], k and v [H][len_k][hd]
+    const bf16 *dov;         // dO' (the upstream gradient of each row's output), [H][len_q][hd]
+    const float *lse2;       // [H][len_q]: log2(sum_u exp2(c q.k_u)), c = scale * log2(e)
+    const float *D;          // [H][len_q]: <dO', O'>
+    bf16 *dq;                // [H][len_q][hd]
+    bf16 *dk, *dv;           // [H][len_k][hd]
+    const int32_t *cu_q;     // [n_seg + 1]: segment u's query rows are [cu_q[u], cu_q[u+1])
+    const int32_t *cu_k;     // [n_seg + 1]: and its key rows [cu_k[u], cu_k[u+1])
     int32_t n_seg;
-    int64_t len;             // rows per head
+    int64_t len_q, len_k;    // rows per head
     int n_heads;
     float scale;
     AttnPlan plan;           // rebuilt for each of the two kernels
@@ -190,7 +198,7 @@ struct BwdRouterLaunch {
 int64_t bwd_dw_chunks(int64_t n);
 hipError_t launch_bwd_rowdot(const bf16 *d_out, const bf16 *out, int64_t rows, float *D,
                              hipStream_t s);
-hipError_t launch_bwd_dp(const float *D, const float *p_sel, int64_t n, int n_heads, float *dp,
+hipError_t launch_bwd_dp(const float *D, const float *p_sel, int64_t n, int n_heads, float scale, float *dp,
                          hipStream_t s);
 hipError_t launch_bwd_gather_f32(const float *src, const int32_t *perm, int64_t n, int n_heads,
                                  float mult, int inverse, float *dst, hipStream_t s);
@@ -208,7 +216,15 @@ struct StgaBuffers {
     int32_t *cu_f;       // [frames + 1]
     int32_t *q_idx;      // [N]
     int32_t *kv_idx;     // [N + extra]
+    int32_t *tpos;       // NULL or [N][4]: the token's query position and its key positions (its
+                         // own, then as borrowed by the next and the previous shot, -1 if none)
 };
+// out[h][t] = w * (a[h][t] + b[h][t] + sum of c[h][p] over the positions p in pos[4t + first ..
+// 4t + first + npos) that are >= 0), in fp32, rounded to bf16 once (head_dim 128; a, b and out
+// token order, out may be a; c with c_rows rows per head)
+hipError_t launch_grad_sum(const bf16 *a, const bf16 *b, const bf16 *c, int64_t c_rows,
+                           const int32_t *pos, int first, int npos, int64_t n, int n_heads,
+                           float w, bf16 *out, hipStream_t s);
 int32_t stga_n_groups(const StgaGeom &g);
 int64_t stga_extra_rows(const StgaGeom &g);
 hipError_t launch_stga_index(const StgaGeom &g, const StgaBuffers &b, hipStream_t s);

@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *gid, int64_
 // Row gather/scatter.  grid = (row blocks, heads, tensors); each thread moves 16 bytes.  Every
 // byte is read once and written once, so the accesses are non-temporal (streamed past the
 // caches rather than kept in them: about 10% faster than ordinary loads and stores here).
-// SCALED: dst row j = bf16(src_scale[perm[j]] * src row perm[j]) (forward direction only)
+// SCALED: dst row j = bf16(src_scale[perm[j]] * src row perm[j]) (forward direction only).  In
+// the forward direction src may hold another number of rows per head than dst (src_rows).
 template <int HD, bool SCALED>
 __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch a) {
     typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch a) {
     constexpr int PASSES = 8;
     const int tensor = blockIdx.z, h = blockIdx.y;
     const int64_t n = a.n;
+    const int64_t srows = (!a.inverse && a.src_rows > 0) ? a.src_rows : n;  // rows perm may name
     const int64_t head_off = (int64_t)h * n * HD;
     // select by comparisons: indexing the by-value pointer arrays with a runtime value
     // would place the whole argument struct in per-lane scratch memory
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch a) {
     if (tensor == 1) { sv = a.src[1]; dv = a.dst[1]; }
     if (tensor == 2) { sv = a.src[2]; dv = a.dst[2]; }
     if (tensor == 3) { sv = a.src[3]; dv = a.dst[3]; }
-    const bf16 *src = static_cast<const bf16 *>(sv) + head_off;
+    const bf16 *src = static_cast<const bf16 *>(sv) + (a.inverse ? head_off : (int64_t)h * srows * HD);
     bf16 *dst = static_cast<bf16 *>(dv) + head_off;
     const int r_in = threadIdx.x / CH, ch = threadIdx.x % CH;
     const int64_t j0 = (int64_t)blockIdx.x * ROWS * PASSES + r_in;
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch a) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const int64_t j = j0 + p * ROWS;
-        const bool ok = j < n && pj[p] >= 0 && pj[p] < n;
+        const bool ok = j < n && pj[p] >= 0 && pj[p] < srows;
         const int64_t s_row = ok ? (a.inverse ? j : (int64_t)pj[p]) : 0;
         buf[p] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(src + s_row * HD + ch * 8));
     }
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch a) {
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
             const int64_t j = j0 + p * ROWS;
-            const bool ok = j < n && pj[p] >= 0 && pj[p] < n;
+            const bool ok = j < n && pj[p] >= 0 && pj[p] < srows;
             const float f = a.src_scale[ok ? pj[p] : 0];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherLaunch a) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const int64_t j = j0 + p * ROWS;
-        if (j < n && pj[p] >= 0 && pj[p] < n) {
+        if (j < n && pj[p] >= 0 && pj[p] < srows) {
             const int64_t d_row = a.inverse ? (int64_t)pj[p] : j;
             __builtin_nontemporal_store(buf[p], reinterpret_cast<i32x4 *>(dst + d_row * HD + ch * 8));
         }

@@ -16,6 +16,8 @@
 //                          the previous shot's last frames (first chunk of a shot), then
 //                          the rows of the next shot's first frames (last chunk).
 // The per-frame grouping is contiguous in frame-major token order: cu_f[f] = f*H*W.
+// For the backward the same pass can also record, per token, the inverse of these maps: its
+// query position and the (up to three) key positions that hold it.
 #include "moga_internal.h"
 
 namespace moga {
@@ -99,8 +101,10 @@ __global__ __launch_bounds__(256) void stga_index_kernel(StgaGeom g, StgaBuffers
     const int wt = g.win_h * g.win_w;
     const int grp = (r[SI_CB] + c) * nwin + w;
     const int row = ((f - (start + c * T)) * g.win_h + ly) * g.win_w + lx;
-    b.q_idx[b.cu_tq[grp] + row] = (int32_t)t;
-    b.kv_idx[b.cu_tk[grp] + row] = (int32_t)t;
+    const int32_t qpos = b.cu_tq[grp] + row, kpos = b.cu_tk[grp] + row;
+    int32_t next_pos = -1, prev_pos = -1;
+    b.q_idx[qpos] = (int32_t)t;
+    b.kv_idx[kpos] = (int32_t)t;
     if (s + 1 < S) {  // borrowed by the first chunk of shot s+1
         const int *rn = b.shot_info + (s + 1) * SI_W;
         const int apn = rn[SI_AP];
@@ -109,7 +113,8 @@ __global__ __launch_bounds__(256) void stga_index_kernel(StgaGeom g, StgaBuffers
             const int g2 = rn[SI_CB] * nwin + w;
             const int tf2 = rn[SI_LEN] < T ? rn[SI_LEN] : T;
             const int r2 = ((f - f0) * g.win_h + ly) * g.win_w + lx;
-            b.kv_idx[b.cu_tk[g2] + tf2 * wt + r2] = (int32_t)t;
+            next_pos = b.cu_tk[g2] + tf2 * wt + r2;
+            b.kv_idx[next_pos] = (int32_t)t;
         }
     }
     if (s > 0) {  // borrowed by the last chunk of shot s-1
@@ -121,9 +126,12 @@ __global__ __launch_bounds__(256) void stga_index_kernel(StgaGeom g, StgaBuffers
             const int tf3 = rp[SI_LEN] - lastc * T;
             const int prev_rows = (lastc == 0 ? rp[SI_AP] : 0) * wt;
             const int r3 = ((f - start) * g.win_h + ly) * g.win_w + lx;
-            b.kv_idx[b.cu_tk[g3] + tf3 * wt + prev_rows + r3] = (int32_t)t;
+            prev_pos = b.cu_tk[g3] + tf3 * wt + prev_rows + r3;
+            b.kv_idx[prev_pos] = (int32_t)t;
         }
     }
+    if (b.tpos)
+        *reinterpret_cast<int4 *>(b.tpos + 4 * t) = make_int4(qpos, kpos, next_pos, prev_pos);
 }
 
 // Group-balancing loss (papernotes.org MoGA note, 关键设计 3): F_i = n_i / N,

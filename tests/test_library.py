@@ -160,18 +160,54 @@ def test_backward_argument_checks(lib):
     assert lib.moga_backward_workspace_bytes(ctypes.byref(_dims(n_groups=0))) == 0
 
 
-def test_hybrid_forward_refuses_lse(lib):
-    """lse belongs to a MoGA-only out (moga_backward pairs the two), so a hybrid forward that
-    asks for it is refused before any launch."""
+def test_hybrid_forward_lse_needs_branches(lib):
+    """With a STGA layout lse holds the three branches' normalisers, which pair with the
+    branch rows: asked for without o_branches the forward is refused before any launch, and
+    o_branches without a STGA layout is an argument error."""
     from sparse_attention_long_moga_amd._capi import MogaInputs, MogaOutputs
     n = 4 * 6 * 8
     d = _dims(n_tokens=n)
     lay = make_stga_layout(4, 6, 8, [0, 2, 4], 3, 4, 2, 2)
     p = 256
     ins = MogaInputs(p, 1, p, p, p, p, None)
-    outs = MogaOutputs(p, p, None, None, None, None, None, None, p)
+    outs = MogaOutputs(p, p, None, None, None, None, None, None, p, None)
+    branches_only = MogaOutputs(p, p, None, None, None, None, None, None, None, p)
     for fn in (lib.moga_forward, lib.moga_forward_fused):
         st = fn(ctypes.byref(ins), ctypes.byref(d), lay.ref(), ctypes.byref(outs),
                 ctypes.c_void_p(256), 1 << 40, None)
         assert st == _capi.MOGA_ERR_UNSUPPORTED
-        assert "lse" in lib.moga_last_error().decode()
+        assert "o_branches" in lib.moga_last_error().decode()
+        st = fn(ctypes.byref(ins), ctypes.byref(d), None, ctypes.byref(branches_only),
+                ctypes.c_void_p(256), 1 << 40, None)
+        assert st == _capi.MOGA_ERR_ARG
+        assert "STGA" in lib.moga_last_error().decode()
+
+
+def test_hybrid_backward_argument_checks(lib):
+    """moga_hybrid_backward validates before touching a GPU: head_dim, the layout, NULL
+    pointers, workspace; its workspace covers the temporal branch's borrowed key rows."""
+    from sparse_attention_long_moga_amd._capi import MogaGrads, MogaInputs, MogaSaved
+    n = 6 * 8 * 16
+    lay = make_stga_layout(6, 8, 16, [0, 3, 6], 4, 8, 2, 2)
+    p = 256
+    ins = MogaInputs(p, 1, p, p, p, p, None)
+    sav = MogaSaved(p, p, p, p, p, p, p)
+    gr = MogaGrads(p, p, p, None, None, None)
+    d128 = _dims(n_tokens=n, head_dim=128)
+    ws = lib.moga_hybrid_backward_workspace_bytes(ctypes.byref(d128), lay.ref())
+    assert ws > lib.moga_backward_workspace_bytes(ctypes.byref(d128))
+    assert lib.moga_hybrid_backward_workspace_bytes(ctypes.byref(_dims(n_tokens=n)), lay.ref()) == 0
+    assert lib.moga_hybrid_backward_workspace_bytes(ctypes.byref(d128), None) == 0
+    call = lambda d, i=ins, s=sav, g=gr, dout=p, w=ws, wsp=p, st=lay.ref(): \
+        lib.moga_hybrid_backward(ctypes.byref(i) if i else None, ctypes.byref(s) if s else None,
+                                 st, dout, 0.5, ctypes.byref(d), ctypes.byref(g) if g else None,
+                                 wsp, w, None)
+    assert call(_dims(n_tokens=n, head_dim=64)) == _capi.MOGA_ERR_UNSUPPORTED
+    assert "head_dim 128" in lib.moga_last_error().decode()
+    assert call(d128, st=None) == _capi.MOGA_ERR_ARG
+    assert "stga" in lib.moga_last_error().decode()
+    bad = make_stga_layout(6, 8, 16, [0, 3, 6], 3, 8, 2, 2)  # 3 rows do not tile 8
+    assert call(d128, st=bad.ref()) == _capi.MOGA_ERR_ARG
+    assert call(d128, s=MogaSaved(p, p, p, p, p, None, p)) == _capi.MOGA_ERR_ARG  # no branches
+    assert call(d128, dout=None) == _capi.MOGA_ERR_ARG
+    assert call(d128, w=ws - 1) == _capi.MOGA_ERR_WORKSPACE
