@@ -156,6 +156,41 @@ def test_group_attn_parity(hd, case):
     assert_close_bf16(host(out).reshape(-1, hd), ref, f"group_attn {case} hd={hd}")
 
 
+def test_group_attn_head_beyond_32bit_offsets():
+    """K/V heads of more than 2^31 bytes (over 8.4 M rows at head_dim 128) leave the
+    direct-load kernel's 32-bit buffer offsets and take the register-staged kernel: 65,568
+    segments of 128 keys and 8 queries, compared on every query of sampled segments,
+    including the last ones, whose keys lie beyond byte 2^31 of the head."""
+    _announce("group_attn beyond 32-bit head", hd=128)
+    n_seg, kper, qper, hd = 65568, 128, 8, 128
+    assert n_seg * kper * hd * 2 > (1 << 31)
+    cu_k = _segments(np.full(n_seg, kper))
+    cu_q = _segments(np.full(n_seg, qper))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4242)
+    q = torch.randn((1, n_seg * qper, hd), generator=g, device=DEV, dtype=torch.bfloat16)
+    k = torch.randn((1, n_seg * kper, hd), generator=g, device=DEV, dtype=torch.bfloat16)
+    v = torch.randn((1, n_seg * kper, hd), generator=g, device=DEV, dtype=torch.bfloat16)
+    out = api.moga_group_attn(q, k, v, torch.from_numpy(cu_q).to(DEV),
+                              torch.from_numpy(cu_k).to(DEV))
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(4243))
+    segs = np.unique(np.concatenate([rng.choice(n_seg, 40, replace=False),
+                                     np.arange(n_seg - 8, n_seg)]))
+    # the sampled segments' rows alone, as a smaller varlen problem for the oracle
+    qi = np.concatenate([np.arange(cu_q[s], cu_q[s + 1]) for s in segs])
+    ki = np.concatenate([np.arange(cu_k[s], cu_k[s + 1]) for s in segs])
+    sub_q = host(q[:, torch.from_numpy(qi).to(DEV)])
+    sub_k = host(k[:, torch.from_numpy(ki).to(DEV)])
+    sub_v = host(v[:, torch.from_numpy(ki).to(DEV)])
+    scq = _segments(np.full(segs.size, qper))
+    sck = _segments(np.full(segs.size, kper))
+    ref, _ = oracle.varlen_attn(sub_q, sub_k, sub_v, scq, sck, 1 / math.sqrt(hd),
+                                np.zeros(qi.size, np.int64), np.arange(qi.size))
+    got = host(out[0, torch.from_numpy(qi).to(DEV)])
+    assert_close_bf16(got, ref, "group_attn beyond 32-bit head offsets")
+
+
 def test_group_attn_leaves_rows_outside_segments():
     _announce("group_attn_untouched")
     h, hd = 1, 64
