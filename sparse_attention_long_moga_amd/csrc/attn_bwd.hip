@@ -349,7 +349,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
             if constexpr (!DK) {
                 // S, P of both 32-query blocks; P to the partner wave; dV^T += dO'^T P.  Both
                 // blocks' products are issued before the first exponentials, so block 0's vector
-                // work runs while block 1's products are still in the matrix core.
+                // work runs while block 1's products are still in the matrix core; block 0's dV
+                // products are issued before block 1's exponentials, which then run while those
+                // products are in the matrix core, and only block 1's dV products follow the
+                // hand-off.
                 bf16x8 pf[2][2];
                 f32x16 sacc[2];
 #pragma unroll
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
                         sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, bf[s], s ? sacc[qb] : f32x16{}, 0, 0, 0);
                     }
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
+                for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         float pv[8];
@@ -368,11 +371,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
                         pf[qb][half] = pack8(pv);
                         pbuf[qb][kw][half][lane] = __builtin_bit_cast(uint4, pf[qb][half]);
                     }
+                    if (qb == 0) {
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) accumulate(gt_, half, pf[0][half]);
+                    }
+                }
                 lds_handoff_barrier();  // P of the tile is visible to the dK waves
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) accumulate(gt_, qb * 2 + half, pf[qb][half]);
+                for (int half = 0; half < 2; ++half) accumulate(gt_, 2 + half, pf[1][half]);
             } else {
                 // dP of both blocks; P from the partner wave; dS = P (dP - D); dK^T += Q^T dS
                 f32x16 pacc[2];
