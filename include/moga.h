@@ -256,8 +256,10 @@ typedef struct {
 size_t moga_backward_workspace_bytes(const moga_dims *dims);
 
 /* The backward above.  in: the forward's x, x_dtype, w, q, k, v (pin is not read: the
- * saved group_id already holds it).  d_out: bf16 [H][N][head_dim], token order.  Needs
- * head_dim 128.  dq, dk, dv, dx, dw, dp are fully overwritten.  dQ and dK/dV are computed by
+ * saved group_id already holds it).  d_out: bf16 [H][N][head_dim], token order.  head_dim 64
+ * or 128 (the attention backward kernels work on 128-channel rows: head_dim 64 rows are copied
+ * into them with the upper half zero, which adds nothing to any score or product, and the
+ * results copied back).  dq, dk, dv, dx, dw, dp are fully overwritten.  dQ and dK/dV are computed by
  * two kernels so that every output row has one writer (no atomics), and all sums run in a
  * fixed order.  ws: moga_backward_workspace_bytes(dims). */
 moga_status moga_backward(const moga_inputs *in, const moga_saved *saved, const void *d_out,
@@ -275,7 +277,8 @@ moga_status moga_backward(const moga_inputs *in, const moga_saved *saved, const 
  * The three branches' dQ, dK, dV are added per token in fp32 and rounded to bf16 once.
  * saved: as moga_forward wrote it with this stga layout, with out = o_branches
  * ([3][H][N][head_dim]) and lse = the [3][H][N] normalisers; the other fields as for
- * moga_backward.  Needs head_dim 128.  ws: moga_hybrid_backward_workspace_bytes. */
+ * moga_backward.  head_dim 64 or 128, as for moga_backward.
+ * ws: moga_hybrid_backward_workspace_bytes. */
 size_t moga_hybrid_backward_workspace_bytes(const moga_dims *dims, const stga_layout *stga);
 moga_status moga_hybrid_backward(const moga_inputs *in, const moga_saved *saved,
                                  const stga_layout *stga, const void *d_out, double d_loss,

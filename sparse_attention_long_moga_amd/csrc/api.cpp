@@ -211,7 +211,8 @@ BwdLayout make_bwd_layout(const moga_dims *d, const StgaGeom *g = nullptr) {
     const int64_t n = d->n_tokens;
     const int64_t nk = g ? n + stga_extra_rows(*g) : n;  // key rows of the widest launch
     const size_t rows = sizeof(float) * d->n_heads * n;
-    const size_t row_bytes = (size_t)d->n_heads * d->head_dim * sizeof(uint16_t);
+    // the backward kernels work on 128-channel rows (head_dim 64 is widened with zeros)
+    const size_t row_bytes = (size_t)d->n_heads * 128 * sizeof(uint16_t);
     const size_t tensor = row_bytes * n, ktensor = row_bytes * nk;
     B.D = c.take(rows);
     B.dp = c.take(sizeof(float) * n);
@@ -405,8 +406,6 @@ moga_status check_bwd_args(const moga_inputs *in, const moga_saved *saved, const
                            double d_loss, const moga_dims *dims, const moga_grads *grads) {
     moga_status st = check_dims(dims);
     if (st != MOGA_OK) return st;
-    if (dims->head_dim != 128)
-        return fail(MOGA_ERR_UNSUPPORTED, "backward needs head_dim 128, got %d", dims->head_dim);
     if (!in || !saved || !grads) return fail(MOGA_ERR_ARG, "inputs, saved or grads is NULL");
     if ((st = check_route_args(in->x, in->x_dtype, in->w, dims)) != MOGA_OK) return st;
     if (!in->q || !in->k || !in->v || !d_out) return fail(MOGA_ERR_ARG, "q, k, v or d_out is NULL");
@@ -432,27 +431,35 @@ moga_status run_moga_bwd(const moga_inputs *in, const moga_saved *saved, const v
                          const BwdLayout &B, hipStream_t s) {
     moga_status st;
     const int64_t n = dims->n_tokens;
-    const int nh = dims->n_heads, m = dims->n_groups;
+    const int nh = dims->n_heads, m = dims->n_groups, hd = dims->head_dim;
     const int32_t *perm = saved->perm;
 
     // D = <G, out> per (head, token) row; dp = dp_scale * sum over heads of D / p
     float *D = at<float>(ws, B.D);
     float *dp = grads->dp ? grads->dp : at<float>(ws, B.dp);
     HIP_TRY(launch_bwd_rowdot(static_cast<const bf16 *>(d_out), static_cast<const bf16 *>(out_m),
-                              (int64_t)nh * n, D, s),
+                              (int64_t)nh * n, hd, D, s),
             "row dot launch");
     HIP_TRY(launch_bwd_dp(D, saved->p_sel, n, nh, dp_scale, dp, s), "dp launch");
-    // group order: Q, K, V; dO' = p * G; D; lse in base 2
+    // group order: Q, K, V; dO' = p * G; D; lse in base 2 (head_dim 64: rows widened to 128)
     void *qp = at<char>(ws, B.qp), *kp = at<char>(ws, B.kp), *vp = at<char>(ws, B.vp);
     void *dov = at<char>(ws, B.dov);
-    const void *src[3] = {in->q, in->k, in->v};
-    void *dst[3] = {qp, kp, vp};
-    if ((st = run_gather(0, perm, dims, src, dst, 3, nullptr, nullptr, s)) != MOGA_OK) return st;
-    {
+    if (hd == 128) {
+        const void *src[3] = {in->q, in->k, in->v};
+        void *dst[3] = {qp, kp, vp};
+        if ((st = run_gather(0, perm, dims, src, dst, 3, nullptr, nullptr, s)) != MOGA_OK) return st;
         GatherLaunch g{};
         g.src[0] = d_out; g.dst[0] = dov; g.n_tensors = 1; g.perm = perm; g.n = n;
-        g.n_heads = nh; g.head_dim = dims->head_dim; g.inverse = 0; g.src_scale = saved->p_sel;
+        g.n_heads = nh; g.head_dim = hd; g.inverse = 0; g.src_scale = saved->p_sel;
         HIP_TRY(launch_gather(g, s), "scaled gather launch");
+    } else {
+        const void *src[4] = {in->q, in->k, in->v, d_out};
+        void *dst[4] = {qp, kp, vp, dov};
+        for (int i = 0; i < 4; ++i)
+            HIP_TRY(launch_pad_rows(static_cast<const bf16 *>(src[i]), n, perm,
+                                    i == 3 ? saved->p_sel : nullptr, n, nh,
+                                    static_cast<bf16 *>(dst[i]), s),
+                    "widening gather launch");
     }
     float *Dp = at<float>(ws, B.Dp), *lse2p = at<float>(ws, B.lse2p);
     HIP_TRY(launch_bwd_gather_f32(D, perm, n, nh, 1.0f, 0, Dp, s), "D gather launch");
@@ -477,8 +484,15 @@ moga_status run_moga_bwd(const moga_inputs *in, const moga_saved *saved, const v
     {
         const void *gsrc[3] = {dqp, dkp, dvp};
         void *gdst[3] = {grads->dq, grads->dk, grads->dv};
-        if ((st = run_gather(1, perm, dims, gsrc, gdst, 3, nullptr, nullptr, s)) != MOGA_OK)
-            return st;
+        if (hd == 128) {
+            if ((st = run_gather(1, perm, dims, gsrc, gdst, 3, nullptr, nullptr, s)) != MOGA_OK)
+                return st;
+        } else {
+            for (int i = 0; i < 3; ++i)
+                HIP_TRY(launch_unpad_rows(static_cast<const bf16 *>(gsrc[i]), perm, n, n, nh,
+                                          static_cast<bf16 *>(gdst[i]), s),
+                        "narrowing scatter launch");
+        }
     }
     // router: softmax backward, dx, dW
     if (grads->dx || grads->dw) {
@@ -753,7 +767,7 @@ size_t moga_backward_workspace_bytes(const moga_dims *dims) {
 }
 
 size_t moga_hybrid_backward_workspace_bytes(const moga_dims *dims, const stga_layout *stga) {
-    if (check_dims(dims) != MOGA_OK || dims->head_dim != 128) return 0;
+    if (check_dims(dims) != MOGA_OK) return 0;
     StgaGeom g;
     if (check_stga(dims, stga, &g) != MOGA_OK) return 0;
     return make_bwd_layout(dims, &g).total;
@@ -784,8 +798,8 @@ moga_status moga_hybrid_backward(const moga_inputs *in, const moga_saved *saved,
     if ((st = check_device()) != MOGA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t n = dims->n_tokens, nk = n + stga_extra_rows(g);
-    const int nh = dims->n_heads;
-    const size_t plane = (size_t)nh * n * dims->head_dim;  // elements of one branch's rows
+    const int nh = dims->n_heads, hd = dims->head_dim;
+    const size_t plane = (size_t)nh * n * hd;  // elements of one branch's rows
     const bf16 *o_br = static_cast<const bf16 *>(saved->out);
     const float *lse_br = saved->lse;
     const float third = 1.0f / 3.0f;
@@ -810,22 +824,34 @@ moga_status moga_hybrid_backward(const moga_inputs *in, const moga_saved *saved,
     a.scale = scale_of(dims);
     a.max_items = B.plan_items;
     attn_plan_carve(a.plan, at<char>(ws, B.plan), B.plan_seg, B.plan_items, 0);
-    // 3 per-frame branch, in token order in place (segments cu_f), with G; results in the MoGA
-    //   copies' dQ, dK, dV regions
+    // 3 per-frame branch, in token order (segments cu_f), with G: in place at head_dim 128,
+    //   on rows widened to 128 channels in the MoGA copies' Q, K, V, dO' regions at 64; results
+    //   in the MoGA copies' dQ, dK, dV regions
+    bf16 *qt = at<bf16>(ws, B.qp), *kt = at<bf16>(ws, B.kp), *vt = at<bf16>(ws, B.vp);
+    bf16 *dot = at<bf16>(ws, B.dov);
     bf16 *dqf = at<bf16>(ws, B.dqp), *dkf = at<bf16>(ws, B.dkp), *dvf = at<bf16>(ws, B.dvp);
-    HIP_TRY(launch_bwd_rowdot(G, o_br + 2 * plane, (int64_t)nh * n, D, s), "row dot launch");
+    HIP_TRY(launch_bwd_rowdot(G, o_br + 2 * plane, (int64_t)nh * n, hd, D, s), "row dot launch");
     HIP_TRY(launch_bwd_gather_f32(lse_br + 2 * (size_t)nh * n, nullptr, n, nh, log2e, 0, lse2p, s),
             "lse scale launch");
-    a.q = static_cast<const bf16 *>(in->q); a.k = static_cast<const bf16 *>(in->k);
-    a.v = static_cast<const bf16 *>(in->v); a.dov = G; a.lse2 = lse2p; a.D = D;
+    if (hd == 128) {
+        a.q = static_cast<const bf16 *>(in->q); a.k = static_cast<const bf16 *>(in->k);
+        a.v = static_cast<const bf16 *>(in->v); a.dov = G;
+    } else {
+        const void *src[4] = {in->q, in->k, in->v, d_out};
+        bf16 *dst[4] = {qt, kt, vt, dot};
+        for (int i = 0; i < 4; ++i)
+            HIP_TRY(launch_pad_rows(static_cast<const bf16 *>(src[i]), n, nullptr, nullptr, n, nh,
+                                    dst[i], s),
+                    "widening copy launch");
+        a.q = qt; a.k = kt; a.v = vt; a.dov = dot;
+    }
+    a.lse2 = lse2p; a.D = D;
     a.dq = dqf; a.dk = dkf; a.dv = dvf;
     a.cu_q = a.cu_k = sb.cu_f; a.n_seg = g.frames; a.len_q = a.len_k = n;
     HIP_TRY(launch_attention_bwd(a, s), "per-frame attention backward launch");
     // 4 temporal branch: Q, dO, D, lse to query positions, K and V to key positions (own rows
     //   and borrowed frames), the backward over the groups, results in position order
-    bf16 *qt = at<bf16>(ws, B.qp), *kt = at<bf16>(ws, B.kp), *vt = at<bf16>(ws, B.vp);
-    bf16 *dot = at<bf16>(ws, B.dov);
-    {
+    if (hd == 128) {
         GatherLaunch gq{};
         gq.src[0] = in->q; gq.dst[0] = qt; gq.src[1] = d_out; gq.dst[1] = dot; gq.n_tensors = 2;
         gq.perm = sb.q_idx; gq.n = n; gq.n_heads = nh; gq.head_dim = dims->head_dim;
@@ -835,8 +861,17 @@ moga_status moga_hybrid_backward(const moga_inputs *in, const moga_saved *saved,
         gk.perm = sb.kv_idx; gk.n = nk; gk.src_rows = n; gk.n_heads = nh;
         gk.head_dim = dims->head_dim;
         HIP_TRY(launch_gather(gk, s), "temporal key gather launch");
+    } else {
+        HIP_TRY(launch_pad_rows(static_cast<const bf16 *>(in->q), n, sb.q_idx, nullptr, n, nh, qt,
+                                s), "temporal query gather launch");
+        HIP_TRY(launch_pad_rows(G, n, sb.q_idx, nullptr, n, nh, dot, s),
+                "temporal query gather launch");
+        HIP_TRY(launch_pad_rows(static_cast<const bf16 *>(in->k), n, sb.kv_idx, nullptr, nk, nh, kt,
+                                s), "temporal key gather launch");
+        HIP_TRY(launch_pad_rows(static_cast<const bf16 *>(in->v), n, sb.kv_idx, nullptr, nk, nh, vt,
+                                s), "temporal key gather launch");
     }
-    HIP_TRY(launch_bwd_rowdot(G, o_br + plane, (int64_t)nh * n, D, s), "row dot launch");
+    HIP_TRY(launch_bwd_rowdot(G, o_br + plane, (int64_t)nh * n, hd, D, s), "row dot launch");
     HIP_TRY(launch_bwd_gather_f32(D, sb.q_idx, n, nh, 1.0f, 0, Dp, s), "D gather launch");
     HIP_TRY(launch_bwd_gather_f32(lse_br + (size_t)nh * n, sb.q_idx, n, nh, log2e, 0, lse2p, s),
             "lse gather launch");
@@ -848,9 +883,12 @@ moga_status moga_hybrid_backward(const moga_inputs *in, const moga_saved *saved,
     // 5 the mean: grad = (MoGA + per-frame + temporal at the token's positions) / 3
     bf16 *dq = static_cast<bf16 *>(grads->dq), *dk = static_cast<bf16 *>(grads->dk),
          *dv = static_cast<bf16 *>(grads->dv);
-    HIP_TRY(launch_grad_sum(dq, dqf, dqt, n, sb.tpos, 0, 1, n, nh, third, dq, s), "dQ sum launch");
-    HIP_TRY(launch_grad_sum(dk, dkf, dkt, nk, sb.tpos, 1, 3, n, nh, third, dk, s), "dK sum launch");
-    HIP_TRY(launch_grad_sum(dv, dvf, dvt, nk, sb.tpos, 1, 3, n, nh, third, dv, s), "dV sum launch");
+    HIP_TRY(launch_grad_sum(dq, dqf, dqt, hd, 128, n, sb.tpos, 0, 1, n, nh, third, dq, s),
+            "dQ sum launch");
+    HIP_TRY(launch_grad_sum(dk, dkf, dkt, hd, 128, nk, sb.tpos, 1, 3, n, nh, third, dk, s),
+            "dK sum launch");
+    HIP_TRY(launch_grad_sum(dv, dvf, dvt, hd, 128, nk, sb.tpos, 1, 3, n, nh, third, dv, s),
+            "dV sum launch");
     return MOGA_OK;
 }
 

@@ -17,15 +17,17 @@ namespace {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// D[h][t] for hd 128 rows: 16 lanes per row, 16 bytes each, then a sum over the 16 lanes.
+// D[h][t] for rows of HD channels: HD/8 lanes per row, 16 bytes each, then a sum over them.
+template <int HD>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16 *d_out, const bf16 *out,
                                                           int64_t rows, float *D) {
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int ch = threadIdx.x & 15;
+    constexpr int LPR = HD / 8, RPB = 256 / LPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + (threadIdx.x / LPR);
+    const int ch = threadIdx.x % LPR;
     float acc = 0.0f;
     if (row < rows) {
-        const uint4 g = *reinterpret_cast<const uint4 *>(d_out + row * 128 + ch * 8);
-        const uint4 o = *reinterpret_cast<const uint4 *>(out + row * 128 + ch * 8);
+        const uint4 g = *reinterpret_cast<const uint4 *>(d_out + row * HD + ch * 8);
+        const uint4 o = *reinterpret_cast<const uint4 *>(out + row * HD + ch * 8);
         const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, ow[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -34,8 +36,53 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16 *d_out, cons
         }
     }
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off, 64);
+    for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
     if (row < rows && ch == 0) D[row] = acc;
+}
+
+// head_dim-64 rows widened to the 128 channels of the backward kernels, the upper half zero:
+// dst[h][j] = (f * src[h][r], 0) with r = perm[j] (perm NULL: j) and f = row_scale[r] (NULL: 1);
+// a row index outside [0, src_rows) gives a zero row.  One thread per 16 bytes of dst.
+__global__ __launch_bounds__(256) void pad_rows_kernel(const bf16 *src, int64_t src_rows,
+                                                        const int32_t *perm, const float *row_scale,
+                                                        int64_t n, bf16 *dst) {
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t j = gi >> 4;
+    if (j >= n) return;
+    const int ch = (int)(gi & 15);
+    const int h = blockIdx.y;
+    const int64_t r = perm ? (int64_t)perm[j] : j;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (ch < 8 && r >= 0 && r < src_rows) {
+        v = *reinterpret_cast<const uint4 *>(src + ((int64_t)h * src_rows + r) * 64 + ch * 8);
+        if (row_scale) {
+            const float f = row_scale[r];
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bf16x2 b = {(__bf16)(f * bf16_lo(w[i])), (__bf16)(f * bf16_hi(w[i]))};
+                w[i] = __builtin_bit_cast(uint32_t, b);
+            }
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+    *reinterpret_cast<uint4 *>(dst + ((int64_t)h * n + j) * 128 + ch * 8) = v;
+}
+
+// The first 64 channels of 128-channel rows: dst[h][perm[j]] = src[h][j][0:64] (perm NULL: j;
+// entries outside [0, dst_rows) are skipped).  One thread per 16 bytes of dst.
+__global__ __launch_bounds__(256) void unpad_rows_kernel(const bf16 *src, const int32_t *perm,
+                                                          int64_t n, int64_t dst_rows, bf16 *dst) {
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t j = gi >> 3;
+    if (j >= n) return;
+    const int ch = (int)(gi & 7);
+    const int h = blockIdx.y;
+    const int64_t r = perm ? (int64_t)perm[j] : j;
+    if (r < 0 || r >= dst_rows) return;
+    *reinterpret_cast<uint4 *>(dst + ((int64_t)h * dst_rows + r) * 64 + ch * 8) =
+        *reinterpret_cast<const uint4 *>(src + ((int64_t)h * n + j) * 128 + ch * 8);
 }
 
 // dp_t = scale * (sum over heads (in head order) of D[h][t]) / p_t.
@@ -69,20 +116,24 @@ __global__ __launch_bounds__(256) void bwd_gather_f32_kernel(const float *src, c
 // Gradient of a token under the mean of the three branches (hybrid backward): the two
 // token-order gradients a and b and the position-order rows c of the token (its query position
 // for dQ; for dK and dV every key position that holds it, i.e. its own group's and those of
-// the groups that borrow its frame), summed in fp32 in that order and scaled by w.  One thread
-// per 8 channels of a head_dim-128 row; every row of out has exactly this one writer.
+// the groups that borrow its frame), summed in fp32 in that order and scaled by w.  a and out
+// have rows of HD channels, b and c rows of bc_hd >= HD channels (the 128-channel rows of the
+// backward kernels), of which the first HD are summed.  One thread per 8 channels; every row of
+// out has exactly this one writer.
+template <int HD>
 __global__ __launch_bounds__(256) void grad_sum_kernel(const bf16 *a, const bf16 *b, const bf16 *c,
-                                                        int64_t c_rows, const int32_t *pos,
-                                                        int first, int npos, int64_t n, float w,
-                                                        bf16 *out) {
-    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16-byte chunk of row h*n + t
-    const int64_t row = gi >> 4;
+                                                        int bc_hd, int64_t c_rows,
+                                                        const int32_t *pos, int first, int npos,
+                                                        int64_t n, float w, bf16 *out) {
+    constexpr int CPR = HD / 8;  // 16-byte chunks per row of a and out
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;  // chunk of row h*n + t
+    const int64_t row = gi / CPR;
     const int h = blockIdx.y;
     if (row >= n) return;
-    const int ch = (int)(gi & 15);
-    const int64_t off = ((int64_t)h * n + row) * 128 + ch * 8;
+    const int ch = (int)(gi % CPR);
+    const int64_t off = ((int64_t)h * n + row) * HD + ch * 8;
     const uint4 ua = *reinterpret_cast<const uint4 *>(a + off);
-    const uint4 ub = *reinterpret_cast<const uint4 *>(b + off);
+    const uint4 ub = *reinterpret_cast<const uint4 *>(b + ((int64_t)h * n + row) * bc_hd + ch * 8);
     const uint32_t aw[4] = {ua.x, ua.y, ua.z, ua.w}, bw[4] = {ub.x, ub.y, ub.z, ub.w};
     float acc[8];
 #pragma unroll
@@ -93,7 +144,7 @@ __global__ __launch_bounds__(256) void grad_sum_kernel(const bf16 *a, const bf16
     for (int k = 0; k < npos; ++k) {
         const int32_t p = pos[4 * row + first + k];
         if (p < 0 || p >= c_rows) continue;
-        const uint4 uc = *reinterpret_cast<const uint4 *>(c + ((int64_t)h * c_rows + p) * 128 + ch * 8);
+        const uint4 uc = *reinterpret_cast<const uint4 *>(c + ((int64_t)h * c_rows + p) * bc_hd + ch * 8);
         const uint32_t cw[4] = {uc.x, uc.y, uc.z, uc.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -340,10 +391,29 @@ hipError_t launch_router_bwd_x(const BwdRouterLaunch &a, hipStream_t s) {
 
 int64_t bwd_dw_chunks(int64_t n) { return (n + kDwChunk - 1) / kDwChunk; }
 
-hipError_t launch_bwd_rowdot(const bf16 *d_out, const bf16 *out, int64_t rows, float *D,
+hipError_t launch_bwd_rowdot(const bf16 *d_out, const bf16 *out, int64_t rows, int hd, float *D,
                              hipStream_t s) {
-    hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, d_out,
-                       out, rows, D);
+    if (hd == 64)
+        hipLaunchKernelGGL(bwd_rowdot_kernel<64>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0,
+                           s, d_out, out, rows, D);
+    else
+        hipLaunchKernelGGL(bwd_rowdot_kernel<128>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                           s, d_out, out, rows, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_pad_rows(const bf16 *src, int64_t src_rows, const int32_t *perm,
+                           const float *row_scale, int64_t n, int n_heads, bf16 *dst,
+                           hipStream_t s) {
+    hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((n * 16 + 255) / 256), (unsigned)n_heads),
+                       dim3(256), 0, s, src, src_rows, perm, row_scale, n, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpad_rows(const bf16 *src, const int32_t *perm, int64_t n, int64_t dst_rows,
+                             int n_heads, bf16 *dst, hipStream_t s) {
+    hipLaunchKernelGGL(unpad_rows_kernel, dim3((unsigned)((n * 8 + 255) / 256), (unsigned)n_heads),
+                       dim3(256), 0, s, src, perm, n, dst_rows, dst);
     return hipGetLastError();
 }
 
@@ -361,12 +431,17 @@ hipError_t launch_bwd_gather_f32(const float *src, const int32_t *perm, int64_t 
     return hipGetLastError();
 }
 
-hipError_t launch_grad_sum(const bf16 *a, const bf16 *b, const bf16 *c, int64_t c_rows,
-                           const int32_t *pos, int first, int npos, int64_t n, int n_heads,
-                           float w, bf16 *out, hipStream_t s) {
-    const int64_t chunks = n * 16;
-    hipLaunchKernelGGL(grad_sum_kernel, dim3((unsigned)((chunks + 255) / 256), (unsigned)n_heads),
-                       dim3(256), 0, s, a, b, c, c_rows, pos, first, npos, n, w, out);
+hipError_t launch_grad_sum(const bf16 *a, const bf16 *b, const bf16 *c, int hd, int bc_hd,
+                           int64_t c_rows, const int32_t *pos, int first, int npos, int64_t n,
+                           int n_heads, float w, bf16 *out, hipStream_t s) {
+    const int64_t chunks = n * (hd / 8);
+    const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)n_heads);
+    if (hd == 64)
+        hipLaunchKernelGGL(grad_sum_kernel<64>, grid, dim3(256), 0, s, a, b, c, bc_hd, c_rows, pos,
+                           first, npos, n, w, out);
+    else
+        hipLaunchKernelGGL(grad_sum_kernel<128>, grid, dim3(256), 0, s, a, b, c, bc_hd, c_rows, pos,
+                           first, npos, n, w, out);
     return hipGetLastError();
 }
 

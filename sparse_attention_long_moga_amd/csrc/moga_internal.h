@@ -196,7 +196,7 @@ struct BwdRouterLaunch {
     float *dw_part;          // [bwd_dw_chunks(n)][d][m]
 };
 int64_t bwd_dw_chunks(int64_t n);
-hipError_t launch_bwd_rowdot(const bf16 *d_out, const bf16 *out, int64_t rows, float *D,
+hipError_t launch_bwd_rowdot(const bf16 *d_out, const bf16 *out, int64_t rows, int hd, float *D,
                              hipStream_t s);
 hipError_t launch_bwd_dp(const float *D, const float *p_sel, int64_t n, int n_heads, float scale, float *dp,
                          hipStream_t s);
@@ -220,11 +220,20 @@ struct StgaBuffers {
                          // own, then as borrowed by the next and the previous shot, -1 if none)
 };
 // out[h][t] = w * (a[h][t] + b[h][t] + sum of c[h][p] over the positions p in pos[4t + first ..
-// 4t + first + npos) that are >= 0), in fp32, rounded to bf16 once (head_dim 128; a, b and out
-// token order, out may be a; c with c_rows rows per head)
-hipError_t launch_grad_sum(const bf16 *a, const bf16 *b, const bf16 *c, int64_t c_rows,
-                           const int32_t *pos, int first, int npos, int64_t n, int n_heads,
-                           float w, bf16 *out, hipStream_t s);
+// 4t + first + npos) that are >= 0), in fp32, rounded to bf16 once (a, b and out token order,
+// out may be a; a and out rows of hd channels, b and c rows of bc_hd >= hd, of which the first
+// hd are used; c with c_rows rows per head)
+hipError_t launch_grad_sum(const bf16 *a, const bf16 *b, const bf16 *c, int hd, int bc_hd,
+                           int64_t c_rows, const int32_t *pos, int first, int npos, int64_t n,
+                           int n_heads, float w, bf16 *out, hipStream_t s);
+// head_dim-64 rows widened to 128 channels (upper half zero): dst[h][j] = f * src[h][r], r =
+// perm[j] (perm NULL: j), f = row_scale[r] (NULL: 1); r outside [0, src_rows) gives a zero row
+hipError_t launch_pad_rows(const bf16 *src, int64_t src_rows, const int32_t *perm,
+                           const float *row_scale, int64_t n, int n_heads, bf16 *dst,
+                           hipStream_t s);
+// back to 64 channels: dst[h][perm[j]] = src[h][j][0:64] (perm NULL: j; src rows of 128)
+hipError_t launch_unpad_rows(const bf16 *src, const int32_t *perm, int64_t n, int64_t dst_rows,
+                             int n_heads, bf16 *dst, hipStream_t s);
 int32_t stga_n_groups(const StgaGeom &g);
 int64_t stga_extra_rows(const StgaGeom &g);
 hipError_t launch_stga_index(const StgaGeom &g, const StgaBuffers &b, hipStream_t s);

@@ -47,8 +47,8 @@ def assert_grad_close(got, ref, what, rrms=GRAD_RMS, rmax=GRAD_MAX):
     assert err <= rmax * scale, f"{what}: max error {err:.3e} > {rmax} x RMS {scale:.3e}"
 
 
-def _case(n, h, m, seed, d=256, x_dtype="bf16"):
-    wl = workloads.small(f"bwd_{n}_{m}", n, d, h, 128, m, seed=seed, x_dtype=x_dtype)
+def _case(n, h, m, seed, d=256, x_dtype="bf16", hd=128):
+    wl = workloads.small(f"bwd_{n}_{m}", n, d, h, hd, m, seed=seed, x_dtype=x_dtype)
     x, w = workloads.make_x(wl, DEV), workloads.make_w(wl, DEV)
     q, k, v = workloads.make_qkv(wl, DEV)
     dout = workloads.make_dout(wl, DEV)
@@ -74,14 +74,16 @@ def _check_all(wl, x, w, q, k, v, dout, d_loss, fwd, grads, group_id, what):
     return ref
 
 
-@pytest.mark.parametrize("n, h, m, seed, x_dtype", [
-    (1000, 2, 5, 51, "bf16"),    # ragged groups (none a multiple of 128)
-    (2600, 2, 3, 52, "f32"),     # several 128-row tiles per group, fp32 router input
-    (777, 3, 8, 53, "bf16"),
+@pytest.mark.parametrize("n, h, m, seed, x_dtype, hd", [
+    (1000, 2, 5, 51, "bf16", 128),    # ragged groups (none a multiple of 128)
+    (2600, 2, 3, 52, "f32", 128),     # several 128-row tiles per group, fp32 router input
+    (777, 3, 8, 53, "bf16", 128),
+    (1300, 2, 4, 58, "f32", 64),      # head_dim 64 (rows widened to the 128-channel kernels)
+    (333, 1, 3, 59, "bf16", 64),
 ])
-def test_backward_parity(n, h, m, seed, x_dtype):
-    _announce("backward", n=n, h=h, m=m, x_dtype=x_dtype)
-    wl, x, w, q, k, v, dout = _case(n, h, m, seed, x_dtype=x_dtype)
+def test_backward_parity(n, h, m, seed, x_dtype, hd):
+    _announce("backward", n=n, h=h, m=m, x_dtype=x_dtype, hd=hd)
+    wl, x, w, q, k, v, dout = _case(n, h, m, seed, x_dtype=x_dtype, hd=hd)
     r = oracle.route(host(x), host(w))
     pin = torch.from_numpy(oracle.near_tie_pins(r)).to(DEV)
     fwd, grads = _forward_backward(wl, x, w, q, k, v, dout, 1.3, pin=pin)

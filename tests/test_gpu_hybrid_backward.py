@@ -38,6 +38,9 @@ GEOMS = {
     # one shot, nothing borrowed; temporal groups of a whole frame window
     "one_shot": dict(frames=6, height=8, width=8, shot_start=[0, 6], win_h=8, win_w=8,
                      t_group=4, aug_frames=0, heads=1, m=3, seed=63),
+    # head_dim 64 (rows widened to the 128-channel kernels), three shots
+    "hd64": dict(frames=9, height=6, width=8, shot_start=[0, 4, 7, 9], win_h=3, win_w=4,
+                 t_group=2, aug_frames=2, heads=2, m=4, seed=64, hd=64),
 }
 
 
@@ -47,9 +50,9 @@ def _announce(what, **kw):
 
 def _setup(geom):
     c = dict(geom)
-    h, m, seed = c.pop("heads"), c.pop("m"), c.pop("seed")
+    h, m, seed, hd = c.pop("heads"), c.pop("m"), c.pop("seed"), c.pop("hd", 128)
     n = c["frames"] * c["height"] * c["width"]
-    wl = workloads.small(f"hyb_{n}_{m}", n, 256, h, 128, m, seed=seed)
+    wl = workloads.small(f"hyb_{n}_{m}", n, 256, h, hd, m, seed=seed)
     x, w = workloads.make_x(wl, DEV), workloads.make_w(wl, DEV)
     q, k, v = workloads.make_qkv(wl, DEV)
     dout = workloads.make_dout(wl, DEV)
@@ -68,6 +71,8 @@ def test_hybrid_backward_parity(name):
     d_loss = 0.7
     fwd = api.moga_forward(x, w, q, k, v, m, alpha=wl.alpha, pin=pin, stga=lay, fused=True,
                            with_lse=True)
+    explicit = api.moga_forward(x, w, q, k, v, m, alpha=wl.alpha, pin=pin, stga=lay,
+                                with_lse=True)
     plain = api.moga_forward(x, w, q, k, v, m, alpha=wl.alpha, pin=pin, stga=lay)
     grads = api.moga_hybrid_backward(x, w, q, k, v, fwd, dout, lay, d_loss=d_loss,
                                      alpha=wl.alpha)
@@ -75,8 +80,11 @@ def test_hybrid_backward_parity(name):
                                      alpha=wl.alpha)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(fwd["group_id"]), r["group_id"])
-    # saving the branches does not change out, and the backward is reproducible
+    # saving the branches does not change out, both forward variants save the same state, and
+    # the backward is reproducible
     assert torch.equal(fwd["out"], plain["out"])
+    for key in ("out", "o_branches", "lse"):
+        assert torch.equal(fwd[key], explicit[key]), key
     for key in grads:
         assert torch.equal(grads[key], again[key]), key
 
