@@ -870,10 +870,11 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t s) {
     if (a.x_is_bf16) {
         const size_t lds_img = (size_t)(3 * a.m + 1) * route_stage_row_bytes(a.d);
         if (a.m <= 16 && lds_img <= (size_t)kRouteLdsW) return launch_stage<8, 1, 512>(a, lds_img, s);
-        // eight 16-token tiles per item: each W fragment loaded from L2 serves 128 tokens
-        // (four tiles: 60 s router 1.64 ms, eight: 1.47 ms)
+        // many 16-token tiles per item, so that each W fragment loaded from L2 serves as many
+        // tokens as the registers allow (60 s router: four tiles 1.64 ms, eight 1.47 ms, ten
+        // 1.44 ms; twelve spill)
         if (a.m <= 16) return launch_mfma<1, 8, 1>(a, s);
-        if (a.m <= 32) return launch_mfma<2, 8, 1>(a, s);
+        if (a.m <= 32) return launch_mfma<2, 10, 1>(a, s);
         if (a.m <= 48) return launch_mfma<3, 2, 1>(a, s);
         return launch_mfma<4, 2, 1>(a, s);
     }
