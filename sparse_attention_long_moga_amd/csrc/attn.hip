@@ -690,9 +690,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         for (int ti = 0; ti < NT; ++ti) o[ti] = f32x16{};
 
         uint4 pf_u[4];  // the tile's probabilities, bf16, in the B-operand layout
-        auto tile = [&](auto bufc, auto maskc, int t) {
+        // MODE 0: a whole tile; 1: the last, partial tile (masked); 2: a last tile of at most 32
+        // keys, whose second 32-key sub-block is all masked: its products and exponentials are
+        // skipped (they would add exact zeros)
+        auto tile = [&](auto bufc, auto modec, int t) {
             constexpr int buf = decltype(bufc)::value;
-            constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
+            constexpr int MODE = decltype(modec)::value;
+            constexpr bool MASK = MODE >= 1, HALF = MODE == 2;
             if (t + 1 < ntiles) {
                 issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
                 load_rows(t + 2);
@@ -706,6 +710,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
                 sacc[sb] = f32x16{};
+                if (HALF && sb == 1) continue;
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                     const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kt + sb * 32 * ROWB + koff[s]);
@@ -717,15 +722,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                 // constant part against one per-lane limit (no per-lane key table to keep)
                 const int lim = klen - t * KT - 4 * hh;
 #pragma unroll
-                for (int sb = 0; sb < 2; ++sb)
+                for (int sb = 0; sb < (HALF ? 1 : 2); ++sb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
                         if (sb * 32 + 8 * (v >> 2) + (v & 3) >= lim) sacc[sb][v] = -INFINITY;
             }
             // this lane's largest score of each sub-block (16 keys each)
-            float pm[2];
+            float pm[2] = {-INFINITY, -INFINITY};
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
+            for (int sb = 0; sb < (HALF ? 1 : 2); ++sb) {
                 const f32x16 &sv = sacc[sb];
                 float m0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
                 m0 = fmaxf(fmaxf(m0, sv[3]), sv[4]);
@@ -765,16 +770,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
             // by one of sub-block 1's reads, then sub-block 1's products each followed by vector
             // work (sub-block 0's probabilities), so the products never wait on a read just issued
             // and the exponentials run while the matrix core is busy
-            __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);  // LDS reads
+            if constexpr (!HALF) {
+                __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);  // LDS reads
 #pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-            }
+                for (int i = 0; i < NS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                }
 #pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+                for (int i = 0; i < NS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+                }
             }
             if (__ballot(up_lane)) {
                 float tmax = max_across_halves(fmaxf(pm[0], pm[1]));
@@ -790,17 +797,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
                 mc = m_run * c;
                 probs(0, mc);
             }
-            probs(1, mc);
+            if constexpr (HALF) {
+                pf_u[2] = make_uint4(0u, 0u, 0u, 0u);
+                pf_u[3] = make_uint4(0u, 0u, 0u, 0u);
+            } else {
+                probs(1, mc);
+            }
             // the row sum adds the bf16 probabilities the MFMA multiplies V with, two per dot2
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
+            for (int ch = 0; ch < (HALF ? 2 : 4); ++ch) {
                 l_run = sum_bf16x2(pf_u[ch].x, l_run);
                 l_run = sum_bf16x2(pf_u[ch].y, l_run);
                 l_run = sum_bf16x2(pf_u[ch].z, l_run);
                 l_run = sum_bf16x2(pf_u[ch].w, l_run);
             }
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
+            for (int ch = 0; ch < (HALF ? 2 : 4); ++ch) {
                 const bf16x8 pfc = __builtin_bit_cast(bf16x8, pf_u[ch]);
 #pragma unroll
                 for (int ti = 0; ti < NT; ++ti) {
@@ -825,8 +837,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         const int nfull = klen / KT;
         using B0 = std::integral_constant<int, 0>;
         using B1 = std::integral_constant<int, 1>;
-        using NoMask = std::integral_constant<bool, false>;
-        using Mask = std::integral_constant<bool, true>;
+        using NoMask = std::integral_constant<int, 0>;
+        using Mask = std::integral_constant<int, 1>;
+        using Half = std::integral_constant<int, 2>;
         // the next item's index to every wave, and its descriptor requested into the other slot
         int next = total;
         auto handoff = [&]() {
@@ -851,8 +864,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
             ++t;
         }
         if (t < ntiles) {
-            if (t & 1) tile(B1{}, Mask{}, t);
-            else tile(B0{}, Mask{}, t);
+            // short-segment (4-wave) items end on a tile of at most 32 keys often enough for the
+            // half tile to pay; the long MoGA items keep their code as it was
+            if constexpr (WAVES == 4) {
+                const bool half = klen - t * KT <= 32;
+                if (t & 1) {
+                    if (half) tile(B1{}, Half{}, t);
+                    else tile(B1{}, Mask{}, t);
+                } else {
+                    if (half) tile(B0{}, Half{}, t);
+                    else tile(B0{}, Mask{}, t);
+                }
+            } else {
+                if (t & 1) tile(B1{}, Mask{}, t);
+                else tile(B0{}, Mask{}, t);
+            }
         }
         if (!handed) {
             handoff();
