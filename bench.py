@@ -35,7 +35,7 @@ METRIC = "MoGA fwd tokens/s + group-attn TFLOP/s (% bf16 MFMA peak) at N=282k, M
 # reports null until the counters are taken again.
 STAGE_REPS = 20  # timed calls per short stage and pass in the stage breakdown
 FLUSH_BYTES = 512 << 20  # scratch read before every timed stage call
-ATTN_TRAFFIC = {"bytes": 10_717_284 * 1024 * 2 + 850_790 * 1024, "attn_hip_sha256_16": "83eb4a6f0a7da998"}
+ATTN_TRAFFIC = {"bytes": 10_717_284 * 1024 * 2 + 850_790 * 1024, "attn_hip_sha256_16": "29b5f1f97824537d"}
 
 
 def attn_traffic_bytes():

@@ -854,6 +854,36 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void attn_kernel_direct(Attn
         // free of it and hand off at the end.
         constexpr bool EARLY = WAVES == 4;
         const bool handed = EARLY && nfull >= 4;
+        // A wave of a 4-wave item without any query row (the last item of a short segment)
+        // computes nothing: it only issues its share of each tile's loads and meets the same
+        // barriers in the same order, so the other block's waves on its SIMD run alone.
+        bool idle = false;
+        if constexpr (WAVES == 4 && !SPLIT) idle = uniform(qb + qt * BQ + wave * 32) >= qe;
+        if (idle) {
+            auto idle_tile = [&](auto bufc, int tt) {
+                constexpr int buf = decltype(bufc)::value;
+                if (tt + 1 < ntiles) {
+                    issue(std::integral_constant<int, buf ^ 1>{}, tt + 1);
+                    load_rows(tt + 2);
+                }
+                __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+                __syncthreads();
+            };
+            for (; t + 1 < nfull; t += 2) {
+                if (EARLY && t == 2) handoff();
+                idle_tile(B0{}, t);
+                idle_tile(B1{}, t + 1);
+            }
+            if (t < nfull) {
+                idle_tile(B0{}, t);
+                ++t;
+            }
+            if (t < ntiles) {
+                if (t & 1) idle_tile(B1{}, t);
+                else idle_tile(B0{}, t);
+            }
+            t = ntiles;
+        }
         for (; t + 1 < nfull; t += 2) {
             if (EARLY && t == 2) handoff();
             tile(B0{}, NoMask{}, t);
