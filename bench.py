@@ -166,6 +166,8 @@ def main():
 
     if not args.no_stages:
         result.update(stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops))
+        if lay:
+            result.update(hybrid_overhead(args, wl, x, w, q, k, v, lay, ws, out, step))
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, w, q, k, v, args.cpu_seconds)
@@ -257,8 +259,39 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
                  t_group=wl.t_group, aug_frames=wl.aug_frames)
         pt = stga_pairs_closed_form(g)
         stages["stga_tflops"] = metrics.attention_flops(pt, h, hd) / (ms["stga"] / 1e3) / 1e12
+        stages["stga_frac_of_bf16_peak"] = stages["stga_tflops"] / MFMA_BF16_PEAK_TFLOPS
     log(f"stages (ms): {ms}  attn {attn_tflops:.1f} TFLOP/s")
     return stages
+
+
+def hybrid_overhead(args, wl, x, w, q, k, v, lay, ws, out, step):
+    """What the two STGA branches add to the forward: each pass times the hybrid forward and
+    the same forward without them (its MoGA epilogue then stores its rows without the mean),
+    back to back, each enqueued whole by one library call; the median difference is the
+    branches' launches plus the mean's extra reads in the MoGA epilogue.  (The stage
+    breakdown times the branches alone, after the flush and an idle gap, where these
+    few-millisecond launches start at a lower engine clock than inside a forward.)"""
+    import numpy as np
+    import torch
+
+    from sparse_attention_long_moga_amd import api
+
+    stream = torch.cuda.current_stream()
+    evs = []
+    for it in range(args.steps + 1):
+        ea, eb, ec = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        ea.record(stream)
+        step()
+        eb.record(stream)
+        api.moga_forward(x, w, q, k, v, wl.n_groups, alpha=wl.alpha, ws=ws, out=out)
+        ec.record(stream)
+        if it > 0:  # the first pair warms the plain forward's allocations
+            evs.append((ea, eb, ec))
+    torch.cuda.synchronize()
+    d = [ea.elapsed_time(eb) - eb.elapsed_time(ec) for ea, eb, ec in evs]
+    ms = float(np.median(d))
+    log(f"hybrid forward over the MoGA-only forward: {ms:.3f} ms")
+    return {"hybrid_over_moga_forward_ms": ms}
 
 
 # The pages' group-count ablation for Wan2.1-1.3B at 10 s (papernotes.org MoGA note,
