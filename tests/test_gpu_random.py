@@ -1,0 +1,134 @@
+"""Seeded sweep of small random configurations of the whole forward (explicit and fused) and of
+the backward, through the C ABI, against the oracle: group counts from 1 to 9, router widths,
+head counts and head sizes, bf16 and fp32 router inputs, forced groups for a random subset of
+tokens, and (for the hybrid forward) random frame grids, windows, shot cuts, temporal group
+sizes and borrowed-frame counts.  Every configuration is drawn from a fixed seed, so a failure
+names a reproducible case."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from sparse_attention_long_moga_amd import api
+from tests.helpers import assert_close_bf16, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+# (height, width, win_h, win_w): windows that tile the frame, from one window per frame down to
+# single-row windows
+GRIDS = [(4, 6, 2, 3), (6, 8, 3, 4), (8, 12, 4, 6), (5, 10, 5, 5), (3, 16, 3, 8), (10, 16, 5, 8),
+         (4, 4, 1, 4), (7, 9, 7, 3)]
+
+
+def _config(seed: int) -> dict:
+    rng = np.random.default_rng(1000 + seed)
+    h_, w_, wh, ww = GRIDS[rng.integers(len(GRIDS))]
+    frames = int(rng.integers(2, 15))
+    n_shots = int(rng.integers(1, min(frames, 5) + 1))
+    cuts = sorted(rng.choice(np.arange(1, frames), size=n_shots - 1, replace=False).tolist())
+    f32 = bool(rng.integers(2))
+    return dict(
+        seed=seed, frames=frames, height=h_, width=w_, win_h=wh, win_w=ww,
+        shot_start=[0] + cuts + [frames], t_group=int(rng.integers(1, 5)),
+        aug_frames=int(rng.integers(0, 4)), m=int(rng.integers(1, 10)),
+        d=int(rng.choice([32, 64, 128, 200] if not f32 else [36, 64, 100])),
+        heads=int(rng.integers(1, 4)), hd=int(rng.choice([64, 128])),
+        hybrid=bool(rng.integers(2)), fused=bool(rng.integers(2)), f32=f32,
+        pin_frac=float(rng.choice([0.0, 0.05, 0.5])))
+
+
+def _inputs(c):
+    n = c["frames"] * c["height"] * c["width"]
+    wl = workloads.small(f"rand_{c['seed']}", n, c["d"], c["heads"], c["hd"], c["m"],
+                         seed=500 + c["seed"], x_dtype="f32" if c["f32"] else "bf16",
+                         mixture="normal" if c["f32"] else "gaussian")
+    x, w = workloads.make_x(wl, DEV), workloads.make_w(wl, DEV)
+    q, k, v = workloads.make_qkv(wl, DEV)
+    grid = {kk: c[kk] for kk in ("frames", "height", "width", "shot_start", "win_h", "win_w",
+                                 "t_group", "aug_frames")}
+    # forced groups for a random subset of tokens, plus the oracle's choice on near ties
+    rng = np.random.default_rng(2000 + c["seed"])
+    r0 = oracle.route(host(x), host(w))
+    pin = oracle.near_tie_pins(r0)
+    forced = rng.random(n) < c["pin_frac"]
+    pin[forced] = rng.integers(0, c["m"], size=int(forced.sum()))
+    return wl, x, w, q, k, v, grid, pin
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_forward(seed):
+    c = _config(seed)
+    print(f"[case] random forward {c}", flush=True)
+    wl, x, w, q, k, v, grid, pin = _inputs(c)
+    n, m, hd, h = wl.n_tokens, c["m"], c["hd"], c["heads"]
+    lay = api.make_stga_layout(**grid) if c["hybrid"] else None
+    got = api.moga_forward(x, w, q, k, v, m, alpha=0.1, pin=torch.from_numpy(pin).to(DEV),
+                           stga=lay, fused=c["fused"])
+    torch.cuda.synchronize()
+    ref_r = oracle.route(host(x), host(w), pin=pin)
+    np.testing.assert_array_equal(host(got["group_id"]), ref_r["group_id"])
+    np.testing.assert_array_equal(host(got["counts"]), ref_r["counts"])
+    np.testing.assert_allclose(host(got["p_sel"]), ref_r["p_sel"], rtol=0, atol=2e-6)
+    np.testing.assert_allclose(host(got["prob_sum"]) / n, ref_r["prob_sum"] / n, rtol=0,
+                               atol=1e-6)
+    cu_ref, perm_ref = oracle.groups(ref_r["group_id"], m)
+    np.testing.assert_array_equal(host(got["cu_seqlens"]), cu_ref)
+    np.testing.assert_array_equal(host(got["perm"]), perm_ref)
+    loss_ref, _, _ = oracle.balance_loss(ref_r["counts"], ref_r["prob_sum"], n, 0.1)
+    assert abs(float(got["loss"].item()) - loss_ref) < 1e-6
+    scale = 1 / math.sqrt(hd)
+    rows_h, rows_t = np.repeat(np.arange(h), n), np.tile(np.arange(n), h)
+    qh, kh, vh = host(q), host(k), host(v)
+    ref, _ = oracle.moga_attn(qh, kh, vh, ref_r["group_id"], m, ref_r["p_sel"], scale, rows_h,
+                              rows_t)
+    if c["hybrid"]:
+        rt, _ = oracle.stga_attn(qh, kh, vh, grid, "temporal", scale, rows_h, rows_t)
+        rf, _ = oracle.stga_attn(qh, kh, vh, grid, "frame", scale, rows_h, rows_t)
+        ref = (ref + rt + rf) / 3.0
+    assert_close_bf16(host(got["out"]).reshape(-1, hd), ref, f"random forward {c}")
+
+
+def _grad_close(got, ref, what, rrms=1e-2, rmax=8e-2):
+    """Relative RMS within rrms and the largest error within rmax times the reference's RMS
+    (the bar of the backward parity tests)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    scale = float(np.sqrt(np.mean(ref * ref)))
+    r = float(np.sqrt(np.mean((got - ref) ** 2)) / scale) if scale > 0 else 0.0
+    err = float(np.abs(got - ref).max())
+    assert r <= rrms, f"{what}: relative RMS {r:.3e} > {rrms}"
+    assert err <= rmax * scale, f"{what}: max error {err:.3e} > {rmax} x RMS {scale:.3e}"
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_backward(seed):
+    c = _config(100 + seed)
+    c["f32"], c["d"] = False, 64
+    print(f"[case] random backward {c}", flush=True)
+    wl, x, w, q, k, v, grid, pin = _inputs(c)
+    m, hd = c["m"], c["hd"]
+    scale = 1 / math.sqrt(hd)
+    lay = api.make_stga_layout(**grid) if c["hybrid"] else None
+    saved = api.moga_forward(x, w, q, k, v, m, alpha=0.1, pin=torch.from_numpy(pin).to(DEV),
+                             stga=lay, with_lse=True, fused=c["fused"])
+    d_out = workloads.make_dout(wl, DEV)
+    if c["hybrid"]:
+        grads = api.moga_hybrid_backward(x, w, q, k, v, saved, d_out, lay, d_loss=0.7, alpha=0.1)
+    else:
+        grads = api.moga_backward(x, w, q, k, v, saved, d_out, d_loss=0.7, alpha=0.1)
+    torch.cuda.synchronize()
+    gid = oracle.route(host(x), host(w), pin=pin)["group_id"]
+    np.testing.assert_array_equal(host(saved["group_id"]), gid)
+    args = (host(x), host(w), host(q), host(k), host(v), gid)
+    if c["hybrid"]:
+        ref = oracle.hybrid_backward(*args, grid, host(d_out), 0.7, 0.1, scale)
+    else:
+        ref = oracle.moga_backward(*args, host(d_out), 0.7, 0.1, scale)
+    for key in ("dq", "dk", "dv", "dp", "dx", "dw"):
+        _grad_close(host(grads[key]), ref[key], f"random backward {key} {c}")
