@@ -1,9 +1,9 @@
-"""Seeded sweep of small random configurations of the whole forward (explicit and fused) and of
-the backward, through the C ABI, against the oracle: group counts from 1 to 9, router widths,
-head counts and head sizes, bf16 and fp32 router inputs, forced groups for a random subset of
-tokens, and (for the hybrid forward) random frame grids, windows, shot cuts, temporal group
-sizes and borrowed-frame counts.  Every configuration is drawn from a fixed seed, so a failure
-names a reproducible case."""
+"""Seeded sweep of small random configurations through the C ABI, against the oracle: the
+whole forward (explicit and fused) and the backward, with group counts from 1 to 9, router
+widths, head counts and head sizes, bf16 and fp32 router inputs, forced groups for a random
+subset of tokens, and (for the hybrid layer) random frame grids, windows, shot cuts, temporal
+group sizes and borrowed-frame counts; and the varlen group attention on random segment lists.
+Every configuration is drawn from a fixed seed, so a failure names a reproducible case."""
 import math
 
 import numpy as np
@@ -132,3 +132,40 @@ def test_random_backward(seed):
         ref = oracle.moga_backward(*args, host(d_out), 0.7, 0.1, scale)
     for key in ("dq", "dk", "dv", "dp", "dx", "dw"):
         _grad_close(host(grads[key]), ref[key], f"random backward {key} {c}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_group_attn(seed):
+    """Varlen group attention on random segment lists (empty segments, segments with queries
+    and no keys, query and key lengths that differ), with and without a per-row factor and at
+    a given or the default softmax scale; the allocation-free entry point gives the same bits."""
+    rng = np.random.default_rng(4000 + seed)
+    n_seg = int(rng.integers(1, 13))
+    hd, h = int(rng.choice([64, 128])), int(rng.integers(1, 4))
+    top = 1500 if rng.random() < 0.3 else 300
+    ql = rng.integers(0, top, n_seg)
+    ql[0] = max(int(ql[0]), 1)
+    kl = ql.copy() if rng.random() < 0.5 else rng.integers(0, top, n_seg)
+    cu_q = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(kl)]).astype(np.int32)
+    lq, lk = int(cu_q[-1]), max(int(cu_k[-1]), 1)
+    softmax_scale = float(rng.choice([0.0, 0.05, 0.2]))
+    print(f"[case] random group_attn seed={seed} ql={ql.tolist()} kl={kl.tolist()} hd={hd} h={h} "
+          f"scale={softmax_scale}", flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5000 + seed)
+    q = torch.randn((h, lq, hd), generator=g, device=DEV, dtype=torch.bfloat16)
+    k = torch.randn((h, lk, hd), generator=g, device=DEV, dtype=torch.bfloat16)
+    v = torch.randn((h, lk, hd), generator=g, device=DEV, dtype=torch.bfloat16)
+    rs = (torch.rand(lq, generator=g, device=DEV) + 0.5) if rng.random() < 0.5 else None
+    cq, ck = torch.from_numpy(cu_q).to(DEV), torch.from_numpy(cu_k).to(DEV)
+    out = api.moga_group_attn(q, k, v, cq, ck, row_scale=rs, softmax_scale=softmax_scale)
+    out2 = api.moga_group_attn_noalloc(q, k, v, cq, ck, row_scale=rs,
+                                       softmax_scale=softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    scale = softmax_scale if softmax_scale > 0 else 1 / math.sqrt(hd)
+    rows_h, rows_i = np.repeat(np.arange(h), lq), np.tile(np.arange(lq), h)
+    ref, _ = oracle.varlen_attn(host(q), host(k), host(v), cu_q, cu_k, scale, rows_h, rows_i,
+                                row_scale=None if rs is None else host(rs))
+    assert_close_bf16(host(out).reshape(-1, hd), ref, f"random group_attn seed={seed}")
