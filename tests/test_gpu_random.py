@@ -169,3 +169,21 @@ def test_random_group_attn(seed):
     ref, _ = oracle.varlen_attn(host(q), host(k), host(v), cu_q, cu_k, scale, rows_h, rows_i,
                                 row_scale=None if rs is None else host(rs))
     assert_close_bf16(host(out).reshape(-1, hd), ref, f"random group_attn seed={seed}")
+
+
+@pytest.mark.parametrize("hybrid", [False, True])
+@pytest.mark.parametrize("fused", [False, True])
+def test_forward_without_optional_outputs(hybrid, fused):
+    """The routing outputs are optional (the library keeps them in the workspace when the
+    caller passes NULL): out and loss are the same bits with and without them."""
+    c = _config(7)
+    c.update(hybrid=hybrid, fused=fused, hd=128, f32=False, d=64)
+    print(f"[case] forward without optional outputs {c}", flush=True)
+    wl, x, w, q, k, v, grid, pin = _inputs(c)
+    lay = api.make_stga_layout(**grid) if hybrid else None
+    full = api.moga_forward(x, w, q, k, v, c["m"], alpha=0.1, stga=lay, fused=fused)
+    bare = dict(out=torch.empty_like(q), loss=torch.empty(1, dtype=torch.float64, device=DEV))
+    api.moga_forward(x, w, q, k, v, c["m"], alpha=0.1, stga=lay, fused=fused, out=bare)
+    torch.cuda.synchronize()
+    assert torch.equal(full["out"], bare["out"])
+    assert torch.equal(full["loss"], bare["loss"])
