@@ -187,3 +187,55 @@ def test_forward_without_optional_outputs(hybrid, fused):
     torch.cuda.synchronize()
     assert torch.equal(full["out"], bare["out"])
     assert torch.equal(full["loss"], bare["loss"])
+
+
+DEGENERATE = {
+    # one token; one group
+    "n1_m1": dict(frames=1, height=1, width=1, win_h=1, win_w=1, shot_start=[0, 1], t_group=1,
+                  aug_frames=0, m=1, hybrid=False),
+    # more groups than tokens: most groups empty
+    "n6_m9": dict(frames=1, height=2, width=3, win_h=1, win_w=3, shot_start=[0, 1], t_group=1,
+                  aug_frames=0, m=9, hybrid=False),
+    # hybrid layer on a 1x1x1 grid: every segment holds the one token
+    "hybrid_n1": dict(frames=1, height=1, width=1, win_h=1, win_w=1, shot_start=[0, 1],
+                      t_group=1, aug_frames=2, m=3, hybrid=True),
+    # one frame per shot, single-token windows, more borrowed frames than the shots hold
+    "hybrid_1frame_shots": dict(frames=4, height=2, width=2, win_h=1, win_w=1,
+                                shot_start=[0, 1, 2, 3, 4], t_group=3, aug_frames=3, m=2,
+                                hybrid=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEGENERATE))
+@pytest.mark.parametrize("hd", [64, 128])
+def test_forward_degenerate(name, hd):
+    c = _config(3)
+    c.update(DEGENERATE[name], hd=hd, heads=2, f32=False, d=64, fused=False, pin_frac=0.0)
+    print(f"[case] degenerate forward {name} {c}", flush=True)
+    wl, x, w, q, k, v, grid, pin = _inputs(c)
+    n, m = wl.n_tokens, c["m"]
+    lay = api.make_stga_layout(**grid) if c["hybrid"] else None
+    got = api.moga_forward(x, w, q, k, v, m, alpha=0.1, pin=torch.from_numpy(pin).to(DEV),
+                           stga=lay)
+    fused = api.moga_forward(x, w, q, k, v, m, alpha=0.1, pin=torch.from_numpy(pin).to(DEV),
+                             stga=lay, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got["out"], fused["out"])
+    ref_r = oracle.route(host(x), host(w), pin=pin)
+    np.testing.assert_array_equal(host(got["group_id"]), ref_r["group_id"])
+    np.testing.assert_array_equal(host(got["counts"]), ref_r["counts"])
+    cu_ref, _ = oracle.groups(ref_r["group_id"], m)
+    np.testing.assert_array_equal(host(got["cu_seqlens"]), cu_ref)
+    scale = 1 / math.sqrt(hd)
+    h = c["heads"]
+    rows_h, rows_t = np.repeat(np.arange(h), n), np.tile(np.arange(n), h)
+    qh, kh, vh = host(q), host(k), host(v)
+    ref, _ = oracle.moga_attn(qh, kh, vh, ref_r["group_id"], m, ref_r["p_sel"], scale, rows_h,
+                              rows_t)
+    if c["hybrid"]:
+        rt, _ = oracle.stga_attn(qh, kh, vh, grid, "temporal", scale, rows_h, rows_t)
+        rf, _ = oracle.stga_attn(qh, kh, vh, grid, "frame", scale, rows_h, rows_t)
+        ref = (ref + rt + rf) / 3.0
+    assert_close_bf16(host(got["out"]).reshape(-1, hd), ref, f"degenerate {name} hd={hd}")
+    loss_ref, _, _ = oracle.balance_loss(ref_r["counts"], ref_r["prob_sum"], n, 0.1)
+    assert abs(float(got["loss"].item()) - loss_ref) < 1e-6
