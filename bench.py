@@ -76,8 +76,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; the multi-GPU (sequence- "
-                          "parallel) path is a design, not an implementation; run --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU: the multi-GPU (sequence-parallel) "
+                          "path is a design, not an implementation; run --gpus 1"}))
         sys.exit(2)
 
     import numpy as np
