@@ -35,11 +35,16 @@ METRIC = "MoGA fwd tokens/s + group-attn TFLOP/s (% bf16 MFMA peak) at N=282k, M
 # reports null until the counters are taken again.
 STAGE_REPS = 20  # timed calls per short stage and pass in the stage breakdown
 FLUSH_BYTES = 512 << 20  # scratch read before every timed stage call
-ATTN_TRAFFIC = {"bytes": 10_717_284 * 1024 * 2 + 850_790 * 1024, "attn_hip_sha256_16": "29b5f1f97824537d"}
+ATTN_TRAFFIC = {"bytes": 10_717_284 * 1024 * 2 + 850_790 * 1024, "attn_hip_sha256_16": "29b5f1f97824537d",
+                "workload": "wan1.3b_30s_skewed_N282360_M5"}
 
 
-def attn_traffic_bytes():
+def attn_traffic_bytes(workload: str):
+    """HBM bytes per launch of the group-attention kernel from the counter runs, for the
+    workload and kernel source they were taken on; None for any other."""
     import hashlib
+    if workload != ATTN_TRAFFIC["workload"]:
+        return None
     src = os.path.join(ROOT, "sparse_attention_long_moga_amd", "csrc", "attn.hip")
     with open(src, "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()[:16]
@@ -249,7 +254,7 @@ def stage_breakdown(args, wl, x, w, q, k, v, lay, ws, dims, counts, attn_flops):
     stages["roofline"] = {
         "bound": "mfma", "kernel": "attn_kernel_direct<8, false, false> (group_attn stage)",
         "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-        "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": attn_traffic_bytes(),
+        "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": attn_traffic_bytes(wl.name),
         "algorithmic_flops_per_launch": attn_flops,
         "launch_ms": ms["group_attn"],
     }
