@@ -105,3 +105,18 @@ def test_full_size_forward(wl):
         assert_close_bf16(host(o_f[gh, gt]), wf, what + " per-frame branch")
     else:
         assert_close_per_group(host(got["out"][gh, gt]), want_m, label, what)
+
+
+@pytest.mark.parametrize("wl", workloads.CONFIGS, ids=[w.name for w in workloads.CONFIGS])
+def test_full_size_fused_forward_is_bitwise_the_explicit_one(wl):
+    """The permute-free forward (rows read through perm inside the attention kernel) gives the
+    same bits as the explicit one at every workload's full size."""
+    print(f"[case] full-size fused forward {wl.name}", flush=True)
+    x, w = workloads.make_x(wl, DEV), workloads.make_w(wl, DEV)
+    q, k, v = workloads.make_qkv(wl, DEV)
+    lay = api.make_stga_layout(**oracle.grid_of(wl)) if wl.hybrid else None
+    a = api.moga_forward(x, w, q, k, v, wl.n_groups, alpha=wl.alpha, stga=lay)
+    b = api.moga_forward_fused(x, w, q, k, v, wl.n_groups, alpha=wl.alpha, stga=lay)
+    torch.cuda.synchronize()
+    for key in ("out", "group_id", "perm", "cu_seqlens", "p_sel", "prob_sum", "counts", "loss"):
+        assert torch.equal(a[key], b[key]), key
