@@ -18,7 +18,8 @@ from ._capi import MogaDims, MogaGrads, MogaInputs, MogaOutputs, MogaSaved, Stga
 __all__ = ["make_dims", "make_stga_layout", "moga_workspace_bytes", "workspace", "moga_route",
            "moga_permute", "moga_unpermute", "moga_group_attn", "moga_group_attn_noalloc",
            "stga_group_attn",
-           "moga_balance_loss", "moga_forward", "moga_forward_fused", "moga_backward"]
+           "moga_balance_loss", "moga_forward", "moga_forward_fused", "moga_backward",
+           "moga_hybrid_backward", "moga_attention"]
 
 
 def _lib():
@@ -388,3 +389,45 @@ def moga_hybrid_backward(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: t
     if stga is None:
         raise ValueError("moga_hybrid_backward needs the forward's stga layout")
     return _backward(x, w, q, k, v, saved, d_out, d_loss, alpha, softmax_scale, ws, grads, stga)
+
+
+_SAVED_KEYS = ("group_id", "p_sel", "counts", "cu_seqlens", "perm", "lse")
+
+
+class _MogaAttention(torch.autograd.Function):
+    """The layer as one autograd node: moga_forward (with the state its backward needs) on the
+    way in, moga_backward or moga_hybrid_backward on the way out."""
+
+    @staticmethod
+    def forward(ctx, x, w, q, k, v, n_groups, alpha, stga, softmax_scale, pin, fused):
+        fwd = moga_forward(x, w, q, k, v, n_groups, alpha=alpha, pin=pin, stga=stga,
+                           softmax_scale=softmax_scale, fused=fused, with_lse=True)
+        rows = fwd["o_branches"] if stga is not None else fwd["out"]
+        ctx.save_for_backward(x, w, q, k, v, rows, *(fwd[key] for key in _SAVED_KEYS))
+        ctx.stga, ctx.alpha, ctx.softmax_scale = stga, alpha, softmax_scale
+        return fwd["out"], fwd["loss"].view(())
+
+    @staticmethod
+    def backward(ctx, g_out, g_loss):
+        x, w, q, k, v, rows, *state = ctx.saved_tensors
+        saved = dict(zip(_SAVED_KEYS, state))
+        saved["o_branches" if ctx.stga is not None else "out"] = rows
+        d_out = torch.zeros_like(q) if g_out is None else g_out.to(q.dtype).contiguous()
+        # the loss's gradient enters the library as a host scalar (one device synchronisation)
+        d_loss = 0.0 if g_loss is None else float(g_loss)
+        grads = _backward(x, w, q, k, v, saved, d_out, d_loss, ctx.alpha, ctx.softmax_scale,
+                          None, None, ctx.stga)
+        return (grads["dx"].to(x.dtype), grads["dw"], grads["dq"], grads["dk"], grads["dv"],
+                None, None, None, None, None, None)
+
+
+def moga_attention(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                   v: torch.Tensor, n_groups: int, alpha: float = 0.1,
+                   stga: Optional[_Layout] = None, softmax_scale: float = 0.0,
+                   pin: Optional[torch.Tensor] = None, fused: bool = True):
+    """Differentiable MoGA layer (the hybrid MoGA + STGA mean with a layout): returns out
+    ([H, N, head_dim] bf16, token order) and the balance loss (fp64 scalar), both tracked by
+    autograd.  The backward is moga_backward / moga_hybrid_backward with the routing held
+    fixed: gradients reach x and w through p(g|x) and the loss, and q, k, v through the
+    attention; none flows through the group choice."""
+    return _MogaAttention.apply(x, w, q, k, v, n_groups, alpha, stga, softmax_scale, pin, fused)

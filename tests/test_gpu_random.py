@@ -239,3 +239,29 @@ def test_forward_degenerate(name, hd):
     assert_close_bf16(host(got["out"]).reshape(-1, hd), ref, f"degenerate {name} hd={hd}")
     loss_ref, _, _ = oracle.balance_loss(ref_r["counts"], ref_r["prob_sum"], n, 0.1)
     assert abs(float(got["loss"].item()) - loss_ref) < 1e-6
+
+
+@pytest.mark.parametrize("hybrid", [False, True])
+def test_autograd_layer_matches_the_backward_calls(hybrid):
+    """moga_attention under autograd: out and loss are moga_forward's, and the gradients of
+    <G, out> + 0.7 loss are bitwise those of moga_backward / moga_hybrid_backward."""
+    c = _config(11)
+    c.update(hybrid=hybrid, hd=128, f32=False, d=64, m=5, pin_frac=0.0)
+    print(f"[case] autograd layer {c}", flush=True)
+    wl, x, w, q, k, v, grid, _ = _inputs(c)
+    lay = api.make_stga_layout(**grid) if hybrid else None
+    leaves = [t.detach().clone().requires_grad_(True) for t in (x, w, q, k, v)]
+    out, loss = api.moga_attention(*leaves, c["m"], alpha=0.1, stga=lay)
+    g = workloads.make_dout(wl, DEV)
+    ((out.float() * g.float()).sum() + 0.7 * loss).backward()
+    saved = api.moga_forward(x, w, q, k, v, c["m"], alpha=0.1, stga=lay, fused=True,
+                             with_lse=True)
+    if hybrid:
+        ref = api.moga_hybrid_backward(x, w, q, k, v, saved, g, lay, d_loss=0.7, alpha=0.1)
+    else:
+        ref = api.moga_backward(x, w, q, k, v, saved, g, d_loss=0.7, alpha=0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), saved["out"])
+    assert torch.equal(loss.detach(), saved["loss"].view(()))
+    for leaf, key in zip(leaves, ("dx", "dw", "dq", "dk", "dv")):
+        assert torch.equal(leaf.grad, ref[key].to(leaf.dtype)), key
