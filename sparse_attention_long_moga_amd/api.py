@@ -19,7 +19,7 @@ __all__ = ["make_dims", "make_stga_layout", "moga_workspace_bytes", "workspace",
            "moga_permute", "moga_unpermute", "moga_group_attn", "moga_group_attn_noalloc",
            "stga_group_attn",
            "moga_balance_loss", "moga_forward", "moga_forward_fused", "moga_backward",
-           "moga_hybrid_backward", "moga_attention"]
+           "moga_hybrid_backward", "moga_attention", "MoGALayer"]
 
 
 def _lib():
@@ -431,3 +431,24 @@ def moga_attention(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.T
     fixed: gradients reach x and w through p(g|x) and the loss, and q, k, v through the
     attention; none flows through the group choice."""
     return _MogaAttention.apply(x, w, q, k, v, n_groups, alpha, stga, softmax_scale, pin, fused)
+
+
+class MoGALayer(torch.nn.Module):
+    """The MoGA attention layer as a module: it owns the router weight W [d_model, n_groups]
+    (fp32, the group centres the router scores tokens against) and, with a STGA layout, forms
+    the mean with the two static branches.  forward(x, q, k, v) returns (out, balance loss)
+    through moga_attention; the Q/K/V projections and the output projection stay with the
+    caller's model."""
+
+    def __init__(self, d_model: int, n_groups: int, alpha: float = 0.1,
+                 stga: Optional[_Layout] = None, softmax_scale: float = 0.0, device=None):
+        super().__init__()
+        self.n_groups, self.alpha, self.stga, self.softmax_scale = n_groups, alpha, stga, softmax_scale
+        self.weight = torch.nn.Parameter(
+            torch.empty(d_model, n_groups, dtype=torch.float32, device=device))
+        torch.nn.init.normal_(self.weight, std=d_model ** -0.5)
+
+    def forward(self, x: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                pin: Optional[torch.Tensor] = None):
+        return moga_attention(x, self.weight, q, k, v, self.n_groups, alpha=self.alpha,
+                              stga=self.stga, softmax_scale=self.softmax_scale, pin=pin)

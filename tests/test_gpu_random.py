@@ -265,3 +265,24 @@ def test_autograd_layer_matches_the_backward_calls(hybrid):
     assert torch.equal(loss.detach(), saved["loss"].view(()))
     for leaf, key in zip(leaves, ("dx", "dw", "dq", "dk", "dv")):
         assert torch.equal(leaf.grad, ref[key].to(leaf.dtype)), key
+
+
+def test_layer_module_is_the_autograd_layer():
+    """MoGALayer holds W as a parameter and runs moga_attention: same outputs, and W's
+    gradient is the one moga_attention gives."""
+    c = _config(12)
+    c.update(hybrid=True, hd=128, f32=False, d=64, m=4, pin_frac=0.0)
+    print(f"[case] layer module {c}", flush=True)
+    wl, x, w, q, k, v, grid, _ = _inputs(c)
+    lay = api.make_stga_layout(**grid)
+    layer = api.MoGALayer(c["d"], c["m"], alpha=0.1, stga=lay, device=DEV)
+    with torch.no_grad():
+        layer.weight.copy_(w)
+    out, loss = layer(x, q, k, v)
+    (out.float().sum() + loss).backward()
+    w2 = w.detach().clone().requires_grad_(True)
+    out2, loss2 = api.moga_attention(x, w2, q, k, v, c["m"], alpha=0.1, stga=lay)
+    (out2.float().sum() + loss2).backward()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(loss, loss2)
+    assert torch.equal(layer.weight.grad, w2.grad)
