@@ -434,9 +434,10 @@ def moga_attention(x: torch.Tensor, w: torch.Tensor, q: torch.Tensor, k: torch.T
 
 
 class MoGALayer(torch.nn.Module):
-    """The MoGA attention layer as a module: it owns the router weight W [d_model, n_groups]
-    (fp32, the group centres the router scores tokens against) and, with a STGA layout, forms
-    the mean with the two static branches.  forward(x, q, k, v) returns (out, balance loss)
+    """The MoGA attention layer as a module (the drop-in layer of the xugj520.cn blog on MoGA,
+    §8): it owns the router weight W [d_model, n_groups] (fp32, the group centres the router
+    scores tokens against) and, with a STGA layout, forms the mean with the two static
+    branches.  forward(x, q, k, v) returns (out, balance loss)
     through moga_attention; the Q/K/V projections and the output projection stay with the
     caller's model."""
 
