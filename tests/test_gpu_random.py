@@ -286,3 +286,51 @@ def test_layer_module_is_the_autograd_layer():
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(loss, loss2)
     assert torch.equal(layer.weight.grad, w2.grad)
+
+
+@pytest.mark.parametrize("hybrid", [False, True])
+def test_forward_replays_from_a_hip_graph(hybrid):
+    """moga_forward allocates, clears and synchronises nothing itself, so with a caller
+    workspace and preallocated outputs it can be captured into a HIP graph: every replay (with
+    eager work and synchronisations between replays, and new input values copied into the
+    captured tensors) gives the bits of an eager call on the same inputs."""
+    c = _config(13)
+    c.update(hybrid=hybrid, hd=128, f32=False, d=64, m=5, pin_frac=0.0)
+    print(f"[case] graph replay {c}", flush=True)
+    wl, x, w, q, k, v, grid, _ = _inputs(c)
+    lay = api.make_stga_layout(**grid) if hybrid else None
+    n, m = wl.n_tokens, c["m"]
+    dims = api.make_dims(n, c["d"], c["heads"], c["hd"], m, alpha=0.1)
+    ws = api.workspace(api.moga_workspace_bytes(dims, lay), DEV)
+
+    def outputs():
+        return dict(out=torch.empty_like(q), loss=torch.empty(1, dtype=torch.float64, device=DEV),
+                    group_id=torch.empty(n, dtype=torch.int32, device=DEV),
+                    p_sel=torch.empty(n, dtype=torch.float32, device=DEV),
+                    cu_seqlens=torch.empty(m + 1, dtype=torch.int32, device=DEV),
+                    perm=torch.empty(n, dtype=torch.int32, device=DEV),
+                    counts=torch.empty(m, dtype=torch.int32, device=DEV),
+                    prob_sum=torch.empty(m, dtype=torch.float64, device=DEV))
+
+    captured = outputs()
+    api.moga_forward(x, w, q, k, v, m, alpha=0.1, stga=lay, ws=ws, out=captured)  # warm
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        api.moga_forward(x, w, q, k, v, m, alpha=0.1, stga=lay, ws=ws, out=captured)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device=DEV)
+    for rep in range(4):
+        if rep >= 2:  # new input values in the captured tensors
+            gen.manual_seed(600 + rep)
+            q.copy_(torch.randn(q.shape, generator=gen, device=DEV).to(q.dtype))
+            k.copy_(torch.randn(k.shape, generator=gen, device=DEV).to(k.dtype))
+        graph.replay()
+        torch.cuda.synchronize()
+        eager_ws = api.workspace(api.moga_workspace_bytes(dims, lay), DEV)
+        eager = api.moga_forward(x, w, q, k, v, m, alpha=0.1, stga=lay, ws=eager_ws,
+                                 out=outputs())
+        _ = (q.float() * 2).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        for key in captured:
+            assert torch.equal(captured[key], eager[key]), (rep, key)
