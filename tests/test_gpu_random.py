@@ -334,3 +334,69 @@ def test_forward_replays_from_a_hip_graph(hybrid):
         torch.cuda.synchronize()
         for key in captured:
             assert torch.equal(captured[key], eager[key]), (rep, key)
+
+
+def test_backward_replays_from_a_hip_graph():
+    """The hybrid backward, with a caller workspace and preallocated gradients, captured into a
+    HIP graph: every replay gives the bits of an eager call."""
+    c = _config(14)
+    c.update(hybrid=True, hd=128, f32=False, d=64, m=5, pin_frac=0.0)
+    print(f"[case] backward graph replay {c}", flush=True)
+    wl, x, w, q, k, v, grid, _ = _inputs(c)
+    lay = api.make_stga_layout(**grid)
+    n, m, d = wl.n_tokens, c["m"], c["d"]
+    saved = api.moga_forward(x, w, q, k, v, m, alpha=0.1, stga=lay, with_lse=True)
+    d_out = workloads.make_dout(wl, DEV)
+    import ctypes
+    from sparse_attention_long_moga_amd import _capi
+    dims = api.make_dims(n, d, c["heads"], c["hd"], m, alpha=0.1)
+    nb = _capi.load().moga_hybrid_backward_workspace_bytes(ctypes.byref(dims), lay.ref())
+    ws = api.workspace(nb, DEV)
+
+    def grads():
+        return dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                    dx=torch.empty(n, d, dtype=torch.float32, device=DEV),
+                    dw=torch.empty(d, m, dtype=torch.float32, device=DEV),
+                    dp=torch.empty(n, dtype=torch.float32, device=DEV))
+
+    captured = grads()
+    api.moga_hybrid_backward(x, w, q, k, v, saved, d_out, lay, d_loss=0.7, ws=ws, grads=captured)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        api.moga_hybrid_backward(x, w, q, k, v, saved, d_out, lay, d_loss=0.7, ws=ws,
+                                 grads=captured)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = api.moga_hybrid_backward(x, w, q, k, v, saved, d_out, lay, d_loss=0.7)
+        _ = (d_out.float() * 3).sum()
+        torch.cuda.synchronize()
+        for key in captured:
+            assert torch.equal(captured[key], eager[key]), (rep, key)
+
+
+def test_concurrent_forwards_on_two_streams():
+    """Two forwards on two streams at once, each with its own workspace and outputs, give the
+    bits of the same calls made one after the other."""
+    outs = []
+    cases = []
+    for seed in (15, 16):
+        c = _config(seed)
+        c.update(hd=128, f32=False, d=64, pin_frac=0.0)
+        cases.append((c, _inputs(c)))
+    ref = []
+    for c, (wl, x, w, q, k, v, grid, _) in cases:
+        lay = api.make_stga_layout(**grid) if c["hybrid"] else None
+        ref.append(api.moga_forward(x, w, q, k, v, c["m"], alpha=0.1, stga=lay))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s, (c, (wl, x, w, q, k, v, grid, _)) in zip(streams, cases):
+        with torch.cuda.stream(s):
+            lay = api.make_stga_layout(**grid) if c["hybrid"] else None
+            outs.append(api.moga_forward(x, w, q, k, v, c["m"], alpha=0.1, stga=lay))
+    torch.cuda.synchronize()
+    for a, b in zip(outs, ref):
+        for key in ("out", "group_id", "perm", "loss"):
+            assert torch.equal(a[key], b[key]), key
