@@ -9,9 +9,12 @@
 // 16x16x32 MFMA takes 16 groups (A, from the split W) against 16 tokens (B), so each logit's
 // reduction over d happens inside the matrix core and only the softmax needs two cross-lane
 // steps.  route_stage_kernel (m <= 16, W image within 64 KiB) reads x rows in whole-row
-// pieces and transposes them through LDS; route_mfma_kernel (larger m * d) loads the B
-// operand straight from memory and streams W from L2.  Group statistics are written per
-// wave or per work item and summed in a fixed order, so they are bitwise reproducible.
+// pieces and transposes them through LDS; route_chunk_kernel (a larger image, m <= 30) reads
+// rows the same way and streams the image through LDS in chunks of 256 columns;
+// route_mfma_kernel (more groups) loads the B operand straight from memory and streams W
+// fragments from L2.  Each of the three takes the k-steps in order and the three terms
+// smallest first, so all give the same logits.  Group statistics are written per wave, block or work
+// item and summed in a fixed order, so they are bitwise reproducible.
 //
 // fp32 x: VALU pass.  Each wave streams TPW token rows at a time with 16-byte coalesced
 // loads (lane l holds columns [VEC*l, VEC*l+VEC) of every 64*VEC-wide stripe), multiplies
@@ -254,10 +257,84 @@ __device__ __forceinline__ void route_mma(f32x4 (&acc)[T][MT], const RouteFrag<M
                                                                      0, 0, 0);
 }
 
-// Softmax, argmax (lowest group index on equal logits), pins, outputs and the statistics of
-// one work item of T*16 tokens starting at t0.  Lane l holds the logits acc[i][mt][v] of
-// groups 16mt + 4kq + v of token t0 + 16i + tok; the item's statistics go to row `item` of
-// part_p / part_c (stride m).
+// Argmax (lowest group index on equal logits), pin, softmax and outputs of one token whose
+// logits lane l holds as acc[mt][v] for groups 16mt + 4kq + v (the four lanes l, l ^ 16, l ^ 32,
+// l ^ 48 hold its other groups); p and the chosen group added to this lane's statistics.
+// pin: the token's pinned group, or anything outside [0, m) for none.
+template <int MT>
+__device__ __forceinline__ void route_token(const RouteLaunch &a, const f32x4 (&acc)[MT], int64_t t,
+                                            bool valid, int pin, int kq, double (&psum)[MT][4],
+                                            int (&cnt)[MT][4]) {
+    const int m = a.m;
+    float best = 0.0f;
+    int bi = kNoGroup;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int g = 16 * mt + 4 * kq + v;
+            if (g < m && (bi == kNoGroup || acc[mt][v] > best)) {
+                best = acc[mt][v];
+                bi = g;
+            }
+        }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+        const float ob = __shfl_xor(best, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (oi != kNoGroup && (bi == kNoGroup || ob > best || (ob == best && oi < bi))) {
+            best = ob;
+            bi = oi;
+        }
+    }
+    const int g = (valid && pin >= 0 && pin < m) ? pin : bi;
+    float e[MT][4];
+    float z = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int gg = 16 * mt + 4 * kq + v;
+            e[mt][v] = gg < m ? __builtin_amdgcn_exp2f((acc[mt][v] - best) * kLog2e) : 0.0f;
+            z += e[mt][v];
+        }
+    // the four lanes of a token add the same pairs, so all get the same z
+    z += __shfl_xor(z, 16, 64);
+    z += __shfl_xor(z, 32, 64);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int gg = 16 * mt + 4 * kq + v;
+            if (gg < m && valid) {
+                const float p = e[mt][v] / z;
+                psum[mt][v] += (double)p;
+                if (gg == g) {
+                    cnt[mt][v] += 1;
+                    a.group_id[t] = g;
+                    a.p_sel[t] = p;
+                }
+            }
+        }
+}
+
+// Sum of one wave's statistics over the 16 lanes of each k-quarter (they hold the same groups).
+template <int MT>
+__device__ __forceinline__ void route_wave_stats(double (&psum)[MT][4], int (&cnt)[MT][4]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                psum[mt][v] += __shfl_xor(psum[mt][v], off, 64);
+                cnt[mt][v] += __shfl_xor(cnt[mt][v], off, 64);
+            }
+}
+
+// Softmax, argmax, pins, outputs and the statistics of one work item of T*16 tokens starting
+// at t0.  Lane l holds the logits acc[i][mt][v] of groups 16mt + 4kq + v of token
+// t0 + 16i + tok; the item's statistics go to row `item` of part_p / part_c (stride m).
 template <int MT, int T>
 __device__ __forceinline__ void route_finish(const RouteLaunch &a, const f32x4 (&acc)[T][MT],
                                              int64_t t0, int item, int tok, int kq) {
@@ -273,73 +350,10 @@ __device__ __forceinline__ void route_finish(const RouteLaunch &a, const f32x4 (
     for (int i = 0; i < T; ++i) {
         const int64_t t = t0 + 16 * i + tok;
         const bool valid = t < n;
-        // argmax, lowest group index on equal logits
-        float best = 0.0f;
-        int bi = kNoGroup;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int g = 16 * mt + 4 * kq + v;
-                if (g < m && (bi == kNoGroup || acc[i][mt][v] > best)) {
-                    best = acc[i][mt][v];
-                    bi = g;
-                }
-            }
-#pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-            const float ob = __shfl_xor(best, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (oi != kNoGroup && (bi == kNoGroup || ob > best || (ob == best && oi < bi))) {
-                best = ob;
-                bi = oi;
-            }
-        }
-        int g = bi;
-        if (a.pin && valid) {
-            const int pv = a.pin[t];
-            if (pv >= 0 && pv < m) g = pv;
-        }
-        float e[MT][4];
-        float z = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int gg = 16 * mt + 4 * kq + v;
-                e[mt][v] = gg < m ? __builtin_amdgcn_exp2f((acc[i][mt][v] - best) * kLog2e)
-                                  : 0.0f;
-                z += e[mt][v];
-            }
-        // the four lanes of a token add the same pairs, so all get the same z
-        z += __shfl_xor(z, 16, 64);
-        z += __shfl_xor(z, 32, 64);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int gg = 16 * mt + 4 * kq + v;
-                if (gg < m && valid) {
-                    const float p = e[mt][v] / z;
-                    psum[mt][v] += (double)p;
-                    if (gg == g) {
-                        cnt[mt][v] += 1;
-                        a.group_id[t] = g;
-                        a.p_sel[t] = p;
-                    }
-                }
-            }
+        const int pin = (a.pin && valid) ? a.pin[t] : -1;
+        route_token<MT>(a, acc[i], t, valid, pin, kq, psum, cnt);
     }
-    // item statistics: the 16 lanes of one k-quarter hold the same groups
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-                psum[mt][v] += __shfl_xor(psum[mt][v], off, 64);
-                cnt[mt][v] += __shfl_xor(cnt[mt][v], off, 64);
-            }
+    route_wave_stats<MT>(psum, cnt);
     if (tok == 0) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -725,6 +739,311 @@ void route_stage_kernel(RouteLaunch a, int n_waves) {
     }
 }
 
+// Columns of W per chunk of route_chunk_kernel, and the bytes of one image row in LDS: the
+// chunk's 512 bytes plus 16, an odd number (33) of 16-byte pieces, so the 16 group rows that
+// one k-slice read touches start in 16 different bank groups.
+constexpr int kChunkCols = 256;
+constexpr int kChunkRow = 2 * kChunkCols + 16;
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one workgroup
+
+// Workgroup barrier for data written into LDS with ordinary stores, leaving vector-memory loads
+// in flight: any fence would wait for them, so the wave's LDS stores are waited for explicitly
+// (lgkmcnt(0)) and the empty asm statements keep the compiler from moving memory accesses
+// across.
+__device__ __forceinline__ void lds_store_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS of one image buffer of route_chunk_kernel: 3m rows of terms and one zero row.
+__host__ __device__ inline int route_chunk_wbuf(int m) {
+    return ((3 * m + 1) * kChunkRow + 255) & ~255;
+}
+
+// The image route_chunk_kernel streams, chunk-major: chunk c, row t m + g, column j holds term t
+// of W[256 c + j][g] (w = t0 + t1 + t2 exactly, each term bf16; zero for k >= d).  Thread i
+// takes the column pair (2 j2, 2 j2 + 1) of one (chunk, group) and writes one dword per term.
+__global__ __launch_bounds__(256) void route_image_kernel(const float *w, int d, int m,
+                                                          int n_chunks, uint32_t *img) {
+    constexpr int kPairs = kChunkCols / 2;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)n_chunks * m * kPairs) return;
+    const int j2 = (int)(idx % kPairs);
+    const int64_t rest = idx / kPairs;
+    const int g = (int)(rest % m), c = (int)(rest / m);
+    uint32_t packed[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int k = c * kChunkCols + 2 * j2 + h;
+        const float v = k < d ? w[(int64_t)k * m + g] : 0.0f;
+        const bf16 b0 = (bf16)v;
+        const float r1 = v - (float)b0;  // exact
+        const bf16 b1 = (bf16)r1;
+        const bf16 b2 = (bf16)(r1 - (float)b1);  // exact, at most 8 significant bits
+        packed[0] |= (uint32_t)__builtin_bit_cast(uint16_t, b0) << (16 * h);
+        packed[1] |= (uint32_t)__builtin_bit_cast(uint16_t, b1) << (16 * h);
+        packed[2] |= (uint32_t)__builtin_bit_cast(uint16_t, b2) << (16 * h);
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+        img[((int64_t)c * 3 * m + t * m + g) * kPairs + j2] = packed[t];
+}
+
+// LDS of route_chunk_kernel<NW, T>: two image buffers and one tile of T x 16 rows per wave.
+template <int NW, int T>
+constexpr size_t route_chunk_smem(int m) {
+    return 2 * (size_t)route_chunk_wbuf(m) + (size_t)NW * 16 * T * 2 * kChunkCols;
+}
+
+// Row-contiguous reads for the matrix cores with W streamed through LDS (bf16 x, m <= 16 MT,
+// a three-term W image too large for route_stage_kernel's LDS budget, as at width 5120).  A
+// block of NW waves owns a contiguous, balanced range of 16-token tiles and takes them NW*T at
+// a time (T consecutive tiles per wave), running through W in chunks of 256 columns.  A unit
+// of work is one chunk of the block's current tiles: each wave writes its tiles' rows (T x 16
+// rows x 512 bytes, 16-byte piece c of row r at position c ^ (r & 15)) from its ring of
+// registers into its own LDS tile, refills the ring with the unit NH ahead, and multiplies the
+// rows by the block's LDS copy of the chunk (16x16x32 MFMAs, A = W terms, B = x).  Meanwhile
+// the block loads the next chunk of the image (from L2) into registers and writes it into the
+// other of two LDS buffers, handed over behind a barrier that waits for LDS stores only, so the
+// rows' loads stay in flight across it.  The waves' statistics are summed in a fixed order
+// into row blockIdx.x of part_p / part_c.
+template <int NW, int T, int MT, int NH>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void route_chunk_kernel(RouteLaunch a, const void *img, int n_chunks, int n_blocks) {
+    static_assert(NH == 1 || NH == 2, "the unit loop below handles one or two ring parts");
+    static_assert(NW % 4 == 0, "whole waves per SIMD");
+    constexpr int UB = 2 * kChunkCols;   // bytes of a row per chunk
+    constexpr int LPR = UB / 16;         // lanes per row in a load
+    constexpr int RPI = 64 / LPR;        // rows per load instruction
+    constexpr int NL = 16 * T / RPI;     // load instructions per unit
+    constexpr int KS = kChunkCols / 32;  // k-steps per chunk
+    constexpr int PPR = UB / 16;         // 16-byte pieces per image row
+    constexpr int NWL = (3 * 16 * MT * PPR + 64 * NW - 1) / (64 * NW);  // image loads per thread
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int d = a.d, m = a.m;
+    const int64_t n = a.n;
+    const int wbuf = route_chunk_wbuf(m);
+    const int lane = threadIdx.x & 63, tok = lane & 15, kq = lane >> 4;
+    const int lrow = lane / LPR, lchunk = lane % LPR;  // the row and piece this lane loads
+    const int wv = uniform_int(threadIdx.x >> 6);
+    const int64_t n_tiles = (n + 15) / 16;
+    const int64_t bt0 = (int64_t)blockIdx.x * n_tiles / n_blocks;
+    const int64_t bt1 = (int64_t)(blockIdx.x + 1) * n_tiles / n_blocks;
+    const int n_units = (int)((bt1 - bt0 + NW * T - 1) / (NW * T)) * n_chunks;
+    const int64_t row_end = min(n, 16 * bt1);  // rows of this block end here
+    const bf16 *x = static_cast<const bf16 *>(a.x);
+    const uint32_t rowb = (uint32_t)d * 2;
+    // this wave's first tile in tile group k
+    auto wave_tile = [&](int k) { return bt0 + (int64_t)k * (NW * T) + wv * T; };
+    // this wave's rows in tile group k (none past the block's range: those loads read zeros)
+    auto rows_rsrc = [&](int k) {
+        const int64_t r0 = 16 * wave_tile(k);
+        const int64_t rows = r0 < row_end ? min((int64_t)(16 * T), row_end - r0) : 0;
+        return make_rsrc(x + (rows > 0 ? r0 : 0) * (int64_t)d, (uint32_t)rows * rowb);
+    };
+    // this lane's byte offset in its rows for chunk c, or one past any descriptor (columns at
+    // or past d)
+    auto xoff = [&](int c) -> uint32_t {
+        return kChunkCols * c + 8 * lchunk < d
+                   ? (uint32_t)lrow * rowb + (uint32_t)UB * c + 16u * lchunk
+                   : 0x80000000u;
+    };
+    const int pieces = 3 * m * PPR;  // of one chunk of the image
+    const __amdgpu_buffer_rsrc_t rimg = make_rsrc(img, (uint32_t)n_chunks * pieces * 16);
+    auto load_image = [&](u32x4 (&wr)[NWL], int c, bool live) {
+#pragma unroll
+        for (int i = 0; i < NWL; ++i) {
+            const int pc = threadIdx.x + i * 64 * NW;
+            wr[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                rimg, (live && pc < pieces) ? (uint32_t)(c * pieces + pc) * 16 : 0x80000000u, 0, 0);
+        }
+    };
+    auto store_image = [&](const u32x4 (&wr)[NWL], int b) {
+#pragma unroll
+        for (int i = 0; i < NWL; ++i) {
+            const int pc = threadIdx.x + i * 64 * NW;
+            if (pc < pieces)
+                *reinterpret_cast<u32x4 *>(smem + b * wbuf + (pc / PPR) * kChunkRow +
+                                           (pc % PPR) * 16) = wr[i];
+        }
+    };
+    // units in order: (tile group, chunk), chunks fastest
+    auto advance = [&](int &k, int &c) {
+        if (++c == n_chunks) { c = 0; ++k; }
+    };
+
+    // zero rows of both buffers (read by the lanes of padding groups), the first chunk, and the
+    // rows of the first NH units
+    if ((int)threadIdx.x < kChunkRow / 4) {
+        *reinterpret_cast<uint32_t *>(smem + 3 * m * kChunkRow + 4 * threadIdx.x) = 0u;
+        *reinterpret_cast<uint32_t *>(smem + wbuf + 3 * m * kChunkRow + 4 * threadIdx.x) = 0u;
+    }
+    u32x4 wr[NWL];
+    load_image(wr, 0, true);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 ring[NH][NL];
+    int kp = 0, cp = 0;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const __amdgpu_buffer_rsrc_t r0 = rows_rsrc(kp);
+        const uint32_t o = xoff(cp);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            ring[h][i] = __builtin_amdgcn_raw_buffer_load_b128(r0, o + i * RPI * rowb, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);  // the order the loop consumes them in
+        }
+        advance(kp, cp);
+    }
+    store_image(wr, 0);
+    lds_store_barrier();
+
+    // A fragments: lane (g = tok, kq) of group tile mt reads term t of W[32 s + 8 kq .. +8]
+    // [16 mt + g]; lanes of padding groups read the zero row, so the k-step loop has no branch
+    int wl[MT], wterm[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const bool act = 16 * mt + tok < m;
+        wl[mt] = (act ? (16 * mt + tok) : 3 * m) * kChunkRow + 16 * kq;
+        wterm[mt] = act ? m * kChunkRow : 0;
+    }
+    char *xs = smem + 2 * wbuf + wv * (16 * T * UB);
+
+    double psum[MT][4];
+    int cnt[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) { psum[mt][v] = 0.0; cnt[mt][v] = 0; }
+    f32x4 acc[T][MT];
+    int pin_raw[T];
+
+    // one unit u = (k, c): write ring part H into the LDS tile and refill it with unit (kp, cp),
+    // NH units ahead; multiply; finish the tiles after the last chunk; hand over the next chunk
+    auto unit = [&](auto hc, int u, int k, int c) {
+        constexpr int H = decltype(hc)::value;
+        const int64_t tile0 = wave_tile(k);
+        // the pins of this lane's tokens, read in every unit (none: zero records); issued before
+        // the refills, so waiting for them waits for nothing newer
+        {
+            const int64_t r0 = 16 * tile0;
+            const int64_t rows = (a.pin && r0 < row_end) ? min((int64_t)(16 * T), row_end - r0) : 0;
+            const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.pin + (rows > 0 ? r0 : 0),
+                                                        (uint32_t)rows * 4);
+#pragma unroll
+            for (int i = 0; i < T; ++i)
+                pin_raw[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, 4u * (16 * i + tok), 0, 0);
+        }
+        const bool wnext = u + 1 < n_units;
+        load_image(wr, c + 1 == n_chunks ? 0 : c + 1, wnext);
+        __builtin_amdgcn_sched_barrier(0);
+        const __amdgpu_buffer_rsrc_t rn = rows_rsrc(kp);
+        const uint32_t on = xoff(cp);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int r = RPI * i + lrow;
+            *reinterpret_cast<u32x4 *>(xs + r * UB + ((lchunk ^ (r & 15)) << 4)) = ring[H][i];
+            __builtin_amdgcn_sched_barrier(0);
+            ring[H][i] = __builtin_amdgcn_raw_buffer_load_b128(rn, on + i * RPI * rowb, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (c == 0) {
+#pragma unroll
+            for (int i = 0; i < T; ++i)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[i][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        const char *wb = smem + (u & 1) * wbuf;
+        // operands of k-step s: the three W terms of each group tile and the x k-slice of each
+        // tile
+        struct Ops {
+            bf16x8 w[3][MT];
+            bf16x8 x[T];
+        };
+        auto read_ops = [&](Ops &f, int s) {
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    f.w[t][mt] = *reinterpret_cast<const bf16x8 *>(wb + wl[mt] + t * wterm[mt] + 64 * s);
+#pragma unroll
+            for (int i = 0; i < T; ++i)
+                f.x[i] = *reinterpret_cast<const bf16x8 *>(xs + (16 * i + tok) * UB +
+                                                           (((4 * s + kq) ^ tok) << 4));
+        };
+        auto mma = [&](const Ops &f) {
+#pragma unroll
+            for (int t = 2; t >= 0; --t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < T; ++i)
+                        acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[t][mt], f.x[i],
+                                                                             acc[i][mt], 0, 0, 0);
+        };
+        // reads one k-step ahead of the products
+        Ops fr[2];
+        read_ops(fr[0], 0);
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+            if (s2 + 1 < KS) read_ops(fr[(s2 + 1) & 1], s2 + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fr[s2 & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (c + 1 == n_chunks) {
+#pragma unroll
+            for (int i = 0; i < T; ++i) {
+                const int64_t t = 16 * (tile0 + i) + tok;
+                if (16 * (tile0 + i) < row_end)  // the same for the whole wave
+                    route_token<MT>(a, acc[i], t, t < row_end, a.pin ? pin_raw[i] : -1, kq, psum,
+                                    cnt);
+            }
+        }
+        if (wnext) store_image(wr, (u + 1) & 1);
+        lds_store_barrier();
+        advance(kp, cp);
+    };
+
+    // NH units per iteration (one per ring part); a count that is not a multiple of NH ends
+    // with a unit past the range, whose loads read nothing and whose tiles are not finished
+    int kc = 0, cc = 0;
+    for (int u = 0; u < n_units; u += NH) {
+        unit(std::integral_constant<int, 0>{}, u, kc, cc);
+        advance(kc, cc);
+        if constexpr (NH == 2) {
+            unit(std::integral_constant<int, 1>{}, u + 1, kc, cc);
+            advance(kc, cc);
+        }
+    }
+    // the block's statistics: each wave's, then the waves' in order (through LDS)
+    route_wave_stats<MT>(psum, cnt);
+    __syncthreads();
+    double *sp = reinterpret_cast<double *>(smem);                 // [NW][16 MT]
+    int *sc = reinterpret_cast<int *>(smem + NW * 16 * MT * 8);    // [NW][16 MT]
+    if (tok == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                sp[wv * 16 * MT + 16 * mt + 4 * kq + v] = psum[mt][v];
+                sc[wv * 16 * MT + 16 * mt + 4 * kq + v] = cnt[mt][v];
+            }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < m) {
+        double p = 0.0;
+        int c = 0;
+        for (int w = 0; w < NW; ++w) {
+            p += sp[w * 16 * MT + threadIdx.x];
+            c += sc[w * 16 * MT + threadIdx.x];
+        }
+        a.part_p[(int64_t)blockIdx.x * m + threadIdx.x] = p;
+        a.part_c[(int64_t)blockIdx.x * m + threadIdx.x] = c;
+    }
+}
+
 // One block per group: fixed-order sum of the per-block partials.
 __global__ __launch_bounds__(256) void route_finalize(const double *part_p, const int32_t *part_c,
                                                        int64_t nblk, int stride, double *prob_sum,
@@ -815,6 +1134,43 @@ hipError_t launch_stage(const RouteLaunch &a, size_t lds, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int NW, int T, int MT, int NH>
+hipError_t launch_chunk(const RouteLaunch &a, hipStream_t s) {
+    int cus = 0;
+    hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    // once per device (and thread-safe): allow the largest LDS of this instantiation
+    static DeviceOnce attr;
+    if ((e = attr.run([] {
+             return hipFuncSetAttribute(
+                 reinterpret_cast<const void *>(&route_chunk_kernel<NW, T, MT, NH>),
+                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                 (int)std::min(route_chunk_smem<NW, T>(16 * MT), kLdsBytes));
+         })) != hipSuccess)
+        return e;
+    const int n_chunks = (a.d + kChunkCols - 1) / kChunkCols;
+    uint32_t *img = reinterpret_cast<uint32_t *>(static_cast<char *>(a.wsplit) + 256);
+    const int64_t pairs = (int64_t)n_chunks * a.m * (kChunkCols / 2);
+    hipLaunchKernelGGL(route_image_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s,
+                       a.w, a.d, a.m, n_chunks, img);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // at most one block per CU, each with the same whole number of tile groups (NW*T tiles) as
+    // nearly as the count allows, so that no block ends on a mostly empty group (60 s router:
+    // 256 blocks of 17.2 groups 1.012 ms, 245 blocks of 17.96 0.988 ms)
+    const int64_t n_tiles = (a.n + 15) / 16;
+    const int64_t groups = (n_tiles + NW * T - 1) / (NW * T);
+    const int64_t iters = (groups + cus - 1) / cus;
+    const int n_blocks = (int)std::max<int64_t>(1, (groups + iters - 1) / iters);
+    const size_t smem = route_chunk_smem<NW, T>(a.m);
+    hipLaunchKernelGGL((route_chunk_kernel<NW, T, MT, NH>), dim3((unsigned)n_blocks),
+                       dim3(64 * NW), smem, s, a,
+                       static_cast<const void *>(img), n_chunks, n_blocks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(route_finalize, dim3(a.m), dim3(256), 0, s, a.part_p, a.part_c, n_blocks,
+                       a.m, a.prob_sum, a.counts);
+    return hipGetLastError();
+}
+
 template <int MT, int T, int U>
 hipError_t launch_mfma(const RouteLaunch &a, hipStream_t s) {
     // occupancy of this instantiation, queried once per device (thread-safe)
@@ -856,24 +1212,27 @@ hipError_t launch_mfma(const RouteLaunch &a, hipStream_t s) {
 int64_t route_blocks(int64_t n) { return (n + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock; }
 
 int64_t route_partials(int64_t n) {
-    // per-block rows of kMaxGroups (fp32 x) or per-wave / per-item rows of m <= kMaxGroups (bf16
-    // x: waves of at least one 16-token tile, items of 64 tokens)
+    // per-block rows of kMaxGroups (fp32 x) or per-wave / per-block / per-item rows of
+    // m <= kMaxGroups (bf16 x: waves and blocks of at least one 16-token tile, items of 64 tokens)
     return std::max<int64_t>(route_blocks(n), (n + 15) / 16);
 }
 
 size_t route_split_bytes(int d, int m) {
     const size_t frags = (size_t)3 * ((m + 15) / 16) * ((d + 31) / 32) * 64 * sizeof(bf16x8);
-    return 256 + frags;
+    const size_t image = (size_t)3 * m * ((d + kChunkCols - 1) / kChunkCols) * kChunkCols * 2;
+    return 256 + std::max(frags, image);
 }
 
 hipError_t launch_route(const RouteLaunch &a, hipStream_t s) {
     if (a.x_is_bf16) {
         const size_t lds_img = (size_t)(3 * a.m + 1) * route_stage_row_bytes(a.d);
         if (a.m <= 16 && lds_img <= (size_t)kRouteLdsW) return launch_stage<8, 1, 512>(a, lds_img, s);
-        // many 16-token tiles per item, so that each W fragment loaded from L2 serves as many
-        // tokens as the registers allow (60 s router: four tiles 1.64 ms, eight 1.47 ms, ten
-        // 1.44 ms; twelve spill)
-        if (a.m <= 16) return launch_mfma<1, 8, 1>(a, s);
+        // a larger image streamed through LDS in chunks of columns, as long as two chunk buffers
+        // and the row tiles fit
+        if (a.m <= 16) return launch_chunk<8, 1, 1, 2>(a, s);
+        if (route_chunk_smem<8, 1>(a.m) <= kLdsBytes) return launch_chunk<8, 1, 2, 2>(a, s);
+        // W fragments streamed from L2 into registers, many 16-token tiles per item, so that
+        // each fragment serves as many tokens as the registers allow
         if (a.m <= 32) return launch_mfma<2, 10, 1>(a, s);
         if (a.m <= 48) return launch_mfma<3, 2, 1>(a, s);
         return launch_mfma<4, 2, 1>(a, s);

@@ -42,10 +42,18 @@ def _router_case(n, d, m, seed, x_dtype="bf16", dirichlet=None):
     (70000, 1536, 5, "bf16", 12),    # many waves, each over a range of 16-token tiles
     (3000, 512, 16, "bf16", 13),     # sixteen groups: every lane of the row-contiguous kernel
     (500, 768, 1, "bf16", 14),       # one group in bf16: p == 1
-    # bf16 x whose three-term W image exceeds the LDS budget with M <= 16: W streamed from L2
-    # in fragments (the Wan2.1-14B width, 5120, with the pages' M = 5, and M = 16)
+    # bf16 x whose three-term W image exceeds the LDS budget: W streamed through LDS in chunks
+    # of 256 columns (the Wan2.1-14B width, 5120, with the pages' M = 5, 16 and 20)
     (3000, 5120, 5, "bf16", 21),
     (2000, 5120, 16, "bf16", 22),
+    (4000, 5120, 20, "bf16", 32),
+    (2100, 1000, 30, "bf16", 33),    # the most groups two chunk buffers hold; a partial chunk
+    (37, 2048, 20, "bf16", 34),      # one block, most of its waves without a tile
+    (1, 5120, 5, "bf16", 35),        # a single token
+    (300, 10240, 1, "bf16", 36),     # one group: p == 1
+    (70000, 2048, 12, "bf16", 37),   # every CU, a partial last tile group per block
+    # bf16 x with 31 or 32 groups and a large image: W fragments streamed from L2
+    (1500, 1024, 32, "bf16", 38),
     # f32 x at every group-count instantiation of the vector router
     (2500, 256, 5, "f32", 23),
     (2500, 256, 8, "f32", 24),
