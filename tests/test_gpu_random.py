@@ -288,6 +288,39 @@ def test_layer_module_is_the_autograd_layer():
     assert torch.equal(layer.weight.grad, w2.grad)
 
 
+@pytest.mark.parametrize("n, d, m, x_dtype", [
+    (3000, 512, 5, "bf16"),    # W image in LDS
+    (2500, 5120, 20, "bf16"),  # the image streamed through LDS in chunks (a pre-pass)
+    (1500, 1024, 32, "bf16"),  # W fragments from L2 (a pre-pass and a work queue)
+    (2000, 256, 8, "f32"),     # the vector router
+])
+def test_route_replays_from_a_hip_graph(n, d, m, x_dtype):
+    """Every router path, captured into a HIP graph with a caller workspace: each replay, with
+    new x between replays, gives the bits of an eager call."""
+    print(f"[case] route graph replay n={n} d={d} m={m} {x_dtype}", flush=True)
+    wl = workloads.small(f"route_graph_{d}_{m}", n, d, 1, 64, m, seed=d + m, x_dtype=x_dtype)
+    x, w = workloads.make_x(wl, DEV), workloads.make_w(wl, DEV)
+    x2 = workloads.make_x(workloads.small("route_graph_b", n, d, 1, 64, m, seed=d + m + 1,
+                                          x_dtype=x_dtype), DEV)
+    dims = api.make_dims(n, d, 1, 64, m)
+    ws = api.workspace(api.moga_workspace_bytes(dims), DEV)
+    api.moga_route(x, w, m, ws=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        got = api.moga_route(x, w, m, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        if rep == 2:
+            x.copy_(x2)
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = api.moga_route(x, w, m)
+        torch.cuda.synchronize()
+        for key in ("group_id", "p_sel", "counts", "prob_sum"):
+            assert torch.equal(got[key], eager[key]), (rep, key)
+
+
 @pytest.mark.parametrize("hybrid", [False, True])
 def test_forward_replays_from_a_hip_graph(hybrid):
     """moga_forward allocates, clears and synchronises nothing itself, so with a caller
