@@ -274,86 +274,116 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
         const bf16 *qbase = a.q + hrow * HD, *gbase = a.dov + hrow * HD;
         const int ntiles = (qlen + KT - 1) / KT;
 
-        // query tile t -> buffer BUF; rows past the group read as zeros
-        auto issue = [&](auto bufc, int t) {
-            constexpr int buf = decltype(bufc)::value;
+        // Query tile t -> buffer BUF (rows past the group read as zeros), in two groups.  The
+        // first (Q and dO' in the A layout, dO' in the T layout, lse2) is issued at the start of
+        // tile t - 1: the buffer's previous tile, t - 2, was last read by those roles before tile
+        // t - 2 ended.  The second (Q in the T layout, D) is read by the dK waves one tile later
+        // than the rest, so it is issued after the middle barrier of tile t - 1, once those
+        // waves are done with tile t - 2.
+        auto tile_rsrc = [&](int t, bool g) {
             const int q0 = t * KT;
             // one tile at most; readfirstlane keeps the count (and so the descriptor) scalar
             const uint32_t bytes = (uint32_t)uniform(min(max(qlen - q0, 0), KT)) * ROWB;
-            const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (int64_t)(rb + q0) * HD, bytes);
-            const __amdgpu_buffer_rsrc_t rg = make_rsrc(gbase + (int64_t)(rb + q0) * HD, bytes);
+            return make_rsrc((g ? gbase : qbase) + (int64_t)(rb + q0) * HD, bytes);
+        };
+        // lse2 or D of the tile's queries (256 entries; 64 are used), by wave 0
+        auto issue_row = [&](unsigned char *dst, const float *src, int t) {
+            if (wave == 0) {
+                const int q0 = t * KT;
+                // what one load reads, kept scalar
+                const uint32_t rbytes = (uint32_t)uniform(min(max(qlen - q0, 0), 256)) * 4;
+                load_lds16(make_rsrc(src + hrow + rb + q0, rbytes), dst, 16 * lane);
+            }
+        };
+        auto issue_first = [&](auto bufc, int t) {
+            constexpr int buf = decltype(bufc)::value;
+            const __amdgpu_buffer_rsrc_t rq = tile_rsrc(t, false), rg = tile_rsrc(t, true);
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 const int slot = (i * WAVES + wave) * 1024;
                 load_lds16(rq, &lds[buf][0][slot], ago[i]);
-                load_lds16(rq, &lds[buf][1][slot], tgo[i]);
                 load_lds16(rg, &lds[buf][2][slot], ago[i]);
                 load_lds16(rg, &lds[buf][3][slot], tgo[i]);
             }
-            if (wave == 0) {  // lse2 and D of the tile's queries (256 entries; 64 are used)
-                // what one load reads, kept scalar
-                const uint32_t rbytes = (uint32_t)uniform(min(max(qlen - q0, 0), 256)) * 4;
-                const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse2 + hrow + rb + q0, rbytes);
-                const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.D + hrow + rb + q0, rbytes);
-                load_lds16(rl, reinterpret_cast<unsigned char *>(&rowv[buf][0][0]), 16 * lane);
-                load_lds16(rd, reinterpret_cast<unsigned char *>(&rowv[buf][1][0]), 16 * lane);
+            issue_row(reinterpret_cast<unsigned char *>(&rowv[buf][0][0]), a.lse2, t);
+        };
+        // LOADS loads per thread (one more in wave 0, issued first): the count the end-of-tile
+        // wait leaves in flight
+        auto issue_second = [&](auto bufc, int t) {
+            constexpr int buf = decltype(bufc)::value;
+            issue_row(reinterpret_cast<unsigned char *>(&rowv[buf][1][0]), a.D, t);
+            const __amdgpu_buffer_rsrc_t rq = tile_rsrc(t, false);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int slot = (i * WAVES + wave) * 1024;
+                load_lds16(rq, &lds[buf][1][slot], tgo[i]);
             }
         };
+        static_assert(LOADS == 2, "the end-of-tile wait below leaves two loads in flight");
 
         f32x16 acc[NT];  // dV^T or dK^T of the wave's 32 keys
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) acc[ti] = f32x16{};
+        f32x16 pacc[2];  // dK waves: dP of the tile before, until its dS is formed
 
+        // acc^T += X^T B for the 16-query chunk ch of a tile, X in the T layout at xt
+        auto accumulate = [&](lds_cu8 *xt, int ch, const bf16x8 &bop) {
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) {
+                lds_cu8 *xp = xt + ch * 16 * ROWB + voff[ti];
+                const uint2 lo = lds_read_tr16(xp), hi = lds_read_tr16(xp + 8 * ROWB);
+                const bf16x8 xf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bop, acc[ti], 0, 0, 0);
+            }
+        };
+        auto pack8 = [](const float (&x)[8]) {
+            return __builtin_bit_cast(
+                bf16x8, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                   pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
+        };
+        // dK waves: dS = P (dP - D) of the tile in buffer PB (P from the dV waves, dP from this
+        // wave's products one tile earlier) and dK^T += Q^T dS
+        auto dk_products = [&](auto pbc) {
+            constexpr int pb = decltype(pbc)::value;
+            lds_cu8 *qt_ = lds_ptr(lds[pb][1]);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const uint4 pw = pbuf[qb][kw][half][lane];
+                    const uint32_t w4[4] = {pw.x, pw.y, pw.z, pw.w};
+                    float4 d4[2];
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2)
+                        d4[k2] = *reinterpret_cast<const float4 *>(
+                            &rowv[pb][1][qb * 32 + 8 * (2 * half + k2) + 4 * hh]);
+                    float ds[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float p = __uint_as_float(e & 1 ? (w4[e >> 1] & 0xffff0000u) : (w4[e >> 1] << 16));
+                        ds[e] = p * (pacc[qb][half * 8 + e] - (&d4[e >> 2].x)[e & 3]);
+                    }
+                    accumulate(qt_, qb * 2 + half, pack8(ds));
+                }
+        };
+
+        // Tile t in buffer BUF.  First half: the dV waves form S and P of tile t (kept in
+        // registers); the dK waves form dS of tile t - 1 and its dK products.  Middle barrier
+        // (LDS only): tile t - 1's P, D and Q^T are no longer read, so the second group of tile
+        // t + 1's loads may go into that buffer.  Second half: the dV waves store P and form the
+        // dV products; the dK waves form dP of tile t.  End barrier: P of tile t is visible and
+        // tile t + 1's first group (and tile t's second) has landed.  Each role's products are
+        // issued in the same order as by a kernel that finishes every tile before the next.
         auto tile = [&](auto rolec, auto bufc, auto maskc, int t) {
             constexpr bool DK = decltype(rolec)::value;
             constexpr int buf = decltype(bufc)::value;
             constexpr bool MASK = decltype(maskc)::value;  // only the last, partial tile
-            if (t + 1 < ntiles) issue(std::integral_constant<int, buf ^ 1>{}, t + 1);
-            lds_cu8 *qa = lds_ptr(lds[buf][0]), *qt_ = lds_ptr(lds[buf][1]);
-            lds_cu8 *ga = lds_ptr(lds[buf][2]), *gt_ = lds_ptr(lds[buf][3]);
-            // P (and dS) of the 16 query rows of this lane in block qb: rows qb*32 + 8*kq +
-            // 4*hh + e, kq < 4, e < 4; the 8 values of half `half` are kq = 2*half, 2*half + 1
-            auto probs = [&](int qb, int half, const f32x16 &sacc, float (&pv)[8]) {
-                float4 l4[2];
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
-                    l4[k2] = *reinterpret_cast<const float4 *>(
-                        &rowv[buf][0][qb * 32 + 8 * (2 * half + k2) + 4 * hh]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int v = half * 8 + e;
-                    float p = __builtin_amdgcn_exp2f(
-                        __builtin_fmaf(sacc[v], c, -(&l4[e >> 2].x)[v & 3]));
-                    if constexpr (MASK) {
-                        const int q = t * KT + qb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-                        if (q >= qlen) p = 0.0f;
-                    }
-                    pv[e] = p;
-                }
-            };
-            auto pack8 = [](const float (&x)[8]) {
-                return __builtin_bit_cast(
-                    bf16x8, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
-            };
-            // acc^T += X^T B for the 16-query chunk ch of the tile, X in the T layout at xt
-            auto accumulate = [&](lds_cu8 *xt, int ch, const bf16x8 &bop) {
-#pragma unroll
-                for (int ti = 0; ti < NT; ++ti) {
-                    lds_cu8 *xp = xt + ch * 16 * ROWB + voff[ti];
-                    const uint2 lo = lds_read_tr16(xp), hi = lds_read_tr16(xp + 8 * ROWB);
-                    const bf16x8 xf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                    acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, bop, acc[ti], 0, 0, 0);
-                }
-            };
+            if (t + 1 < ntiles) issue_first(std::integral_constant<int, buf ^ 1>{}, t + 1);
+            bf16x8 pf[2][2];
             if constexpr (!DK) {
-                // S, P of both 32-query blocks; P to the partner wave; dV^T += dO'^T P.  Both
-                // blocks' products are issued before the first exponentials, so block 0's vector
-                // work runs while block 1's products are still in the matrix core; block 0's dV
-                // products are issued before block 1's exponentials, which then run while those
-                // products are in the matrix core, and only block 1's dV products follow the
-                // hand-off.
-                bf16x8 pf[2][2];
+                lds_cu8 *qa = lds_ptr(lds[buf][0]);
+                // P of the 16 query rows of this lane in block qb: rows qb*32 + 8*kq + 4*hh + e,
+                // kq < 4, e < 4; the 8 values of half `half` are kq = 2*half, 2*half + 1
                 f32x16 sacc[2];
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
@@ -363,25 +393,46 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
                         sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, bf[s], s ? sacc[qb] : f32x16{}, 0, 0, 0);
                     }
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
+                for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
+                        float4 l4[2];
+#pragma unroll
+                        for (int k2 = 0; k2 < 2; ++k2)
+                            l4[k2] = *reinterpret_cast<const float4 *>(
+                                &rowv[buf][0][qb * 32 + 8 * (2 * half + k2) + 4 * hh]);
                         float pv[8];
-                        probs(qb, half, sacc[qb], pv);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int v = half * 8 + e;
+                            float p = __builtin_amdgcn_exp2f(
+                                __builtin_fmaf(sacc[qb][v], c, -(&l4[e >> 2].x)[v & 3]));
+                            // query t*KT + qb*32 + 8*(v/4) + 4*hh + v%4: the constant part
+                            // against one per-lane limit (no per-lane table to keep)
+                            if constexpr (MASK)
+                                if (qb * 32 + 8 * (v >> 2) + (v & 3) >= qlen - t * KT - 4 * hh) p = 0.0f;
+                            pv[e] = p;
+                        }
                         pf[qb][half] = pack8(pv);
-                        pbuf[qb][kw][half][lane] = __builtin_bit_cast(uint4, pf[qb][half]);
                     }
-                    if (qb == 0) {
-#pragma unroll
-                        for (int half = 0; half < 2; ++half) accumulate(gt_, half, pf[0][half]);
-                    }
-                }
-                lds_handoff_barrier();  // P of the tile is visible to the dK waves
-#pragma unroll
-                for (int half = 0; half < 2; ++half) accumulate(gt_, 2 + half, pf[1][half]);
             } else {
-                // dP of both blocks; P from the partner wave; dS = P (dP - D); dK^T += Q^T dS
-                f32x16 pacc[2];
+                if (t > 0) dk_products(std::integral_constant<int, buf ^ 1>{});
+            }
+            lds_handoff_barrier();  // middle: tile t - 1 is no longer read
+            if (t + 1 < ntiles) issue_second(std::integral_constant<int, buf ^ 1>{}, t + 1);
+            if constexpr (!DK) {
+                lds_cu8 *gt_ = lds_ptr(lds[buf][3]);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+                        pbuf[qb][kw][half][lane] = __builtin_bit_cast(uint4, pf[qb][half]);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) accumulate(gt_, qb * 2 + half, pf[qb][half]);
+            } else {
+                lds_cu8 *ga = lds_ptr(lds[buf][2]);
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -389,33 +440,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
                         const bf16x8 gf = lds_read_b128(ga + qb * 32 * ROWB + koff[s]);
                         pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, bf[s], s ? pacc[qb] : f32x16{}, 0, 0, 0);
                     }
-                lds_handoff_barrier();  // P of the tile is in pbuf
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const uint4 pw = pbuf[qb][kw][half][lane];
-                        const uint32_t w4[4] = {pw.x, pw.y, pw.z, pw.w};
-                        float4 d4[2];
-#pragma unroll
-                        for (int k2 = 0; k2 < 2; ++k2)
-                            d4[k2] = *reinterpret_cast<const float4 *>(
-                                &rowv[buf][1][qb * 32 + 8 * (2 * half + k2) + 4 * hh]);
-                        float ds[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float p = __uint_as_float(e & 1 ? (w4[e >> 1] & 0xffff0000u) : (w4[e >> 1] << 16));
-                            ds[e] = p * (pacc[qb][half * 8 + e] - (&d4[e >> 2].x)[e & 3]);
-                        }
-                        accumulate(qt_, qb * 2 + half, pack8(ds));
-                    }
             }
-            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed
-            __syncthreads();
+            // end: everything but the two newest loads (tile t + 1's second group, LOADS per
+            // thread; in wave 0 the row load before them is waited for too) has landed
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2), lgkmcnt and expcnt at their maximum
+            lds_handoff_barrier();
         };
 
         if (ntiles > 0) {
-            issue(std::integral_constant<int, 0>{}, 0);
+            issue_first(std::integral_constant<int, 0>{}, 0);
+            issue_second(std::integral_constant<int, 0>{}, 0);
             __builtin_amdgcn_s_waitcnt(0x0f70);
             __syncthreads();
         }
@@ -429,6 +464,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
         // one copy of the tile loop per role, so that the compiler's tracking of outstanding
         // loads never merges the two roles' paths (merged, it adds waits for loads in flight)
         auto run = [&](auto rolec) {
+            constexpr bool DK = decltype(rolec)::value;
             int t = 0;
             for (; t + 1 < nfull; t += 2) {
                 tile(rolec, B0{}, NoMask{}, t);
@@ -441,6 +477,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(AttnBwdLaunch a) 
             if (t < ntiles) {
                 if (t & 1) tile(rolec, B1{}, Mask{}, t);
                 else tile(rolec, B0{}, Mask{}, t);
+            }
+            // the last tile's dK products (its second group of loads is the one left in flight)
+            if (ntiles > 0) {
+                __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+                __syncthreads();
+                if constexpr (DK) {
+                    if ((ntiles - 1) & 1) dk_products(B1{});
+                    else dk_products(B0{});
+                }
             }
         };
         if (dk_role) run(std::true_type{});
