@@ -208,8 +208,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunc
 // Item = (group, head, 128 key rows).  Eight waves; waves w and w + 4 share a SIMD and own the
 // same 32 key rows (32 (w & 3) .. + 31).  Per 32-query block, wave w computes S = Q K^T and
 // P, hands P (bf16, in the B-operand layout) to wave w + 4 through LDS and accumulates
-// dV^T += dO'^T P; wave w + 4 computes dP = dO' V^T, takes P after one workgroup barrier and
-// accumulates dK^T += Q^T dS with dS = P (dP - D).  Each wave issues 16 products per block
+// dV^T += dO'^T P; wave w + 4 computes dP = dO' V^T and, half a tile later, once P is
+// visible, accumulates dK^T += Q^T dS with dS = P (dP - D).  Each wave issues 16 products per block
 // (the same total as one wave doing both) and holds one 64-register accumulator, so two fit
 // a SIMD.  Per 64-query tile: Q and dO' each in the A layout (read as A operands) and in the
 // T layout (read transposed), plus lse2 and D of the tile's queries.  K^T (dV waves) or V^T
