@@ -130,10 +130,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_bwd_dq_kernel(AttnBwdLaunc
                     for (int e = 0; e < 8; ++e) {
                         const int v = half * 8 + e;
                         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c, -lse2));
-                        if constexpr (MASK) {
-                            const int key = t * KT + sb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-                            if (key >= klen) p = 0.0f;
-                        }
+                        // key t*KT + sb*32 + 8*(v/4) + 4*hh + v%4: the constant part against one
+                        // per-lane limit (no per-lane table to keep)
+                        if constexpr (MASK)
+                            if (sb * 32 + 8 * (v >> 2) + (v & 3) >= klen - t * KT - 4 * hh) p = 0.0f;
                         ds[e] = p * (pacc[v] - dd);
                     }
                     const uint4 packed = make_uint4(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
