@@ -52,6 +52,8 @@ def _router_case(n, d, m, seed, x_dtype="bf16", dirichlet=None):
     (1, 5120, 5, "bf16", 35),        # a single token
     (300, 10240, 1, "bf16", 36),     # one group: p == 1
     (70000, 2048, 12, "bf16", 37),   # every CU, a partial last tile group per block
+    (1234, 200, 20, "bf16", 39),     # one partial chunk (the image would fit in LDS, M > 16)
+    (999, 1000, 17, "bf16", 40),     # one group past the first group tile
     # bf16 x with 31 or 32 groups and a large image: W fragments streamed from L2
     (1500, 1024, 32, "bf16", 38),
     # f32 x at every group-count instantiation of the vector router
