@@ -13,8 +13,8 @@
 // rows the same way and streams the image through LDS in chunks of 256 columns;
 // route_mfma_kernel (more groups) loads the B operand straight from memory and streams W
 // fragments from L2.  Each of the three takes the k-steps in order and the three terms
-// smallest first, so all give the same logits.  Group statistics are written per wave, block or work
-// item and summed in a fixed order, so they are bitwise reproducible.
+// smallest first, so all give the same logits.  Group statistics are written per wave, block
+// or work item and summed in a fixed order, so they are bitwise reproducible.
 //
 // fp32 x: VALU pass.  Each wave streams TPW token rows at a time with 16-byte coalesced
 // loads (lane l holds columns [VEC*l, VEC*l+VEC) of every 64*VEC-wide stripe), multiplies
