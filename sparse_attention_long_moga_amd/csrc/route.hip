@@ -186,6 +186,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// cache policy of the loads of x: every row is read once, so the loads are non-temporal (the nt
+// bit), which streams them past the caches rather than keeping them there (30 s router 161 ->
+// 142 us, 60 s 1.00 -> 0.93 ms)
+constexpr int kStreamed = 2;
+
 // a value the caller knows to be the same in every lane, made visibly so to the compiler
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -235,7 +240,7 @@ __device__ __forceinline__ void route_load(RouteFrag<MT, T> &f, __amdgpu_buffer_
                                            uint32_t woff, int frags, int steps, int s) {
 #pragma unroll
     for (int i = 0; i < T; ++i)
-        f.x[i] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], 64 * s, 0));
+        f.x[i] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], 64 * s, kStreamed));
 #pragma unroll
     for (int j = 0; j < 3; ++j)
 #pragma unroll
@@ -553,7 +558,7 @@ void route_stage_kernel(RouteLaunch a, int n_waves) {
         const uint32_t o = xoff(jp);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            ring[h][i] = __builtin_amdgcn_raw_buffer_load_b128(r0, o + i * RPI * rowb, 0, 0);
+            ring[h][i] = __builtin_amdgcn_raw_buffer_load_b128(r0, o + i * RPI * rowb, 0, kStreamed);
             __builtin_amdgcn_sched_barrier(0);  // the order the loop consumes them in
         }
         advance(tp, jp);
@@ -619,7 +624,7 @@ void route_stage_kernel(RouteLaunch a, int n_waves) {
             const int r = RPI * i + lrow;
             *reinterpret_cast<u32x4 *>(xs + r * UB + ((lchunk ^ (r & 15)) << 4)) = ring[H][i];
             __builtin_amdgcn_sched_barrier(0);
-            ring[H][i] = __builtin_amdgcn_raw_buffer_load_b128(rn, on + i * RPI * rowb, 0, 0);
+            ring[H][i] = __builtin_amdgcn_raw_buffer_load_b128(rn, on + i * RPI * rowb, 0, kStreamed);
             __builtin_amdgcn_sched_barrier(0);
         }
         // operands of k-step s of this unit: the three W terms and the x tile's k-slice
@@ -891,7 +896,7 @@ void route_chunk_kernel(RouteLaunch a, const void *img, int n_chunks, int n_bloc
         const uint32_t o = xoff(cp);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            ring[h][i] = __builtin_amdgcn_raw_buffer_load_b128(r0, o + i * RPI * rowb, 0, 0);
+            ring[h][i] = __builtin_amdgcn_raw_buffer_load_b128(r0, o + i * RPI * rowb, 0, kStreamed);
             __builtin_amdgcn_sched_barrier(0);  // the order the loop consumes them in
         }
         advance(kp, cp);
@@ -945,7 +950,7 @@ void route_chunk_kernel(RouteLaunch a, const void *img, int n_chunks, int n_bloc
             const int r = RPI * i + lrow;
             *reinterpret_cast<u32x4 *>(xs + r * UB + ((lchunk ^ (r & 15)) << 4)) = ring[H][i];
             __builtin_amdgcn_sched_barrier(0);
-            ring[H][i] = __builtin_amdgcn_raw_buffer_load_b128(rn, on + i * RPI * rowb, 0, 0);
+            ring[H][i] = __builtin_amdgcn_raw_buffer_load_b128(rn, on + i * RPI * rowb, 0, kStreamed);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (c == 0) {
