@@ -76,8 +76,6 @@ struct PermuteLaunch {
     int64_t n;
     int m;
     int32_t *table;     // [nblk][m] per-block counts
-    int32_t *base_rel;  // [nblk][m] exclusive prefix over blocks, per group
-    int32_t *totals;    // [m]
     int32_t *cu;        // [m+1]
     int32_t *perm;      // [n]
 };

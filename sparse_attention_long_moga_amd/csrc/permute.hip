@@ -5,8 +5,8 @@
 // A counting sort with no atomics deciding positions:
 //   hist    - block b counts the group ids of its kPermTokensPerBlock tokens with wave
 //             ballots (lane i accumulates group i) -> table[b][i];
-//   scan    - one block per group: exclusive prefix of table[.][i] over blocks;
-//   scatter - cu = prefix of group totals; every token's position is
+//   scatter - each block takes its own exclusive prefix of table[.][i] over the blocks before
+//             it and the group totals; cu = prefix of group totals; every token's position is
 //             cu[g] + (tokens of g in earlier blocks) + (earlier in this block), the
 //             in-block part from ballots and popcounts, so equal ids keep token order.
 // The row gathers then move whole head_dim rows (128 or 256 bytes) with 16-byte lanes.
@@ -24,9 +24,18 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *gid, int64_t n
     __shared__ int wc[4][kMaxGroups];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t b0 = (int64_t)blockIdx.x * kPermTokensPerBlock;
+    // every id of the block is loaded first: one memory round trip, not one per pass
+    constexpr int R = kPermTokensPerBlock / 256;
+    int gv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t t = b0 + r * 256 + threadIdx.x;
+        gv[r] = t < n ? gid[t] : -1;
+    }
     int cnt = 0;  // lane i counts group i
-    for (int64_t t = b0 + threadIdx.x; t < b0 + kPermTokensPerBlock; t += 256) {
-        const int g = t < n ? gid[t] : -1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int g = gv[r];
         for (int i = 0; i < m; ++i) {
             const uint64_t bal = __ballot(g == i);
             if (lane == i) cnt += __popcll(bal);
@@ -39,52 +48,52 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *gid, int64_t n
             wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] + wc[3][threadIdx.x];
 }
 
-// Block i: base_rel[b][i] = sum_{b' < b} table[b'][i]; totals[i] = sum over all blocks.
-__global__ __launch_bounds__(256) void scan_kernel(const int32_t *table, int64_t nblk, int m,
-                                                    int32_t *base_rel, int32_t *totals) {
-    __shared__ int s[256];
-    const int g = blockIdx.x;
-    int carry = 0;
-    for (int64_t c0 = 0; c0 < nblk; c0 += 256) {
-        const int64_t b = c0 + threadIdx.x;
-        const int v = b < nblk ? table[b * m + g] : 0;
-        s[threadIdx.x] = v;
-        __syncthreads();
-        // Hillis-Steele inclusive scan over 256 entries
-        for (int off = 1; off < 256; off <<= 1) {
-            const int add = (int)threadIdx.x >= off ? s[threadIdx.x - off] : 0;
-            __syncthreads();
-            s[threadIdx.x] += add;
-            __syncthreads();
-        }
-        if (b < nblk) base_rel[b * m + g] = carry + s[threadIdx.x] - v;
-        carry += s[255];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) totals[g] = carry;
-}
-
+// Block b: its tokens' positions.  The exclusive prefix of table[.][i] over blocks b' < b and
+// the group totals are taken here from the whole table (nblk x m integers, read from L2 by every
+// block; integer sums, so the order of the LDS atomics does not matter), then
+// cu = prefix of group totals and every token's position is cu[g] + (tokens of g in earlier
+// blocks) + (earlier in this block), the in-block part from ballots and popcounts.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *gid, int64_t n, int m,
-                                                       const int32_t *base_rel,
-                                                       const int32_t *totals, int32_t *cu,
-                                                       int32_t *perm) {
+                                                       const int32_t *table, int nblk,
+                                                       int32_t *cu, int32_t *perm) {
+    __shared__ int before[kMaxGroups], total[kMaxGroups];
     __shared__ int base[kMaxGroups];
     __shared__ int wc[4][kMaxGroups];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the block's ids are requested before the table is read, so both loads overlap
+    constexpr int R = kPermTokensPerBlock / 256;
+    int gv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t t = (int64_t)blockIdx.x * kPermTokensPerBlock + r * 256 + threadIdx.x;
+        gv[r] = t < n ? gid[t] : -1;
+    }
+    if ((int)threadIdx.x < m) before[threadIdx.x] = total[threadIdx.x] = 0;
+    __syncthreads();
+    {
+        const int ne = nblk * m, mine = (int)blockIdx.x * m;
+        for (int e = threadIdx.x; e < ne; e += 256) {
+            const int v = table[e], g = e % m;
+            atomicAdd(&total[g], v);
+            if (e < mine) atomicAdd(&before[g], v);
+        }
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
         int acc = 0;
         for (int i = 0; i < m; ++i) {
-            base[i] = acc + base_rel[(int64_t)blockIdx.x * m + i];
+            base[i] = acc + before[i];
             if (blockIdx.x == 0) cu[i] = acc;
-            acc += totals[i];
+            acc += total[i];
         }
         if (blockIdx.x == 0) cu[m] = acc;
     }
     __syncthreads();
     const int64_t b0 = (int64_t)blockIdx.x * kPermTokensPerBlock;
-    for (int64_t c0 = b0; c0 < b0 + kPermTokensPerBlock; c0 += 256) {
-        const int64_t t = c0 + threadIdx.x;
-        const int g = t < n ? gid[t] : -1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t t = b0 + r * 256 + threadIdx.x;
+        const int g = gv[r];
         int rank = 0;
         for (int i = 0; i < m; ++i) {
             const uint64_t bal = __ballot(g == i);
@@ -192,11 +201,8 @@ hipError_t launch_perm_index(const PermuteLaunch &a, hipStream_t s) {
                        a.table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(scan_kernel, dim3(a.m), dim3(256), 0, s, a.table, nblk, a.m, a.base_rel,
-                       a.totals);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nblk), dim3(256), 0, s, a.group_id, a.n, a.m,
-                       a.base_rel, a.totals, a.cu, a.perm);
+                       a.table, (int)nblk, a.cu, a.perm);
     return hipGetLastError();
 }
 
