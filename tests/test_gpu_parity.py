@@ -103,6 +103,9 @@ def test_route_pins_force_groups():
 @pytest.mark.parametrize("n, m, hd, case", [
     (5000, 5, 128, "random"), (4097, 7, 64, "empty_group"), (2048, 1, 128, "one_group"),
     (3000, 4, 64, "collapse"), (1, 3, 64, "single"), (6000, 64, 64, "random"),
+    # many index blocks: runs of one group longer than a block (most groups absent from most
+    # blocks, so every block's prefix adds many zeros), and a skewed mixture over 64 groups
+    (200001, 64, 64, "runs"), (150000, 64, 64, "skewed"),
 ])
 def test_permute_parity_and_round_trip(n, m, hd, case):
     _announce("permute", n=n, m=m, hd=hd, case=case)
@@ -112,6 +115,10 @@ def test_permute_parity_and_round_trip(n, m, hd, case):
         g[g == 3] = 4
     if case == "collapse":
         g[:] = 2
+    if case == "runs":
+        g = np.repeat(rng.integers(0, m, n // 5000 + 1), 5000)[:n].astype(np.int32)
+    if case == "skewed":
+        g = rng.choice(m, n, p=rng.dirichlet(np.full(m, 0.2))).astype(np.int32)
     gid = torch.from_numpy(g).to(DEV)
     h = 3
     q = torch.randn((h, n, hd), device=DEV, dtype=torch.bfloat16)
