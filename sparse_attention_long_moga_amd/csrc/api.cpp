@@ -136,7 +136,7 @@ struct Carver {
 
 struct Layout {
     // MoGA
-    size_t part_p, part_c, wsplit, gid, psel, counts, probsum, cu, perm, table, pperm;
+    size_t part_p, part_c, wsplit, gid, psel, counts, probsum, cu, perm, table, base_rel, totals, pperm;
     size_t qp, kp, vp, plan;
     // STGA
     size_t shot_info, cu_tq, cu_tk, cu_f, q_idx, kv_idx, ot, of;
@@ -162,6 +162,8 @@ Layout make_layout(const moga_dims *d, const StgaGeom *g) {
     L.cu = c.take(sizeof(int32_t) * (m + 1));
     L.perm = c.take(sizeof(int32_t) * n);
     L.table = c.take(sizeof(int32_t) * nbp * m);
+    L.base_rel = c.take(sizeof(int32_t) * nbp * m);
+    L.totals = c.take(sizeof(int32_t) * m);
     L.pperm = c.take(sizeof(float) * n);
     L.qp = c.take(tensor);
     L.kp = c.take(tensor);
@@ -287,7 +289,8 @@ moga_status run_perm_index(const int32_t *gid, const moga_dims *d, int32_t *cu, 
                            void *ws, const Layout &L, hipStream_t s) {
     PermuteLaunch p{};
     p.group_id = gid; p.n = d->n_tokens; p.m = d->n_groups;
-    p.table = at<int32_t>(ws, L.table); p.cu = cu; p.perm = perm;
+    p.table = at<int32_t>(ws, L.table); p.base_rel = at<int32_t>(ws, L.base_rel);
+    p.totals = at<int32_t>(ws, L.totals); p.cu = cu; p.perm = perm;
     HIP_TRY(launch_perm_index(p, s), "permute index launch");
     return MOGA_OK;
 }

@@ -20,6 +20,7 @@ constexpr int kMaxShots = 256;    // STGA shots passed by value
 constexpr int kAttnBQMin = 128;   // smallest query rows per attention work item (4 waves x 32)
 constexpr int kAttnThreads = 256;
 constexpr int kPermTokensPerBlock = 2048;
+constexpr int64_t kFusedScanReads = int64_t(1) << 24;  // nblk^2 x m bound of the in-scatter scan
 constexpr int kRouteTokensPerBlock = 256;
 constexpr int kPlanSortMax = 4096; // segments sorted by key length up to this count
 
@@ -76,6 +77,8 @@ struct PermuteLaunch {
     int64_t n;
     int m;
     int32_t *table;     // [nblk][m] per-block counts
+    int32_t *base_rel;  // [nblk][m] exclusive prefix over blocks (large inputs: scan launch)
+    int32_t *totals;    // [m]
     int32_t *cu;        // [m+1]
     int32_t *perm;      // [n]
 };

@@ -48,14 +48,43 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *gid, int64_t n
             wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] + wc[3][threadIdx.x];
 }
 
+// Block i (large inputs only): base_rel[b][i] = sum_{b' < b} table[b'][i]; totals[i] = the sum
+// over all blocks.  One block per group, a Hillis-Steele scan over 256 entries at a time.
+__global__ __launch_bounds__(256) void scan_kernel(const int32_t *table, int64_t nblk, int m,
+                                                    int32_t *base_rel, int32_t *totals) {
+    __shared__ int s[256];
+    const int g = blockIdx.x;
+    int carry = 0;
+    for (int64_t c0 = 0; c0 < nblk; c0 += 256) {
+        const int64_t b = c0 + threadIdx.x;
+        const int v = b < nblk ? table[b * m + g] : 0;
+        s[threadIdx.x] = v;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int add = (int)threadIdx.x >= off ? s[threadIdx.x - off] : 0;
+            __syncthreads();
+            s[threadIdx.x] += add;
+            __syncthreads();
+        }
+        if (b < nblk) base_rel[b * m + g] = carry + s[threadIdx.x] - v;
+        carry += s[255];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) totals[g] = carry;
+}
+
 // Block b: its tokens' positions.  The exclusive prefix of table[.][i] over blocks b' < b and
-// the group totals are taken here from the whole table (nblk x m integers, read from L2 by every
-// block; integer sums, so the order of the LDS atomics does not matter), then
+// the group totals come from scan_kernel (base_rel, totals) or, when base_rel is NULL, are taken
+// here from the whole table (nblk x m integers, read from L2 by every block, so only for inputs
+// where nblk^2 x m stays small; integer sums, so the order of the LDS atomics does not matter),
+// then
 // cu = prefix of group totals and every token's position is cu[g] + (tokens of g in earlier
 // blocks) + (earlier in this block), the in-block part from ballots and popcounts.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *gid, int64_t n, int m,
                                                        const int32_t *table, int nblk,
-                                                       int32_t *cu, int32_t *perm) {
+                                                       const int32_t *base_rel,
+                                                       const int32_t *totals, int32_t *cu,
+                                                       int32_t *perm) {
     __shared__ int before[kMaxGroups], total[kMaxGroups];
     __shared__ int base[kMaxGroups];
     __shared__ int wc[4][kMaxGroups];
@@ -68,9 +97,14 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *gid, int64_
         const int64_t t = (int64_t)blockIdx.x * kPermTokensPerBlock + r * 256 + threadIdx.x;
         gv[r] = t < n ? gid[t] : -1;
     }
-    if ((int)threadIdx.x < m) before[threadIdx.x] = total[threadIdx.x] = 0;
-    __syncthreads();
-    {
+    if (base_rel) {
+        if ((int)threadIdx.x < m) {
+            before[threadIdx.x] = base_rel[(int64_t)blockIdx.x * m + threadIdx.x];
+            total[threadIdx.x] = totals[threadIdx.x];
+        }
+    } else {
+        if ((int)threadIdx.x < m) before[threadIdx.x] = total[threadIdx.x] = 0;
+        __syncthreads();
         const int ne = nblk * m, mine = (int)blockIdx.x * m;
         for (int e = threadIdx.x; e < ne; e += 256) {
             const int v = table[e], g = e % m;
@@ -201,8 +235,17 @@ hipError_t launch_perm_index(const PermuteLaunch &a, hipStream_t s) {
                        a.table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // the scan inside the scatter costs nblk^2 x m table reads: up to 2^24 (1.5 M at 563,160
+    // tokens and 20 groups) it saves a launch; above, the linear scan runs as its own launch
+    const bool fused = nblk * nblk * a.m <= kFusedScanReads;
+    if (!fused) {
+        hipLaunchKernelGGL(scan_kernel, dim3(a.m), dim3(256), 0, s, a.table, nblk, a.m, a.base_rel,
+                           a.totals);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nblk), dim3(256), 0, s, a.group_id, a.n, a.m,
-                       a.table, (int)nblk, a.cu, a.perm);
+                       a.table, (int)nblk, fused ? nullptr : a.base_rel,
+                       fused ? nullptr : a.totals, a.cu, a.perm);
     return hipGetLastError();
 }
 

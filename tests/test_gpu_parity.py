@@ -137,6 +137,29 @@ def test_permute_parity_and_round_trip(n, m, hd, case):
     assert torch.equal(back[0], q) and torch.equal(back[1], k)
 
 
+@pytest.mark.parametrize("n, m, case", [
+    (1048576, 64, "random"),   # 512 index blocks: the largest table the scatter scans itself
+    (1048577, 64, "random"),   # 513 blocks: the scan runs as its own launch
+    (1200001, 64, "runs"),     # the scan launch with most groups absent from most blocks
+    (4000000, 5, "skewed"),    # five groups over 1954 blocks: the scan launch
+])
+def test_index_build_large(n, m, case):
+    """cu_seqlens and perm alone (no rows moved) on both sides of the in-scatter scan's bound."""
+    _announce("index build", n=n, m=m, case=case)
+    rng = np.random.Generator(np.random.PCG64(n + 7 * m))
+    if case == "runs":
+        g = np.repeat(rng.integers(0, m, n // 5000 + 1), 5000)[:n].astype(np.int32)
+    elif case == "skewed":
+        g = rng.choice(m, n, p=rng.dirichlet(np.full(m, 0.5))).astype(np.int32)
+    else:
+        g = rng.integers(0, m, n).astype(np.int32)
+    cu, perm, _, _ = api.moga_permute(torch.from_numpy(g).to(DEV), [], m)
+    torch.cuda.synchronize()
+    cu_ref, perm_ref = oracle.groups(g, m)
+    np.testing.assert_array_equal(host(cu), cu_ref)
+    np.testing.assert_array_equal(host(perm), perm_ref)
+
+
 # ------------------------------------------------------------------------------- varlen attention
 def _segments(lengths):
     return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
